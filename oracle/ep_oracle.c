@@ -1,0 +1,271 @@
+/*
+ * ep_oracle.c -- plain CPU oracle for MoE expert-parallel prepare, dispatch,
+ * combine, dispatch_bwd and combine_bwd at one GPU's share of the work.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously-correct model
+ * that the HIP library is checked against. Only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg may load it; the library itself never
+ * calls it, and it shares no code, header or table with the library.
+ *
+ * Everything here is single-threaded scalar C, one loop per step of the
+ * definition. Integer work is exact; the only floating point is an ordered
+ * binary32 sum followed by one round-to-nearest-even to bf16.
+ *
+ * Sources (the expert-parallel pull requests these ops come from):
+ *  - "Expert Parallelism: common C API + NCCL EP backend", section "Per-step
+ *    (allocation-free, CUDA-graph capturable)": the five per-step calls and
+ *    their one-line meanings (prepare writes the routing maps for a handle;
+ *    dispatch sends token rows and routing weights to their experts; combine
+ *    is an unweighted scatter-sum back to the sources, the caller having
+ *    already multiplied by the received weights; dispatch_bwd and combine_bwd
+ *    are the two backward ops; combine_bwd leaves padded rows zero).
+ *  - "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with
+ *    symm-mem zero-copy", section "Public Python API": payloads are bf16 and
+ *    topk_idx is int64; section "Testing": identity round trip, VJP,
+ *    bit stability.
+ *  - "Expert-parallel implementations for ep_dispatch_experts", table
+ *    "Implementations": a rank masks the routes that go to other ranks'
+ *    experts; here a masked route carries the id -1.
+ *
+ * Readings where the pages leave a step open (each one is also a test):
+ *  - Rows of an expert's segment are in ascending flattened route order
+ *    s = t*K + k (a stable counting sort keyed by expert id).
+ *  - An expert's segment is its route count rounded up to a multiple of the
+ *    alignment A; pad rows sit at the end of the segment and are zero in
+ *    every expert-major output. An expert with no routes has an empty segment.
+ *  - token_counts are the raw (unpadded) per-expert route counts.
+ *  - Exactly -1 marks a masked route. Any other id outside [0,E) raises the
+ *    BAD_EXPERT status bit and is then treated as masked.
+ *  - If the padded total exceeds the receive capacity, the OVERFLOW bit is
+ *    raised and every route whose row would lie at or past the capacity is
+ *    dropped (slot -1); rows past the capacity are never written.
+ *  - combine sums, in ascending k, the fp32 values of the rows of the token's
+ *    valid routes, starting from the first valid row (so a single route is a
+ *    bit copy, -0.0 included), then rounds once to bf16. A token with no
+ *    valid route gets +0.
+ *  - fp32 -> bf16 rounds to nearest, ties to even, keeps subnormals, carries
+ *    into infinity on overflow, and returns the canonical quiet NaN 0x7FC0
+ *    for any NaN (the sign of a NaN produced by an add is not portable).
+ */
+#include <fenv.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <xmmintrin.h>
+
+#define ORACLE_STATUS_BAD_EXPERT 1u
+#define ORACLE_STATUS_OVERFLOW 2u
+
+/* Return codes of the oracle entry points. */
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARGS 1
+#define ORACLE_ERR_FPENV 2
+
+/* The oracle relies on IEEE binary32 with round-to-nearest and with
+ * subnormals neither flushed on output (FTZ) nor treated as zero on input
+ * (DAZ). Refuse to run in any other floating-point environment. */
+static int fpenv_is_ieee(void) {
+  unsigned csr = _mm_getcsr();
+  if (csr & (1u << 15)) return 0; /* FTZ */
+  if (csr & (1u << 6)) return 0;  /* DAZ */
+  return fegetround() == FE_TONEAREST;
+}
+
+/* bf16 -> fp32: a bf16 value is the upper half of the binary32 pattern. */
+static float bf16_to_float(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even (IEEE 754 roundTiesToEven
+ * applied to the 8-bit significand of bfloat16). The two candidates are the
+ * truncation and the next representable value above it in magnitude; the
+ * discarded low half decides between them. */
+uint16_t ep_oracle_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+    return 0x7FC0u; /* canonical quiet NaN */
+  uint16_t truncated = (uint16_t)(u >> 16);
+  uint32_t discarded = u & 0xFFFFu;
+  int round_up;
+  if (discarded > 0x8000u) {
+    round_up = 1;
+  } else if (discarded < 0x8000u) {
+    round_up = 0;
+  } else {
+    round_up = (truncated & 1u) != 0u; /* exact tie: go to the even one */
+  }
+  /* For finite values, the next bf16 pattern up is the next value in
+   * magnitude (the carry moves into the exponent, up to infinity). */
+  return (uint16_t)(truncated + (round_up ? 1u : 0u));
+}
+
+float ep_oracle_bf16_to_f32(uint16_t h) { return bf16_to_float(h); }
+
+/* Worst-case number of received rows: every token sends min(K,E) distinct
+ * routes and every expert adds up to A-1 pad rows. */
+int64_t ep_oracle_recv_capacity_worst(int64_t T, int32_t K, int32_t E, int32_t A) {
+  int64_t per_token = K < E ? K : E;
+  return T * per_token + (int64_t)E * (int64_t)(A - 1);
+}
+
+/*
+ * prepare: routing ids -> per-expert counts, aligned segment offsets, the
+ * slot of every route and the source route of every received row.
+ *
+ *   topk_idx  int64 [T*K]   routing id of route s = t*K + k
+ *   counts    int32 [E]     valid routes per expert (unpadded)
+ *   offsets   int32 [E+1]   segment starts; offsets[E] = padded total
+ *   slot      int32 [T*K]   received row of route s, -1 if masked or dropped
+ *   row_src   int32 [cap]   route s held by received row r, -1 for pad rows
+ *                           (rows at or past offsets[E] are left untouched)
+ *   status    uint32        BAD_EXPERT / OVERFLOW bits
+ */
+int ep_oracle_prepare(int64_t T, int32_t K, int32_t E, int32_t A, int64_t cap,
+                      const int64_t* topk_idx, int32_t* counts, int32_t* offsets,
+                      int32_t* slot, int32_t* row_src, uint32_t* status) {
+  if (T < 0 || K < 1 || E < 1 || A < 1 || cap < 0) return ORACLE_ERR_ARGS;
+  if (!counts || !offsets || !status) return ORACLE_ERR_ARGS;
+  const int64_t routes = T * (int64_t)K;
+  if (routes > 0 && (!topk_idx || !slot)) return ORACLE_ERR_ARGS;
+  uint32_t st = 0;
+
+  /* Step 1: classify each route and count the valid ones per expert. */
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t s = 0; s < routes; ++s) {
+    int64_t e = topk_idx[s];
+    if (e == -1) continue;                  /* masked */
+    if (e < 0 || e >= E) {                  /* out of range: flag, then mask */
+      st |= ORACLE_STATUS_BAD_EXPERT;
+      continue;
+    }
+    counts[e] += 1;
+  }
+
+  /* Step 2: segment e is counts[e] rounded up to a multiple of A. */
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t padded = ((int64_t)counts[e] + A - 1) / A * A;
+    offsets[e + 1] = (int32_t)(offsets[e] + padded);
+  }
+  const int64_t total = offsets[E];
+  if (total > cap) st |= ORACLE_STATUS_OVERFLOW;
+
+  /* Step 3: fill the segments in route order. Every row first counts as a
+   * pad; a route then claims the next free row of its expert's segment. */
+  const int64_t live = total < cap ? total : cap;
+  for (int64_t r = 0; r < live; ++r) row_src[r] = -1;
+  int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  if (!cursor) return ORACLE_ERR_ARGS;
+  for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t s = 0; s < routes; ++s) {
+    int64_t e = topk_idx[s];
+    if (e < 0 || e >= E) {
+      slot[s] = -1;
+      continue;
+    }
+    int64_t r = cursor[e]++;
+    if (r >= cap) {
+      slot[s] = -1;                         /* dropped on overflow */
+      continue;
+    }
+    slot[s] = (int32_t)r;
+    row_src[r] = (int32_t)s;
+  }
+  free(cursor);
+  *status = st;
+  return ORACLE_OK;
+}
+
+/*
+ * dispatch (token part and weight part): received row r holds the token row
+ * of the route it came from, or zeros for a pad row. Rows at or past
+ * min(total, cap) are not touched.
+ *
+ *   x        bf16 [T*H]     token rows
+ *   w        f32  [T*K]     routing weights (may be NULL: then no weight output)
+ *   recv     bf16 [cap*H]
+ *   recv_w   f32  [cap]
+ */
+int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int64_t cap, int64_t total,
+                       const int32_t* row_src, const uint16_t* x, const float* w,
+                       uint16_t* recv, float* recv_w) {
+  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0) return ORACLE_ERR_ARGS;
+  const int64_t live = total < cap ? total : cap;
+  for (int64_t r = 0; r < live; ++r) {
+    int32_t s = row_src[r];
+    if (s >= 0) {
+      int64_t t = s / K;
+      for (int64_t h = 0; h < H; ++h) recv[r * H + h] = x[t * H + h];
+      if (w && recv_w) recv_w[r] = w[s];
+    } else {
+      for (int64_t h = 0; h < H; ++h) recv[r * H + h] = 0;
+      if (w && recv_w) recv_w[r] = 0.0f;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* combine_bwd is the same row map as dispatch's token part, applied to the
+ * gradient of the combined output. */
+int ep_oracle_combine_bwd(int64_t T, int32_t K, int64_t H, int64_t cap, int64_t total,
+                          const int32_t* row_src, const uint16_t* g_result,
+                          uint16_t* g_expert_out) {
+  return ep_oracle_dispatch(T, K, H, cap, total, row_src, g_result, NULL, g_expert_out,
+                            NULL);
+}
+
+/*
+ * combine: for each token, the ordered binary32 sum over its valid routes
+ * (k ascending) of the received rows, rounded once to bf16.
+ *
+ *   rows     bf16 [cap*H]   expert outputs, expert-major
+ *   out      bf16 [T*H]
+ */
+int ep_oracle_combine(int64_t T, int32_t K, int64_t H, const int32_t* slot,
+                      const uint16_t* rows, uint16_t* out) {
+  if (T < 0 || K < 1 || H < 1) return ORACLE_ERR_ARGS;
+  if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      int have = 0;
+      for (int32_t k = 0; k < K; ++k) {
+        int32_t r = slot[t * K + k];
+        if (r < 0) continue;
+        float v = bf16_to_float(rows[(int64_t)r * H + h]);
+        if (!have) {
+          acc = v;
+          have = 1;
+        } else {
+          acc = acc + v;
+        }
+      }
+      out[t * H + h] = have ? ep_oracle_f32_to_bf16(acc) : (uint16_t)0;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * dispatch_bwd: the token gradient is combine applied to the gradient of the
+ * received rows; the weight gradient of route s is the gradient of the
+ * received weight in its slot, or +0 when the route is masked or no weight
+ * gradient is given (g_recv_w NULL).
+ */
+int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, const int32_t* slot,
+                           const uint16_t* g_recv, const float* g_recv_w,
+                           uint16_t* grad_tokens, float* grad_w) {
+  int rc = ep_oracle_combine(T, K, H, slot, g_recv, grad_tokens);
+  if (rc != ORACLE_OK) return rc;
+  if (!grad_w) return ORACLE_OK;
+  for (int64_t s = 0; s < T * (int64_t)K; ++s) {
+    int32_t r = slot[s];
+    grad_w[s] = (r >= 0 && g_recv_w) ? g_recv_w[r] : 0.0f;
+  }
+  return ORACLE_OK;
+}
