@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the expert-parallel routing hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: prepare, dispatch,
+combine, combine_bwd and dispatch_bwd on the DeepSeek-V3-shaped workload
+(T=4096 tokens, H=7168 bf16, E=256 experts, top-8 group-limited routing,
+alignment 128), with every input resident in HBM before timing starts.
+
+The headline is dispatch+combine throughput in algorithmic HBM GB/s (bytes
+the method must move, see ``algorithmic_bytes``) over their kernel time,
+measured with HIP events recorded on the stream the kernels run on. The line
+also carries the roofline of the dominant kernel and the CPU oracle timed on a
+bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_ep_prepare_amd", "csrc", f)
+                  for f in ("ep_kernels.hip", "ep_api.hip", "ep_internal.h")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np):
+    """Bytes each op must move at minimum (each row once).
+
+    B = 2H bytes per bf16 row, R valid routes, P pad rows, T_act tokens with
+    at least one valid route.
+      dispatch      T_act*B + (R+P)*B + 4R + 8(R+P)   rows, weights in/out, row map
+      combine       R*B + T*B + 4TK                   rows in/out, slot map
+      combine_bwd   T_act*B + (R+P)*B + 4(R+P)        rows in/out, row map
+      dispatch_bwd  R*B + 4R + T*B + 8TK              rows in/out, weights, slot map
+      prepare       8TK + 4TK + 4(R+P) + 8E           ids, slots, row map, counts
+    """
+    import numpy as np
+    B = 2 * H
+    R = int(counts_np.sum())
+    total = int(offsets_np[-1])
+    P = total - R
+    T_act = int((topk_idx >= 0).any(axis=1).sum()) if T else 0
+    return {
+        "dispatch": T_act * B + (R + P) * B + 4 * R + 8 * (R + P),
+        "combine": R * B + T * B + 4 * T * K,
+        "combine_bwd": T_act * B + (R + P) * B + 4 * (R + P),
+        "dispatch_bwd": R * B + 4 * R + T * B + 8 * T * K,
+        "prepare": 8 * T * K + 4 * T * K + 4 * (R + P) + 8 * E,
+        "_R": R, "_P": P, "_T_act": T_act, "_total": total,
+    }
+
+
+def load_traffic(kernel: str, workload: str, src_hash: str):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
+    used only when it was taken on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on the same inputs: whole
+    steps repeated until the time budget is spent (at least one)."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    t_d = t_c = 0.0
+    n = 0
+    start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, cap)
+        t1 = time.perf_counter()
+        oracle.dispatch(p, host["x"], r.topk_weights)
+        t2 = time.perf_counter()
+        oracle.combine(p, host["expert_out"])
+        t3 = time.perf_counter()
+        oracle.combine_bwd(p, host["g_result"])
+        oracle.dispatch_bwd(p, host["g_recv"], host["g_recv_w"])
+        t_d += t2 - t1
+        t_c += t3 - t2
+        n += 1
+        if time.perf_counter() - start > budget_s:
+            break
+    return t_d / n, t_c / n, n, time.perf_counter() - start
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the path; runs on more than one GPU "
+              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_ep_prepare_amd as ep
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = workloads.CONFIGS[args.workload]
+    T, K, E, A, H = cfg.T, cfg.K, cfg.E, cfg.A, cfg.H
+    log(f"workload {cfg.name}: T={T} H={H} E={E} K={K} A={A}")
+    r = workloads.make_routing(cfg)
+    cap = ep.recv_capacity_worst(T, K, E, A)
+    L = ep.Layout(T, K, E, A, H, cap)
+    dev = torch.device("cuda")
+    handle = ep.new_handle(L)
+    idx = torch.from_numpy(r.topk_idx).to(dev)
+    w = torch.from_numpy(r.topk_weights).to(dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    x = workloads.randn_bf16_torch((T, H), 1)
+    recv = torch.zeros(cap, H, dtype=torch.bfloat16, device=dev)
+    recv_w = torch.zeros(cap, dtype=torch.float32, device=dev)
+    result = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    g_result = workloads.randn_bf16_torch((T, H), 2)
+    g_exp = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    g_recv = workloads.randn_bf16_torch((cap, H), 3)
+    g_recv_w = workloads.randn_bf16_torch((cap,), 4).float()
+    g_tok = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    g_w = torch.empty(T, K, dtype=torch.float32, device=dev)
+
+    # The experts' stand-in: expert_out = bf16(recv * recv_topk_weights),
+    # computed once outside the timed region (the caller's pre-multiply).
+    ep.prepare(L, idx, counts, handle, offsets)
+    ep.dispatch(L, handle, x, w, recv, recv_w)
+    expert_out = (recv.float() * recv_w[:, None]).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    counts_np = counts.cpu().numpy()
+    offsets_np = offsets.cpu().numpy()
+    nbytes = algorithmic_bytes(T, K, E, H, r.topk_idx, counts_np, offsets_np)
+    log(f"R={nbytes['_R']} P={nbytes['_P']} total={nbytes['_total']} cap={cap} "
+        f"T_act={nbytes['_T_act']}")
+
+    ops = ["prepare", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ep.prepare(L, idx, counts, handle, offsets)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.dispatch(L, handle, x, w, recv, recv_w)
+        if ev is not None:
+            ev[2].record(stream)
+        ep.combine(L, handle, expert_out, result)
+        if ev is not None:
+            ev[3].record(stream)
+        ep.combine_bwd(L, handle, g_result, g_exp)
+        if ev is not None:
+            ev[4].record(stream)
+        ep.dispatch_bwd(L, handle, g_recv, g_recv_w, g_tok, g_w)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert ep.read_status(handle) == 0, "unexpected status bits"
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per_op_ms = {op: [] for op in ops}
+    for ev in events:
+        for j, op in enumerate(ops):
+            per_op_ms[op].append(ev[j].elapsed_time(ev[j + 1]))
+    avg = {op: float(np.mean(v)) for op, v in per_op_ms.items()}
+    med = {op: float(np.median(v)) for op, v in per_op_ms.items()}
+
+    def gbs(op):
+        return nbytes[op] / (avg[op] * 1e-3) / 1e9
+
+    pair_bytes = nbytes["dispatch"] + nbytes["combine"]
+    pair_s = (avg["dispatch"] + avg["combine"]) * 1e-3
+    value = pair_bytes / pair_s / 1e9
+    dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
+                   key=lambda op: avg[op])
+    kernel_of = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
+                 "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel"}
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(f"{dominant}", cfg.name, src_hash)
+    achieved = gbs(dominant)
+    roofline = {"bound": "hbm", "kernel": f"{kernel_of[dominant]} ({dominant})",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "algorithmic_bytes_per_launch": nbytes[dominant],
+                "avg_launch_us": round(avg[dominant] * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload")
+        host = {
+            "x": x.view(torch.int16).cpu().numpy().view(np.uint16),
+            "expert_out": expert_out.view(torch.int16).cpu().numpy().view(np.uint16),
+            "g_result": g_result.view(torch.int16).cpu().numpy().view(np.uint16),
+            "g_recv": g_recv.view(torch.int16).cpu().numpy().view(np.uint16),
+            "g_recv_w": g_recv_w.cpu().numpy(),
+        }
+        td, tc, n, spent = cpu_baseline(cfg, r, host, cap, args.cpu_budget)
+        cpu = {"value": round(pair_bytes / (td + tc) / 1e9, 3), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"{n} whole step(s) of the {cfg.name} workload (all five ops, "
+                         f"same inputs) by the single-threaded C oracle, {spent:.1f} s; "
+                         f"dispatch {td * 1e3:.1f} ms, combine {tc * 1e3:.1f} ms per step",
+               "host_cpu_count": os.cpu_count()}
+
+    line = {
+        "metric": "dispatch+combine HBM GB/s (% of MI355X peak) and tokens/s, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} topk={K} alignment={A} "
+                               f"routing={cfg.routing} cap={cap}",
+                   "global_batch": T, "parallelism": "none (one GPU's share)"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(T / pair_s, 1),
+        "ops": {op: {"avg_us": round(avg[op] * 1e3, 2), "median_us": round(med[op] * 1e3, 2),
+                     "algorithmic_bytes": nbytes[op],
+                     "GBps": round(gbs(op), 1) if op != "prepare" else None}
+                for op in ops},
+        "routing": {"R": nbytes["_R"], "P": nbytes["_P"], "total": nbytes["_total"],
+                    "T_act": nbytes["_T_act"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

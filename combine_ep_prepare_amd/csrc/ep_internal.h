@@ -1,0 +1,116 @@
+// ep_internal.h -- handle layout and kernel launchers shared by the C-ABI
+// entry points (ep_api.hip) and the gfx950 kernels (ep_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace epmi {
+
+constexpr int kWave = 64;
+constexpr int kMaxTopk = 64;
+constexpr int kMaxExperts = 2048;
+constexpr uint32_t kHandleMagic = 0x45504D49u;  // "EPMI"
+
+// Routes per prepare work unit (one wavefront): kPrepRounds x 64.
+constexpr int kPrepRounds = 8;
+constexpr int kUnitRoutes = kPrepRounds * kWave;
+
+// Header at the start of every handle (256 bytes reserved).
+struct HandleHeader {
+  uint32_t status;      // EP_STATUS_* bits of the last prepare
+  uint32_t magic;       // kHandleMagic once prepared
+  int64_t num_tokens;
+  int32_t topk;
+  int32_t num_experts;
+  int32_t alignment;
+  int32_t num_units;
+  int64_t recv_capacity;
+  int32_t total;        // offsets[E]
+  int32_t pads_live;    // pad rows below recv_capacity
+};
+static_assert(sizeof(HandleHeader) <= 256, "header too large");
+
+// Byte offsets of the regions of a handle; every region is 256-byte aligned.
+struct HandleLayout {
+  size_t header, counts, offsets, pad_offsets, slot, row_src, pad_rows, unit_hist,
+      unit_flags, bytes;
+  int32_t num_units;
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+inline int32_t prep_units(int64_t routes) {
+  return (int32_t)((routes + kUnitRoutes - 1) / kUnitRoutes);
+}
+
+inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) {
+  HandleLayout h{};
+  const int64_t routes = T * (int64_t)K;
+  h.num_units = prep_units(routes);
+  size_t at = 0;
+  h.header = at;       at += 256;
+  h.counts = at;       at += align256(sizeof(int32_t) * (size_t)E);
+  h.offsets = at;      at += align256(sizeof(int32_t) * (size_t)(E + 1));
+  h.pad_offsets = at;  at += align256(sizeof(int32_t) * (size_t)(E + 1));
+  h.slot = at;         at += align256(sizeof(int32_t) * (size_t)routes);
+  h.row_src = at;      at += align256(sizeof(int32_t) * (size_t)cap);
+  h.pad_rows = at;     at += align256(sizeof(int32_t) * (size_t)cap);
+  h.unit_hist = at;    at += align256(sizeof(int32_t) * (size_t)h.num_units * (size_t)E);
+  h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
+  h.bytes = at;
+  return h;
+}
+
+// Device pointers into one handle, passed by value to every kernel.
+struct HandleView {
+  HandleHeader* header;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pad_offsets;
+  int32_t* slot;
+  int32_t* row_src;
+  int32_t* pad_rows;
+  int32_t* unit_hist;
+  int32_t* unit_flags;
+};
+
+inline HandleView handle_view(void* mem, const HandleLayout& h) {
+  char* b = static_cast<char*>(mem);
+  HandleView v;
+  v.header = reinterpret_cast<HandleHeader*>(b + h.header);
+  v.counts = reinterpret_cast<int32_t*>(b + h.counts);
+  v.offsets = reinterpret_cast<int32_t*>(b + h.offsets);
+  v.pad_offsets = reinterpret_cast<int32_t*>(b + h.pad_offsets);
+  v.slot = reinterpret_cast<int32_t*>(b + h.slot);
+  v.row_src = reinterpret_cast<int32_t*>(b + h.row_src);
+  v.pad_rows = reinterpret_cast<int32_t*>(b + h.pad_rows);
+  v.unit_hist = reinterpret_cast<int32_t*>(b + h.unit_hist);
+  v.unit_flags = reinterpret_cast<int32_t*>(b + h.unit_flags);
+  return v;
+}
+
+// Sizes every kernel receives.
+struct Dims {
+  int64_t T;
+  int32_t K;
+  int32_t E;
+  int32_t A;
+  int32_t num_units;
+  int64_t cap;
+  int64_t H;
+};
+
+// Launchers (ep_kernels.hip). Each returns the hipError_t of its launch.
+hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
+                          int32_t* user_counts, int32_t* user_offsets, int num_cus,
+                          hipStream_t stream);
+hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
+                               const float* w, uint16_t* dst, float* dst_w, int num_cus,
+                               hipStream_t stream);
+hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
+                              const float* g_w, uint16_t* dst, float* dst_w,
+                              int num_cus, hipStream_t stream);
+
+}  // namespace epmi

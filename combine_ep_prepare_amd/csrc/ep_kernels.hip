@@ -1,0 +1,618 @@
+// ep_kernels.hip -- gfx950 (CDNA4) kernels for MoE expert-parallel routing.
+//
+// Three kernel families serve the five ops of "Expert Parallelism: common C
+// API + NCCL EP backend" (section "Per-step (allocation-free, CUDA-graph
+// capturable)") at one GPU's share:
+//
+//   prepare      prepare_hist_kernel + prepare_slots_kernel: a per-wavefront
+//                expert histogram privatised in LDS, a block-wide wavefront-
+//                shuffle exclusive scan of the aligned segment lengths, and a
+//                stable (route-ordered) slot map.
+//   dispatch,    scatter_rows_kernel: the linear map D that copies token row
+//   combine_bwd  t into the received row of each of its valid routes and
+//                zero-fills pad rows. Every source row is read once.
+//   combine,     reduce_rows_kernel: the transpose of D. Each token row is the
+//   dispatch_bwd fp32 sum, k ascending, of the received rows of its valid
+//                routes, rounded once to bf16; the dispatch_bwd weight
+//                gradient is gathered in the same pass.
+//
+// None of this is a dense contraction, so no MFMA: every kernel is bound by
+// HBM traffic (or, for prepare, by latency). Rows move as 16-byte vectors,
+// 64 lanes x 16 B = 1 KiB per wavefront instruction, fully coalesced.
+// Work is split into (row, column-block) items handed out to wavefronts in a
+// grid-stride loop whose bound is read on the device, so no host sync is ever
+// needed and every launch is graph-capturable.
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace epmi {
+
+namespace {
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N). Keeps
+// every index of the small per-lane register arrays a constant, so they stay
+// in VGPRs instead of being demoted to LDS or scratch.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) {
+  return static_cast<uint64_t>(__ballot(p));
+}
+
+// Lanes whose (valid) key equals this lane's key: the intersection, over the
+// key's bits, of the ballot of lanes agreeing on that bit. nbits ballots
+// instead of one iteration per distinct key.
+__device__ __forceinline__ uint64_t match_peers(uint32_t key, bool valid, int nbits) {
+  uint64_t m = wave_ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t ones = wave_ballot(valid && bit);
+    m &= bit ? ones : ~ones;
+  }
+  return m;
+}
+
+__device__ __forceinline__ bool handle_matches(const HandleHeader* h, const Dims& d) {
+  return h->magic == kHandleMagic && h->num_tokens == d.T && h->topk == d.K &&
+         h->num_experts == d.E && h->alignment == d.A && h->recv_capacity == d.cap;
+}
+
+__device__ __forceinline__ void flag_layout_mismatch(const HandleView& hv) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&hv.header->status, EP_STATUS_LAYOUT);
+}
+
+// fp32 -> bf16 bits, round to nearest even; any NaN -> 0x7FC0. Adding
+// 0x7FFF plus the lowest kept bit carries into the kept half exactly when the
+// discarded half is above one half ulp, or equal to it with an odd kept half.
+__device__ __forceinline__ uint32_t rne_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// prepare
+// ---------------------------------------------------------------------------
+
+// One wavefront per unit of kUnitRoutes consecutive routes. Histogram of the
+// unit's valid expert ids in a wave-private LDS row; each distinct id of a
+// 64-route round is added once, by its lowest lane, with the peer count.
+__global__ void __launch_bounds__(512)
+prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int nbits) {
+  extern __shared__ int32_t lds[];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int E = d.E;
+  int32_t* hist = lds + w * E;
+  for (int e = lane; e < E; e += kWave) hist[e] = 0;
+  __syncthreads();
+
+  const int64_t routes = d.T * d.K;
+  const int32_t u = blockIdx.x * nw + w;
+  bool bad_any = false;
+  if (u < d.num_units) {
+    const int64_t base = (int64_t)u * kUnitRoutes;
+    int64_t ids[kPrepRounds];
+#pragma unroll
+    for (int i = 0; i < kPrepRounds; ++i) {
+      const int64_t s = base + i * kWave + lane;
+      ids[i] = s < routes ? topk_idx[s] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kPrepRounds; ++i) {
+      const int64_t id = ids[i];
+      const bool valid = id >= 0 && id < E;
+      const bool bad = !valid && id != -1;
+      bad_any |= wave_ballot(bad) != 0;
+      const uint32_t key = valid ? (uint32_t)id : 0u;
+      const uint64_t peers = match_peers(key, valid, nbits);
+      if (valid && lane == __ffsll((unsigned long long)peers) - 1)
+        atomicAdd(&hist[key], (int32_t)__popcll(peers));
+    }
+  }
+  __syncthreads();
+  if (u < d.num_units) {
+    int32_t* out = hv.unit_hist + (int64_t)u * E;
+    for (int e = lane; e < E; e += kWave) out[e] = hist[e];
+    if (lane == 0) hv.unit_flags[u] = bad_any ? 1 : 0;
+  }
+}
+
+// Every block derives the same counts and aligned offsets from the unit
+// histograms (block 0 publishes them), then its wavefronts revisit their
+// units and hand out rows: slot = segment start + routes of the same expert
+// in earlier units + rank among earlier lanes and rounds of this unit.
+__global__ void __launch_bounds__(512)
+prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
+                     int32_t* __restrict__ user_counts, int32_t* __restrict__ user_offsets,
+                     int nbits) {
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t s_wave_tot[2][16];
+  __shared__ int32_t s_pads_live;
+  const int nthr = blockDim.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int nw = nthr / kWave;
+  const int E = d.E;
+  const int32_t A = d.A;
+  const int32_t U = d.num_units;
+  const int32_t u0 = blockIdx.x * nw;
+  int32_t* s_counts = lds;              // [E]
+  int32_t* s_pre = s_counts + E;        // [E] routes in units before this block
+  int32_t* s_offs = s_pre + E;          // [E+1]
+  int32_t* s_padoff = s_offs + E + 1;   // [E+1]
+  int32_t* s_red = s_padoff + E + 1;    // [2*nthr]
+  int32_t* s_cursor = s_red + 2 * nthr; // [nw*E]
+
+  // 1. Column sums of the unit histograms: all units, and units before u0.
+  const int ncols = E < nthr ? E : nthr;
+  const int nparts = nthr / ncols;
+  for (int e0 = 0; e0 < E; e0 += ncols) {
+    const int col = tid % ncols;
+    const int part = tid / ncols;
+    const int e = e0 + col;
+    int32_t all = 0, pre = 0;
+    if (part < nparts && e < E) {
+      for (int32_t u = part; u < U; u += nparts) {
+        const int32_t v = hv.unit_hist[(int64_t)u * E + e];
+        all += v;
+        pre += u < u0 ? v : 0;
+      }
+    }
+    s_red[tid] = all;
+    s_red[nthr + tid] = pre;
+    __syncthreads();
+    if (tid < ncols && e < E) {
+      int32_t a = 0, p = 0;
+      for (int q = 0; q < nparts; ++q) {
+        a += s_red[q * ncols + tid];
+        p += s_red[nthr + q * ncols + tid];
+      }
+      s_counts[e] = a;
+      s_pre[e] = p;
+    }
+    __syncthreads();
+  }
+
+  // 2. Exclusive scans over experts of the aligned segment lengths and of the
+  //    pad rows: a contiguous chunk per thread, a shuffle scan inside each
+  //    wavefront, then the wavefront totals.
+  const int per = (E + nthr - 1) / nthr;
+  const int b0 = tid * per;
+  int32_t loc_a = 0, loc_p = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < E) {
+      const int32_t c = s_counts[e];
+      const int32_t padded = (c + A - 1) / A * A;
+      loc_a += padded;
+      loc_p += padded - c;
+    }
+  }
+  int32_t inc_a = loc_a, inc_p = loc_p;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t ta = __shfl_up(inc_a, off);
+    const int32_t tp = __shfl_up(inc_p, off);
+    if (lane >= off) {
+      inc_a += ta;
+      inc_p += tp;
+    }
+  }
+  if (lane == kWave - 1) {
+    s_wave_tot[0][w] = inc_a;
+    s_wave_tot[1][w] = inc_p;
+  }
+  if (tid == 0) s_pads_live = 0;
+  __syncthreads();
+  int32_t ex_a = inc_a - loc_a, ex_p = inc_p - loc_p;
+  for (int q = 0; q < w; ++q) {
+    ex_a += s_wave_tot[0][q];
+    ex_p += s_wave_tot[1][q];
+  }
+  int32_t live_pads = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < E) {
+      const int32_t c = s_counts[e];
+      const int32_t padded = (c + A - 1) / A * A;
+      s_offs[e] = ex_a;
+      s_padoff[e] = ex_p;
+      const int64_t lo = (int64_t)ex_a + c, hi = (int64_t)ex_a + padded;
+      const int64_t lo_c = lo < d.cap ? lo : d.cap, hi_c = hi < d.cap ? hi : d.cap;
+      live_pads += (int32_t)(hi_c - lo_c);
+      ex_a += padded;
+      ex_p += padded - c;
+    }
+  }
+  if (tid == nthr - 1) {
+    s_offs[E] = ex_a;
+    s_padoff[E] = ex_p;
+  }
+  if (live_pads) atomicAdd(&s_pads_live, live_pads);
+  __syncthreads();
+
+  // 3. Block 0 publishes counts, offsets and the header.
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += nthr) {
+      hv.offsets[e] = s_offs[e];
+      hv.pad_offsets[e] = s_padoff[e];
+      if (user_offsets) user_offsets[e] = s_offs[e];
+      if (e < E) {
+        hv.counts[e] = s_counts[e];
+        user_counts[e] = s_counts[e];
+      }
+    }
+    int32_t f = 0;
+    for (int32_t u = tid; u < U; u += nthr) f |= hv.unit_flags[u];
+    const int any_bad = __syncthreads_or(f);
+    if (tid == 0) {
+      HandleHeader* h = hv.header;
+      const int32_t total = s_offs[E];
+      h->status = (any_bad ? EP_STATUS_BAD_EXPERT : 0u) |
+                  ((int64_t)total > d.cap ? EP_STATUS_OVERFLOW : 0u);
+      h->num_tokens = d.T;
+      h->topk = d.K;
+      h->num_experts = d.E;
+      h->alignment = d.A;
+      h->num_units = d.num_units;
+      h->recv_capacity = d.cap;
+      h->total = total;
+      h->pads_live = s_pads_live;
+      h->magic = kHandleMagic;
+    }
+  }
+
+  // 4. Per-wavefront cursors: segment start + routes of earlier units.
+  for (int e = tid; e < E; e += nthr) {
+    int32_t run = s_offs[e] + s_pre[e];
+    for (int q = 0; q < nw; ++q) {
+      s_cursor[q * E + e] = run;
+      const int32_t u = u0 + q;
+      if (u < U) run += hv.unit_hist[(int64_t)u * E + e];
+    }
+  }
+  __syncthreads();
+
+  // 5. Stable slots: the lowest lane of each distinct id claims popc(peers)
+  //    rows from the cursor; every peer adds its rank among earlier lanes.
+  const int64_t routes = d.T * d.K;
+  const int32_t u = u0 + w;
+  if (u < U) {
+    const int64_t base = (int64_t)u * kUnitRoutes;
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    int64_t ids[kPrepRounds];
+#pragma unroll
+    for (int i = 0; i < kPrepRounds; ++i) {
+      const int64_t s = base + i * kWave + lane;
+      ids[i] = s < routes ? topk_idx[s] : -1;
+    }
+    int32_t* cursor = s_cursor + w * E;
+#pragma unroll
+    for (int i = 0; i < kPrepRounds; ++i) {
+      const int64_t id = ids[i];
+      const bool valid = id >= 0 && id < E;
+      const uint32_t key = valid ? (uint32_t)id : 0u;
+      const uint64_t peers = match_peers(key, valid, nbits);
+      const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+      int32_t first = 0;
+      if (valid && lane == leader) first = atomicAdd(&cursor[key], (int32_t)__popcll(peers));
+      first = __shfl(first, leader);
+      const int64_t s = base + i * kWave + lane;
+      if (s < routes) {
+        const int64_t row = (int64_t)first + __popcll(peers & lanes_below);
+        const bool keep = valid && row < d.cap;
+        hv.slot[s] = keep ? (int32_t)row : -1;
+        if (keep) hv.row_src[row] = (int32_t)s;
+      }
+    }
+  }
+
+  // 6. Pad rows of the experts this block owns: row_src = -1 and the list of
+  //    live pad rows (ascending, so the live ones form a prefix).
+  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    const int64_t lo = (int64_t)s_offs[e] + s_counts[e];
+    const int64_t hi_full = s_offs[e + 1];
+    const int64_t hi = hi_full < d.cap ? hi_full : d.cap;
+    for (int64_t r = lo + tid; r < hi; r += nthr) {
+      hv.row_src[r] = -1;
+      hv.pad_rows[s_padoff[e] + (r - lo)] = (int32_t)r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D: dispatch (token rows + weights) and combine_bwd (gradient rows)
+// ---------------------------------------------------------------------------
+
+// Items: (token, column block) for every token, then (pad row, column block)
+// for every live pad row. A token item reads its 1 KiB x CH slice of the row
+// once and stores it to the received row of each valid route.
+template <int KT, int CH>
+__global__ void __launch_bounds__(256)
+scatter_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
+                    const float* __restrict__ w, uint16_t* __restrict__ dst,
+                    float* __restrict__ dst_w) {
+  const HandleHeader* h = hv.header;
+  if (!handle_matches(h, d)) {
+    flag_layout_mismatch(hv);
+    return;
+  }
+  const int K = KT > 0 ? KT : d.K;
+  const int lane = lane_id();
+  const int64_t V = d.H / 8;
+  constexpr int64_t CB = (int64_t)kWave * CH;
+  const int64_t ncb = (V + CB - 1) / CB;
+  const int64_t tok_items = d.T * ncb;
+  const int64_t n_items = tok_items + (int64_t)h->pads_live * ncb;
+  const int64_t wpb = blockDim.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * wpb;
+  const uint4* __restrict__ src4 = reinterpret_cast<const uint4*>(src);
+  uint4* __restrict__ dst4 = reinterpret_cast<uint4*>(dst);
+
+  for (int64_t it = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave; it < n_items;
+       it += nwaves) {
+    if (it < tok_items) {
+      const int64_t t = it / ncb;
+      const int64_t cb = it - t * ncb;
+      const int32_t sl = lane < K ? hv.slot[t * K + lane] : -1;
+      uint64_t vm = wave_ballot(sl >= 0);
+      if (vm == 0) continue;
+      if (cb == 0 && w != nullptr && dst_w != nullptr && sl >= 0) dst_w[sl] = w[t * K + lane];
+      const int64_t v0 = cb * CB + lane;
+      const uint4* srow = src4 + t * V;
+      uint4 buf[CH];
+      static_for<CH>([&](auto j) {
+        const int64_t v = v0 + j * kWave;
+        buf[j] = v < V ? srow[v] : make_uint4(0u, 0u, 0u, 0u);
+      });
+      while (vm) {
+        const int k = __ffsll((unsigned long long)vm) - 1;
+        vm &= vm - 1;
+        const int32_t r = __builtin_amdgcn_readlane(sl, k);
+        uint4* drow = dst4 + (int64_t)r * V;
+        static_for<CH>([&](auto j) {
+          const int64_t v = v0 + j * kWave;
+          if (v < V) drow[v] = buf[j];
+        });
+      }
+    } else {
+      const int64_t pit = it - tok_items;
+      const int64_t p = pit / ncb;
+      const int64_t cb = pit - p * ncb;
+      const int32_t r = hv.pad_rows[p];
+      if (cb == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
+      uint4* drow = dst4 + (int64_t)r * V;
+      const int64_t v0 = cb * CB + lane;
+      static_for<CH>([&](auto j) {
+        const int64_t v = v0 + j * kWave;
+        if (v < V) drow[v] = make_uint4(0u, 0u, 0u, 0u);
+      });
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D^T: combine (expert rows -> token rows) and dispatch_bwd
+// ---------------------------------------------------------------------------
+
+// Items: (token, column block). The valid rows' slices are all loaded first
+// (up to G of them in flight per lane), then summed in fp32 in ascending k
+// from the first valid one, then rounded once.
+template <int KT, int CH>
+__global__ void __launch_bounds__(256)
+reduce_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
+                   const float* __restrict__ g_w, uint16_t* __restrict__ dst,
+                   float* __restrict__ dst_w) {
+  const HandleHeader* h = hv.header;
+  if (!handle_matches(h, d)) {
+    flag_layout_mismatch(hv);
+    return;
+  }
+  constexpr int G = KT > 0 ? KT : 8;
+  const int K = KT > 0 ? KT : d.K;
+  const int lane = lane_id();
+  const int64_t V = d.H / 8;
+  constexpr int64_t CB = (int64_t)kWave * CH;
+  const int64_t ncb = (V + CB - 1) / CB;
+  const int64_t n_items = d.T * ncb;
+  const int64_t wpb = blockDim.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * wpb;
+  const uint4* __restrict__ src4 = reinterpret_cast<const uint4*>(src);
+  uint4* __restrict__ dst4 = reinterpret_cast<uint4*>(dst);
+
+  for (int64_t it = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave; it < n_items;
+       it += nwaves) {
+    const int64_t t = it / ncb;
+    const int64_t cb = it - t * ncb;
+    const int32_t sl = lane < K ? hv.slot[t * K + lane] : -1;
+    const uint64_t vm = wave_ballot(sl >= 0);
+    if (cb == 0 && dst_w != nullptr && lane < K)
+      dst_w[t * K + lane] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
+    const int64_t v0 = cb * CB + lane;
+    float acc[CH][8];
+    bool have = false;
+    for (int k0 = 0; k0 < K; k0 += G) {
+      uint4 buf[G][CH];
+      static_for<G>([&](auto g) {
+        const int k = k0 + g;
+        if (k < K && ((vm >> k) & 1ull)) {
+          const int32_t r = __builtin_amdgcn_readlane(sl, k);
+          const uint4* srow = src4 + (int64_t)r * V;
+          static_for<CH>([&](auto j) {
+            const int64_t v = v0 + j * kWave;
+            buf[g][j] = v < V ? srow[v] : make_uint4(0u, 0u, 0u, 0u);
+          });
+        }
+      });
+      static_for<G>([&](auto g) {
+        const int k = k0 + g;
+        if (k < K && ((vm >> k) & 1ull)) {
+          static_for<CH>([&](auto j) {
+            const uint32_t wd[4] = {buf[g][j].x, buf[g][j].y, buf[g][j].z, buf[g][j].w};
+            static_for<4>([&](auto q) {
+              const float lo = bf16_lo(wd[q]), hi = bf16_hi(wd[q]);
+              if (have) {
+                acc[j][2 * q] += lo;
+                acc[j][2 * q + 1] += hi;
+              } else {
+                acc[j][2 * q] = lo;
+                acc[j][2 * q + 1] = hi;
+              }
+            });
+          });
+          have = true;
+        }
+      });
+    }
+    uint4* drow = dst4 + t * V;
+    static_for<CH>([&](auto j) {
+      const int64_t v = v0 + j * kWave;
+      if (v < V) {
+        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+        if (have) {
+          o.x = rne_bf16(acc[j][0]) | (rne_bf16(acc[j][1]) << 16);
+          o.y = rne_bf16(acc[j][2]) | (rne_bf16(acc[j][3]) << 16);
+          o.z = rne_bf16(acc[j][4]) | (rne_bf16(acc[j][5]) << 16);
+          o.w = rne_bf16(acc[j][6]) | (rne_bf16(acc[j][7]) << 16);
+        }
+        drow[v] = o;
+      }
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int key_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+constexpr size_t kLdsBudget = 65536;
+
+size_t slots_lds_bytes(int E, int nw) {
+  return sizeof(int32_t) * (size_t)(4 * E + 2 + 2 * kWave * nw + nw * E);
+}
+
+constexpr int kScatterCH = 2;
+constexpr int kReduceCH = 1;
+constexpr int kBlock = 256;
+constexpr int kBlocksPerCU = 8;
+
+int grid_for(int64_t items, int num_cus) {
+  const int64_t waves_per_block = kBlock / kWave;
+  int64_t blocks = (items + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)num_cus * kBlocksPerCU;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+template <int KT>
+hipError_t scatter_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* w,
+                     uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((scatter_rows_kernel<KT, kScatterCH>), dim3(grid), dim3(kBlock), 0,
+                     stream, d, hv, src, w, dst, dst_w);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t reduce_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* g_w,
+                    uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH>), dim3(grid), dim3(kBlock), 0,
+                     stream, d, hv, src, g_w, dst, dst_w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
+                          int32_t* user_counts, int32_t* user_offsets, int num_cus,
+                          hipStream_t stream) {
+  (void)num_cus;
+  const int nbits = key_bits(d.E);
+  const int U = d.num_units;
+  if (U > 0) {
+    int nw1 = 8;
+    while (nw1 > 1 && sizeof(int32_t) * (size_t)nw1 * d.E > kLdsBudget) nw1 /= 2;
+    const int grid1 = (U + nw1 - 1) / nw1;
+    hipLaunchKernelGGL(prepare_hist_kernel, dim3(grid1), dim3(nw1 * kWave),
+                       sizeof(int32_t) * (size_t)nw1 * d.E, stream, d, hv, topk_idx, nbits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  int nw2 = 8;
+  while (nw2 > 1 && slots_lds_bytes(d.E, nw2) > kLdsBudget) nw2 /= 2;
+  int grid2 = (U + nw2 - 1) / nw2;
+  if (grid2 < 1) grid2 = 1;
+  hipLaunchKernelGGL(prepare_slots_kernel, dim3(grid2), dim3(nw2 * kWave),
+                     slots_lds_bytes(d.E, nw2), stream, d, hv, topk_idx, user_counts,
+                     user_offsets, nbits);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
+                               const float* w, uint16_t* dst, float* dst_w, int num_cus,
+                               hipStream_t stream) {
+  const int64_t V = d.H / 8;
+  const int64_t CB = (int64_t)kWave * kScatterCH;
+  const int64_t ncb = (V + CB - 1) / CB;
+  const int64_t max_items = (d.T + d.cap) * ncb;
+  if (max_items == 0) return hipSuccess;
+  const int grid = grid_for(max_items, num_cus);
+  switch (d.K) {
+    case 1: return scatter_k<1>(d, hv, src, w, dst, dst_w, grid, stream);
+    case 2: return scatter_k<2>(d, hv, src, w, dst, dst_w, grid, stream);
+    case 4: return scatter_k<4>(d, hv, src, w, dst, dst_w, grid, stream);
+    case 6: return scatter_k<6>(d, hv, src, w, dst, dst_w, grid, stream);
+    case 8: return scatter_k<8>(d, hv, src, w, dst, dst_w, grid, stream);
+    default: return scatter_k<0>(d, hv, src, w, dst, dst_w, grid, stream);
+  }
+}
+
+hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
+                              const float* g_w, uint16_t* dst, float* dst_w, int num_cus,
+                              hipStream_t stream) {
+  const int64_t V = d.H / 8;
+  const int64_t CB = (int64_t)kWave * kReduceCH;
+  const int64_t ncb = (V + CB - 1) / CB;
+  const int64_t items = d.T * ncb;
+  if (items == 0) return hipSuccess;
+  const int grid = grid_for(items, num_cus);
+  switch (d.K) {
+    case 1: return reduce_k<1>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    case 2: return reduce_k<2>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    case 4: return reduce_k<4>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    case 6: return reduce_k<6>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    case 8: return reduce_k<8>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    default: return reduce_k<0>(d, hv, src, g_w, dst, dst_w, grid, stream);
+  }
+}
+
+}  // namespace epmi

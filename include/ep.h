@@ -1,0 +1,215 @@
+/*
+ * ep.h -- MoE expert-parallel token routing on one AMD Instinct MI355X
+ * (gfx950): prepare, dispatch, combine and their two backward ops.
+ *
+ * The five per-step calls follow the per-step part of the common C API in
+ * "Expert Parallelism: common C API + NCCL EP backend" (section "Per-step
+ * (allocation-free, CUDA-graph capturable)"), at one GPU's share of the work:
+ * prepare builds the routing maps of a handle, dispatch moves token rows and
+ * their routing weights into an expert-major receive buffer, combine sums the
+ * expert outputs of each token back into a token row without weighting them
+ * (the caller has already multiplied by the received weights), and
+ * dispatch_bwd / combine_bwd are the adjoints of dispatch / combine.
+ *
+ * Conventions shared by every call
+ *  - Routes are numbered s = t*K + k over the [T,K] routing table.
+ *  - A route is valid iff 0 <= topk_idx[s] < E. The id -1 marks a masked
+ *    route (one whose expert lives elsewhere; see the masking of
+ *    "Expert-parallel implementations for ep_dispatch_experts", table
+ *    "Implementations"). Any other id is an error: the device raises
+ *    EP_STATUS_BAD_EXPERT and the route is then treated as masked.
+ *  - Expert e owns the received rows [offsets[e], offsets[e+1]). Its valid
+ *    routes fill the first counts[e] rows in ascending s; the segment is then
+ *    padded with zero rows up to a multiple of the alignment A. An expert
+ *    with no route has an empty segment. total = offsets[E].
+ *  - Payloads are bf16 passed as uint16_t bit patterns ("[PyTorch] Expert
+ *    Parallelism: PyTorch wrapper + autograd ops with symm-mem zero-copy",
+ *    section "Public Python API": bf16 only, int64 routing ids); routing
+ *    weights are fp32. Rows are contiguous, H elements each, row-major.
+ *  - All pointers are device pointers unless stated otherwise. Payload
+ *    pointers must be 16-byte aligned and H must be a multiple of 8. A
+ *    pointer to a buffer with no element (T == 0 for [T,...] buffers,
+ *    recv_capacity == 0 for [recv_capacity,...] buffers) may be NULL.
+ *  - Work is enqueued on `stream` and nothing waits for it: no call below
+ *    synchronises, allocates, frees or keeps a pointer after it returns,
+ *    except ep_read_status, which waits for the stream. The caller owns
+ *    every buffer. Outputs must not overlap inputs or each other.
+ *  - Host-detectable errors return an ep_status_t before any HIP call is
+ *    made; nothing is enqueued then. Data-dependent errors raise sticky bits
+ *    in the handle's status word (see ep_read_status).
+ *  - Calls on one handle must be ordered on the GPU (same stream, or events)
+ *    with prepare first. Several handles may be in flight at once.
+ */
+#ifndef EP_MI355X_EP_H
+#define EP_MI355X_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+  EP_OK = 0,
+  EP_ERR_NULL = 1,        /* a required pointer is NULL */
+  EP_ERR_SHAPE = 2,       /* a size is out of range (see ep_layout_t) */
+  EP_ERR_ALIGN = 3,       /* a payload pointer is not 16-byte aligned */
+  EP_ERR_HANDLE_SIZE = 4, /* handle_bytes < ep_handle_mem_size(layout) */
+  EP_ERR_CAPACITY = 5,    /* recv_capacity < 0 or >= 2^31 */
+  EP_ERR_DEVICE = 6,      /* the current device is not gfx950 */
+  EP_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} ep_status_t;
+
+/* Sticky device-side bits of a handle's status word. */
+enum {
+  EP_STATUS_BAD_EXPERT = 1u, /* prepare saw an id outside [0,E) other than -1 */
+  EP_STATUS_OVERFLOW = 2u,   /* prepare: total > recv_capacity; routes whose row
+                                would lie at or past the capacity were dropped */
+  EP_STATUS_LAYOUT = 4u      /* a payload op was given a layout other than the
+                                one the handle was prepared with, or a handle
+                                that was never prepared; the op wrote nothing */
+};
+
+/*
+ * Per-layer sizes (the role of the layer configuration in the common C API,
+ * passed by pointer as plain data).
+ *   num_tokens    T >= 0
+ *   topk          K in [1, 64]
+ *   num_experts   E in [1, 2048], local experts
+ *   alignment     A >= 1 rows (the per-expert dispatch output alignment)
+ *   reserved      must be 0
+ *   hidden        H >= 8, a multiple of 8 (bf16 elements per row)
+ *   recv_capacity rows of every expert-major buffer, 0 <= cap < 2^31
+ * T*K + E*(A-1) must be below 2^31 (every offset fits an int32).
+ */
+typedef struct ep_layout {
+  int64_t num_tokens;
+  int32_t topk;
+  int32_t num_experts;
+  int32_t alignment;
+  int32_t reserved;
+  int64_t hidden;
+  int64_t recv_capacity;
+} ep_layout_t;
+
+/* Rows that can never overflow: every token sends min(K,E) distinct routes
+ * and every expert adds at most A-1 pad rows: T*min(K,E) + E*(A-1). With
+ * repeated ids in a token's top-k the bound is T*K + E*(A-1). Returns -1 for
+ * out-of-range arguments. Host only. */
+int64_t ep_recv_capacity_worst(int64_t num_tokens, int32_t topk, int32_t num_experts,
+                               int32_t alignment);
+
+/* Bytes of device memory the caller must provide as `handle_mem` for this
+ * layout (the handle-size query of the common C API). Returns 0 for an
+ * invalid layout. Host only. */
+size_t ep_handle_mem_size(const ep_layout_t* layout);
+
+/* Byte offsets, inside handle_mem, of the routing maps that prepare writes,
+ * so that callers can read them (all int32 unless stated):
+ *   status   uint32 status word (EP_STATUS_* bits)
+ *   counts   [E]     valid routes per expert
+ *   offsets  [E+1]   segment starts, offsets[E] = total
+ *   slot     [T*K]   received row of route s, -1 if masked or dropped
+ *   row_src  [recv_capacity]  route held by received row r, -1 for a pad row;
+ *            entries at or past min(total, recv_capacity) are unspecified
+ *   bytes    == ep_handle_mem_size(layout)
+ * Every offset is a multiple of 256. Host only. */
+typedef struct ep_handle_regions {
+  size_t status;
+  size_t counts;
+  size_t offsets;
+  size_t slot;
+  size_t row_src;
+  size_t bytes;
+} ep_handle_regions_t;
+
+ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* out);
+
+/*
+ * prepare: from the int64 routing table, write the per-expert token counts,
+ * the aligned segment offsets and the slot map into the handle.
+ *   topk_idx        int64 [T,K]                  input
+ *   token_counts    int32 [E]                    output: valid routes per expert
+ *                                                (not padded)
+ *   expert_offsets  int32 [E+1] or NULL          output: segment starts,
+ *                                                expert_offsets[E] = total
+ *   handle_mem      handle_bytes of device memory, fully (re)written here
+ * After this call the handle holds, for the later ops, the received row of
+ * every route (-1 if masked or dropped) and the source route of every live
+ * received row (-1 for pads). Its status word is reset, then raises
+ * BAD_EXPERT / OVERFLOW as described above.
+ */
+ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
+                       int32_t* token_counts, int32_t* expert_offsets, void* handle_mem,
+                       size_t handle_bytes, hipStream_t stream);
+
+/*
+ * dispatch: recv_tokens[r,:] = tokens[s/K,:] and recv_topk_weights[r] =
+ * topk_weights[s] for every live row r holding route s (bit copies); pad
+ * rows get +0 in both. Rows at or past min(total, recv_capacity) are not
+ * written.
+ *   tokens             bf16 [T,H]
+ *   topk_weights       fp32 [T,K] or NULL
+ *   recv_tokens        bf16 [recv_capacity,H]
+ *   recv_topk_weights  fp32 [recv_capacity]; must be NULL iff topk_weights is
+ *                      (when T > 0 and recv_capacity > 0)
+ */
+ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
+                        size_t handle_bytes, const uint16_t* tokens,
+                        const float* topk_weights, uint16_t* recv_tokens,
+                        float* recv_topk_weights, hipStream_t stream);
+
+/*
+ * combine: result[t,:] = bf16(sum over the valid routes of t, k ascending,
+ * of expert_out[slot(t,k),:]), accumulated in fp32 starting from the first
+ * valid row and rounded once to nearest-even (NaN -> 0x7FC0). A token with
+ * no valid route gets +0. Unweighted.
+ *   expert_out  bf16 [recv_capacity,H] (only live rows are read)
+ *   result      bf16 [T,H]
+ */
+ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
+                       size_t handle_bytes, const uint16_t* expert_out, uint16_t* result,
+                       hipStream_t stream);
+
+/*
+ * dispatch_bwd (adjoint of dispatch): grad_tokens = combine(grad) with the
+ * same fp32 ascending-k rule; grad_topk_weights[s] = g_recv_topk_weights[r]
+ * for the row r of a valid route s, else +0. A NULL g_recv_topk_weights
+ * (no gradient flowed into the received weights) gives +0 everywhere; a NULL
+ * grad_topk_weights skips the weight gradient.
+ *   grad                 bf16 [recv_capacity,H]
+ *   g_recv_topk_weights  fp32 [recv_capacity] or NULL
+ *   grad_tokens          bf16 [T,H]
+ *   grad_topk_weights    fp32 [T,K] or NULL
+ */
+ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
+                            size_t handle_bytes, const uint16_t* grad,
+                            const float* g_recv_topk_weights, uint16_t* grad_tokens,
+                            float* grad_topk_weights, hipStream_t stream);
+
+/*
+ * combine_bwd (adjoint of combine): grad_expert_out[r,:] = grad[s/K,:] for
+ * every live row r holding route s; pad rows are zeroed. Rows at or past
+ * min(total, recv_capacity) are not written.
+ *   grad             bf16 [T,H]
+ *   grad_expert_out  bf16 [recv_capacity,H]
+ */
+ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
+                           size_t handle_bytes, const uint16_t* grad,
+                           uint16_t* grad_expert_out, hipStream_t stream);
+
+/* Copy the handle's status word (EP_STATUS_* bits) to *host_out. Waits for
+ * `stream`; not for the hot path. host_out is a host pointer. */
+ep_status_t ep_read_status(const void* handle_mem, uint32_t* host_out, hipStream_t stream);
+
+/* Static description of an ep_status_t. Never NULL. Host only. */
+const char* ep_status_str(ep_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_EP_H */

@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+- the library loads and exports every function include/ep.h declares;
+- size queries (handle size, worst-case capacity, handle regions);
+- every host-detectable error returns its code before any HIP call. Each
+  case below fails validation, so no device pointer is ever dereferenced.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import combine_ep_prepare_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+# Fake, never dereferenced device addresses (16-byte aligned / misaligned).
+P = C.c_void_p(0x10000)
+P2 = C.c_void_p(0x20000)
+MIS = C.c_void_p(0x10008)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 10
+    lib = C.CDLL(ep.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ep.h but not exported"
+    assert set(names) == set(ep.ENTRY_POINTS)
+
+
+def lay(T=16, K=2, E=4, A=8, H=64, cap=None):
+    if cap is None:
+        cap = max(64, ep.recv_capacity_worst(T, K, E, A))
+    return ep.Layout(T, K, E, A, H, cap)
+
+
+def test_recv_capacity_worst():
+    assert ep.recv_capacity_worst(4096, 8, 256, 128) == 4096 * 8 + 256 * 127
+    assert ep.recv_capacity_worst(10, 8, 4, 1) == 40         # K > E: min(K, E) routes
+    assert ep.recv_capacity_worst(0, 8, 32, 128) == 32 * 127
+    assert ep.recv_capacity_worst(-1, 8, 32, 128) == -1
+    assert ep.recv_capacity_worst(1, 0, 32, 128) == -1
+
+
+def test_handle_size_and_regions():
+    L = lay(T=4096, K=8, E=256, A=128, H=7168)
+    n = ep.handle_mem_size(L)
+    r = ep.handle_regions(L)
+    assert r.bytes == n
+    for off in (r.counts, r.offsets, r.slot, r.row_src):
+        assert off % 256 == 0
+    assert r.counts + 4 * 256 <= r.offsets
+    assert r.offsets + 4 * 257 <= r.slot
+    assert r.slot + 4 * 4096 * 8 <= r.row_src
+    assert r.row_src + 4 * L.cap <= n
+    # the handle grows with the capacity and does not depend on H
+    assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=512)) == n
+    assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=7168, cap=L.cap * 2)) > n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), ep.EP_ERR_SHAPE),
+    (dict(K=0), ep.EP_ERR_SHAPE),
+    (dict(K=65), ep.EP_ERR_SHAPE),
+    (dict(E=0), ep.EP_ERR_SHAPE),
+    (dict(E=2049), ep.EP_ERR_SHAPE),
+    (dict(A=0), ep.EP_ERR_SHAPE),
+    (dict(H=0), ep.EP_ERR_SHAPE),
+    (dict(H=12), ep.EP_ERR_SHAPE),
+    (dict(cap=-1), ep.EP_ERR_CAPACITY),
+    (dict(cap=2 ** 31), ep.EP_ERR_CAPACITY),
+    (dict(T=2 ** 28, K=8), ep.EP_ERR_SHAPE),           # T*K >= 2^31
+    (dict(E=2048, A=2 ** 21, cap=0), ep.EP_ERR_SHAPE),  # E*(A-1) >= 2^31
+])
+def test_bad_layouts_rejected(kw, code):
+    L = lay(**kw)
+    assert ep.handle_mem_size(L) == 0
+    assert ep.lib.ep_prepare(C.byref(L), P, P, None, P, 1 << 30, None) == code
+    assert ep.lib.ep_dispatch(C.byref(L), P, 1 << 30, P, None, P2, None, None) == code
+    assert ep.lib.ep_combine(C.byref(L), P, 1 << 30, P, P2, None) == code
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, 1 << 30, P, None, P2, None, None) == code
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, 1 << 30, P, P2, None) == code
+    r = ep.HandleRegions()
+    assert ep.lib.ep_handle_regions(C.byref(L), C.byref(r)) == code
+
+
+def test_reserved_field_must_be_zero():
+    L = lay()
+    L.reserved = 1
+    assert ep.handle_mem_size(L) == 0
+
+
+def test_null_layout_and_pointers():
+    L = lay()
+    n = ep.handle_mem_size(L)
+    assert ep.lib.ep_prepare(None, P, P, None, P, n, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_prepare(C.byref(L), None, P, None, P, n, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_prepare(C.byref(L), P, None, None, P, n, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_prepare(C.byref(L), P, P, None, None, n, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch(C.byref(L), None, n, P, None, P2, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, None, None, P2, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, P, None, None, None, None) == ep.EP_ERR_NULL
+    # weights and received weights must be given together
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, P, P2, P2, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, P, None, P2, P2, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_combine(C.byref(L), P, n, None, P2, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_combine(C.byref(L), P, n, P, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, n, None, None, P2, None, None) == \
+        ep.EP_ERR_NULL
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n, None, P2, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n, P, None, None) == ep.EP_ERR_NULL
+    out = C.c_uint32(0)
+    assert ep.lib.ep_read_status(None, C.byref(out), None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_read_status(P, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_handle_regions(C.byref(L), None) == ep.EP_ERR_NULL
+
+
+def test_handle_too_small():
+    L = lay()
+    n = ep.handle_mem_size(L)
+    assert ep.lib.ep_prepare(C.byref(L), P, P, None, P, n - 1, None) == ep.EP_ERR_HANDLE_SIZE
+    assert ep.lib.ep_dispatch(C.byref(L), P, n - 1, P, None, P2, None, None) == \
+        ep.EP_ERR_HANDLE_SIZE
+    assert ep.lib.ep_combine(C.byref(L), P, 0, P, P2, None) == ep.EP_ERR_HANDLE_SIZE
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, 7, P, None, P2, None, None) == \
+        ep.EP_ERR_HANDLE_SIZE
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n - 256, P, P2, None) == \
+        ep.EP_ERR_HANDLE_SIZE
+
+
+def test_misaligned_pointers():
+    L = lay()
+    n = ep.handle_mem_size(L)
+    assert ep.lib.ep_prepare(C.byref(L), P, P, None, MIS, n, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_dispatch(C.byref(L), MIS, n, P, None, P2, None, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, MIS, None, P2, None, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, P, None, MIS, None, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_combine(C.byref(L), P, n, MIS, P2, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_combine(C.byref(L), P, n, P, MIS, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, n, MIS, None, P2, None, None) == \
+        ep.EP_ERR_ALIGN
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, n, P, None, MIS, None, None) == \
+        ep.EP_ERR_ALIGN
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n, MIS, P2, None) == ep.EP_ERR_ALIGN
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n, P, MIS, None) == ep.EP_ERR_ALIGN
+    out = C.c_uint32(0)
+    assert ep.lib.ep_read_status(MIS, C.byref(out), None) == ep.EP_ERR_ALIGN
+
+
+def test_status_strings():
+    for code in range(8):
+        s = ep.status_str(code)
+        assert s and s != "unknown ep_status_t"
+    assert ep.status_str(99) == "unknown ep_status_t"
+
+
+def test_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    L = lay()
+    h = torch.empty(ep.handle_mem_size(L), dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        ep.prepare(L, torch.zeros((16, 2), dtype=torch.int32), torch.zeros(4, dtype=torch.int32), h)
+    with pytest.raises(ValueError):   # not a GPU tensor
+        ep.prepare(L, torch.zeros((16, 2), dtype=torch.int64), torch.zeros(4, dtype=torch.int32), h)

@@ -209,3 +209,15 @@ def small_int_bf16(rng, shape, bound: int = 16) -> np.ndarray:
     """bf16 bits of integers in [-bound, bound]: sums of a few stay exact."""
     v = rng.integers(-bound, bound + 1, size=shape).astype(np.float32)
     return _bf16_bits(v)
+
+
+def randn_bf16_torch(shape, seed: int, device="cuda"):
+    """N(0,1) bf16 tensor drawn with PyTorch's seeded generator on ``device``.
+
+    Used for the large payloads of full-size runs, where host generation
+    would dominate; the same tensor (copied to the host) feeds the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED_BASE * 1_000_003 + int(seed))
+    return torch.randn(tuple(shape), generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
