@@ -71,20 +71,135 @@ def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np):
     }
 
 
-def load_traffic(kernel: str, workload: str, src_hash: str):
+def _pmc_path(op: str, workload: str) -> str:
+    return os.path.join(PROFILE_DIR, f"{KERNEL_OF_OP[op]}_{op}_{workload}_pmc.txt")
+
+
+def load_traffic(op: str, workload: str, src_hash: str):
     """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
     used only when it was taken on the current kernel sources."""
-    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.json")
+    path = _pmc_path(op, workload)
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            d = json.load(f)
-    except (OSError, ValueError):
+            line = [ln for ln in f if ln.startswith("JSON: ")][-1]
+        d = json.loads(line[len("JSON: "):])
+    except (OSError, ValueError, IndexError):
         return None
     if d.get("kernel_source_hash") != src_hash:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def _read_csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
+                "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel"}
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
+                  out_dir: str = PROFILE_DIR):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, both with --calibration-copy-mib) into per-op HBM bytes.
+
+    Each counter is scaled by what it reads for the plain copy of known size
+    (PyTorch's elementwise copy kernel, the largest dispatch whose name holds
+    "copy"), so the result is in true bytes. Dispatches of our two payload
+    kernels are attributed to ops by their order inside each step: scatter
+    (dispatch), reduce (combine), scatter (combine_bwd), reduce (dispatch_bwd).
+    """
+    import numpy as np
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _read_csv_rows(d, "counter_collection.csv")
+                if r.get("Counter_Name") == counter]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        # the calibration copy is a plain device-to-device copy of copy_mib
+        # MiB (PyTorch hands it to the runtime's copyBuffer kernel)
+        calib = [r for r in rows if "copybuffer" in r["Kernel_Name"].lower()
+                 and float(r["Counter_Value"]) > copy_mib * 1024.0 / 8]
+        if not calib:
+            raise SystemExit(f"no calibration copy found for {counter} in {d}")
+        expected_kib = copy_mib * 1024.0
+        factor = float(np.median([float(r["Counter_Value"]) for r in calib])) / expected_kib
+        # the timed steps follow the calibration copy; the one dispatch made
+        # before it (to build the expert outputs) is left out
+        last_copy = max(int(r.get("Dispatch_Id", 0)) for r in calib)
+        seq = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows
+               if int(r.get("Dispatch_Id", 0)) > last_copy
+               and ("scatter_rows_kernel" in r["Kernel_Name"]
+                    or "reduce_rows_kernel" in r["Kernel_Name"])]
+        per_op = {op: [] for op in KERNEL_OF_OP}
+        # steps alternate scatter, reduce, scatter, reduce
+        order = ["dispatch", "combine", "combine_bwd", "dispatch_bwd"]
+        for i, (name, kib) in enumerate(seq):
+            op = order[i % 4]
+            assert KERNEL_OF_OP[op] in name, (op, name)
+            per_op[op].append(kib / factor * 1024.0)
+        res[counter] = {"factor": factor,
+                        "per_op_bytes": {op: float(np.median(v)) for op, v in per_op.items() if v}}
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "calibration": {"copy_mib": copy_mib,
+                           "fetch_factor": res["FETCH_SIZE"]["factor"],
+                           "write_factor": res["WRITE_SIZE"]["factor"]}}
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc <COUNTER> "
+           "-d <dir> -o <name> --output-format csv -- python3 bench.py --workload "
+           f"{workload} --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy-mib {copy_mib}"
+           "   (once with FETCH_SIZE, once with WRITE_SIZE); then python bench.py "
+           f"--summarize-pmc <fetch dir> <write dir> --workload {workload} "
+           f"--calibration-copy-mib {copy_mib}")
+    for op in KERNEL_OF_OP:
+        fb = res["FETCH_SIZE"]["per_op_bytes"].get(op)
+        wb = res["WRITE_SIZE"]["per_op_bytes"].get(op)
+        if fb is None or wb is None:
+            continue
+        summary = dict(out)
+        summary.update({"op": op, "kernel": KERNEL_OF_OP[op], "fetch_bytes_per_launch": fb,
+                        "write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb})
+        path = _pmc_path(op, workload)
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {KERNEL_OF_OP[op]} ({op}), workload {workload}\n")
+            f.write(f"# command: {cmd}\n")
+            f.write(f"# FETCH_SIZE scale {out['calibration']['fetch_factor']:.4f}, WRITE_SIZE "
+                    f"scale {out['calibration']['write_factor']:.4f} (counter / true bytes of "
+                    f"a {copy_mib} MiB device copy in the same run)\n")
+            f.write(f"# per launch (median over the timed steps): fetch {fb / 1e6:.1f} MB, "
+                    f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB\n")
+            f.write("JSON: " + json.dumps(summary) + "\n")
+        print(f"{path}: fetch {fb / 1e6:.1f} MB write {wb / 1e6:.1f} MB", flush=True)
+
+
+def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
+                    out_dir: str = PROFILE_DIR):
+    """profiles/ep_kernels_<workload>_kernel_stats.txt from a rocprofv3
+    --kernel-trace --stats run of this script."""
+    rows = _read_csv_rows(trace_dir, "kernel_stats.csv")
+    path = os.path.join(out_dir, f"ep_kernels_{workload}_kernel_stats.txt")
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <dir> -o "
+           f"trace --output-format csv -- python3 bench.py --workload {workload} --steps "
+           f"{steps} --warmup {warmup} --no-cpu-baseline")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics, workload {workload}\n")
+        f.write(f"# command: {cmd}\n")
+        f.write(f"# kernel source hash {kernel_source_hash()}\n")
+        f.write(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+                f"{'share%':>7s}\n")
+        for r in rows:
+            name = r["Name"]
+            short = name.split("(")[0].replace("void ", "")
+            f.write(f"{short[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                    f"{float(r['Percentage']):7.2f}\n")
+    print(path, flush=True)
 
 
 def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
@@ -122,7 +237,20 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/*_pmc.txt from two rocprofv3 counter runs")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.calibration_copy_mib)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.steps, args.warmup)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -175,6 +303,15 @@ def main():
     log(f"R={nbytes['_R']} P={nbytes['_P']} total={nbytes['_total']} cap={cap} "
         f"T_act={nbytes['_T_act']}")
 
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 19          # bf16 elements
+        src_c = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+        dst_c = torch.empty_like(src_c)
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+
     ops = ["prepare", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
     stream = torch.cuda.current_stream()
 
@@ -226,10 +363,9 @@ def main():
     value = pair_bytes / pair_s / 1e9
     dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
                    key=lambda op: avg[op])
-    kernel_of = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
-                 "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel"}
+    kernel_of = KERNEL_OF_OP
     src_hash = kernel_source_hash()
-    traffic = load_traffic(f"{dominant}", cfg.name, src_hash)
+    traffic = load_traffic(dominant, cfg.name, src_hash)
     achieved = gbs(dominant)
     roofline = {"bound": "hbm", "kernel": f"{kernel_of[dominant]} ({dominant})",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

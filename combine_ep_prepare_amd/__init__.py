@@ -83,12 +83,12 @@ class EpError(RuntimeError):
         self.code = code
 
 
-def _load_library():
-    if not os.path.exists(LIB_PATH):
+def _load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; "
             "g.build()'` (hipcc, gfx950)")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(path)
     i64, i32, vp, sz = C.c_int64, C.c_int32, C.c_void_p, C.c_size_t
     lp = C.POINTER(Layout)
     lib.ep_recv_capacity_worst.argtypes = [i64, i32, i32, i32]

@@ -11,6 +11,7 @@ namespace epmi {
 constexpr int kWave = 64;
 constexpr int kMaxTopk = 64;
 constexpr int kMaxExperts = 2048;
+constexpr int kKeyBits = 11;  // bits of an expert id below kMaxExperts
 constexpr uint32_t kHandleMagic = 0x45504D49u;  // "EPMI"
 
 // Routes per prepare work unit (one wavefront): kPrepRounds x 64.

@@ -57,21 +57,24 @@ __device__ __forceinline__ uint64_t wave_ballot(bool p) {
 // instead of one iteration per distinct key.
 __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool valid, int nbits) {
   uint64_t m = wave_ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (key >> b) & 1u;
-    const uint64_t ones = wave_ballot(valid && bit);
-    m &= bit ? ones : ~ones;
-  }
+  // all kKeyBits bits, unrolled: bits at or above nbits are zero in every
+  // valid key and leave m unchanged
+  static_for<kKeyBits>([&](auto b) {
+    if (b < nbits) {
+      const bool bit = (key >> b) & 1u;
+      const uint64_t ones = wave_ballot(valid && bit);
+      m &= bit ? ones : ~ones;
+    }
+  });
   return m;
 }
 
-__device__ __forceinline__ bool handle_matches(const HandleHeader* h, const Dims& d) {
-  return h->magic == kHandleMagic && h->num_tokens == d.T && h->topk == d.K &&
-         h->num_experts == d.E && h->alignment == d.A && h->recv_capacity == d.cap;
-}
-
-__device__ __forceinline__ void flag_layout_mismatch(const HandleView& hv) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&hv.header->status, EP_STATUS_LAYOUT);
+// The whole header is copied in one go and then tested without
+// short-circuits, so it costs one round trip instead of one per field.
+__device__ __forceinline__ bool handle_matches(const HandleHeader& hh, const Dims& d) {
+  return (hh.magic == kHandleMagic) & (hh.num_tokens == d.T) & (hh.topk == d.K) &
+         (hh.num_experts == d.E) & (hh.alignment == d.A) & (hh.recv_capacity == d.cap) &
+         (hh.total >= 0) & (hh.pads_live >= 0);
 }
 
 // fp32 -> bf16 bits, round to nearest even; any NaN -> 0x7FC0. Adding
@@ -93,6 +96,27 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // prepare
 // ---------------------------------------------------------------------------
 
+namespace {
+
+// The kPrepRounds x 64 routing ids of one unit. Every load is issued
+// unconditionally (lanes past the last route re-read it; unit_id() masks
+// them where the ids are used), so all of them are in flight together.
+__device__ __forceinline__ void load_unit_ids(const int64_t* __restrict__ topk_idx,
+                                              int64_t base, int64_t routes, int lane,
+                                              int64_t (&ids)[kPrepRounds]) {
+  static_for<kPrepRounds>([&](auto i) {
+    const int64_t s = base + i * kWave + lane;
+    ids[i] = topk_idx[s < routes ? s : routes - 1];
+  });
+}
+
+__device__ __forceinline__ int64_t unit_id(const int64_t (&ids)[kPrepRounds], int i,
+                                           int64_t s, int64_t routes) {
+  return s < routes ? ids[i] : -1;
+}
+
+}  // namespace
+
 // One wavefront per unit of kUnitRoutes consecutive routes. Histogram of the
 // unit's valid expert ids in a wave-private LDS row; each distinct id of a
 // 64-route round is added once, by its lowest lane, with the peer count.
@@ -113,14 +137,10 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
   if (u < d.num_units) {
     const int64_t base = (int64_t)u * kUnitRoutes;
     int64_t ids[kPrepRounds];
+    load_unit_ids(topk_idx, base, routes, lane, ids);
 #pragma unroll
     for (int i = 0; i < kPrepRounds; ++i) {
-      const int64_t s = base + i * kWave + lane;
-      ids[i] = s < routes ? topk_idx[s] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < kPrepRounds; ++i) {
-      const int64_t id = ids[i];
+      const int64_t id = unit_id(ids, i, base + i * kWave + lane, routes);
       const bool valid = id >= 0 && id < E;
       const bool bad = !valid && id != -1;
       bad_any |= wave_ballot(bad) != 0;
@@ -163,9 +183,20 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   int32_t* s_offs = s_pre + E;          // [E+1]
   int32_t* s_padoff = s_offs + E + 1;   // [E+1]
   int32_t* s_red = s_padoff + E + 1;    // [2*nthr]
-  int32_t* s_cursor = s_red + 2 * nthr; // [nw*E]
+  int32_t* s_cursor = s_red + 2 * nthr; // [nw*E]: own units' counts, then cursors
 
-  // 1. Column sums of the unit histograms: all units, and units before u0.
+  // The routing ids of this wavefront's unit are loaded first, so that their
+  // latency overlaps the histogram loads below.
+  const int64_t routes = d.T * d.K;
+  const int32_t my_unit = u0 + w;
+  const int64_t base = (int64_t)my_unit * kUnitRoutes;
+  int64_t ids[kPrepRounds];
+  if (my_unit < U) load_unit_ids(topk_idx, base, routes, lane, ids);
+
+  // 1. Column sums of the unit histograms over all units and over the units
+  //    before this block; this block's own unit rows are kept in LDS. Loads
+  //    are issued kBatch at a time per thread so that many are in flight.
+  constexpr int kBatch = 16;
   const int ncols = E < nthr ? E : nthr;
   const int nparts = nthr / ncols;
   for (int e0 = 0; e0 < E; e0 += ncols) {
@@ -174,10 +205,19 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
     const int e = e0 + col;
     int32_t all = 0, pre = 0;
     if (part < nparts && e < E) {
-      for (int32_t u = part; u < U; u += nparts) {
-        const int32_t v = hv.unit_hist[(int64_t)u * E + e];
-        all += v;
-        pre += u < u0 ? v : 0;
+      for (int32_t ub = part; ub < U; ub += kBatch * nparts) {
+        int32_t v[kBatch];
+        static_for<kBatch>([&](auto j) {
+          const int32_t u = ub + j * nparts;
+          v[j] = hv.unit_hist[(int64_t)(u < U ? u : U - 1) * E + e];
+        });
+        static_for<kBatch>([&](auto j) {
+          const int32_t u = ub + j * nparts;
+          const int32_t c = u < U ? v[j] : 0;
+          all += c;
+          pre += u < u0 ? c : 0;
+          if (u >= u0 && u < u0 + nw) s_cursor[(u - u0) * E + e] = c;
+        });
       }
     }
     s_red[tid] = all;
@@ -223,14 +263,15 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
     s_wave_tot[0][w] = inc_a;
     s_wave_tot[1][w] = inc_p;
   }
-  if (tid == 0) s_pads_live = 0;
   __syncthreads();
   int32_t ex_a = inc_a - loc_a, ex_p = inc_p - loc_p;
   for (int q = 0; q < w; ++q) {
     ex_a += s_wave_tot[0][q];
     ex_p += s_wave_tot[1][q];
   }
-  int32_t live_pads = 0;
+  // Pad rows below the capacity: all of them, unless the capacity falls
+  // inside expert e's segment; then the pads of the experts before e plus
+  // those of e's pad rows that lie below it. Exactly one thread writes.
   for (int i = 0; i < per; ++i) {
     const int e = b0 + i;
     if (e < E) {
@@ -238,9 +279,10 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
       const int32_t padded = (c + A - 1) / A * A;
       s_offs[e] = ex_a;
       s_padoff[e] = ex_p;
-      const int64_t lo = (int64_t)ex_a + c, hi = (int64_t)ex_a + padded;
-      const int64_t lo_c = lo < d.cap ? lo : d.cap, hi_c = hi < d.cap ? hi : d.cap;
-      live_pads += (int32_t)(hi_c - lo_c);
+      if ((int64_t)ex_a <= d.cap && d.cap < (int64_t)ex_a + padded) {
+        const int64_t first_pad = (int64_t)ex_a + c;
+        s_pads_live = ex_p + (int32_t)(d.cap > first_pad ? d.cap - first_pad : 0);
+      }
       ex_a += padded;
       ex_p += padded - c;
     }
@@ -248,8 +290,8 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   if (tid == nthr - 1) {
     s_offs[E] = ex_a;
     s_padoff[E] = ex_p;
+    if ((int64_t)ex_a <= d.cap) s_pads_live = ex_p;
   }
-  if (live_pads) atomicAdd(&s_pads_live, live_pads);
   __syncthreads();
 
   // 3. Block 0 publishes counts, offsets and the header.
@@ -283,79 +325,172 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
     }
   }
 
-  // 4. Per-wavefront cursors: segment start + routes of earlier units.
+  // 4. Per-wavefront cursors: segment start + routes of earlier units
+  //    (turns the own-unit counts kept in LDS into running starts, in place).
   for (int e = tid; e < E; e += nthr) {
     int32_t run = s_offs[e] + s_pre[e];
-    for (int q = 0; q < nw; ++q) {
+    for (int q = 0; q < nw && u0 + q < U; ++q) {
+      const int32_t c = s_cursor[q * E + e];
       s_cursor[q * E + e] = run;
-      const int32_t u = u0 + q;
-      if (u < U) run += hv.unit_hist[(int64_t)u * E + e];
+      run += c;
     }
   }
   __syncthreads();
 
   // 5. Stable slots: the lowest lane of each distinct id claims popc(peers)
   //    rows from the cursor; every peer adds its rank among earlier lanes.
-  const int64_t routes = d.T * d.K;
-  const int32_t u = u0 + w;
-  if (u < U) {
-    const int64_t base = (int64_t)u * kUnitRoutes;
+  //    All rounds are matched first, then all claims are issued back to
+  //    back (the LDS serves one wavefront's atomics in order, so the rounds
+  //    still claim in route order), then all results are shared.
+  if (my_unit < U) {
     const uint64_t lanes_below = (1ull << lane) - 1ull;
-    int64_t ids[kPrepRounds];
-#pragma unroll
-    for (int i = 0; i < kPrepRounds; ++i) {
-      const int64_t s = base + i * kWave + lane;
-      ids[i] = s < routes ? topk_idx[s] : -1;
-    }
     int32_t* cursor = s_cursor + w * E;
-#pragma unroll
-    for (int i = 0; i < kPrepRounds; ++i) {
-      const int64_t id = ids[i];
-      const bool valid = id >= 0 && id < E;
-      const uint32_t key = valid ? (uint32_t)id : 0u;
-      const uint64_t peers = match_peers(key, valid, nbits);
-      const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
-      int32_t first = 0;
-      if (valid && lane == leader) first = atomicAdd(&cursor[key], (int32_t)__popcll(peers));
-      first = __shfl(first, leader);
+    uint64_t peers[kPrepRounds];
+    uint32_t key[kPrepRounds];
+    bool valid[kPrepRounds];
+    static_for<kPrepRounds>([&](auto i) {
+      const int64_t id = unit_id(ids, i, base + i * kWave + lane, routes);
+      valid[i] = id >= 0 && id < E;
+      key[i] = valid[i] ? (uint32_t)id : 0u;
+      peers[i] = match_peers(key[i], valid[i], nbits);
+    });
+    int32_t first[kPrepRounds];
+    int leader[kPrepRounds];
+    static_for<kPrepRounds>([&](auto i) {
+      leader[i] = valid[i] ? __ffsll((unsigned long long)peers[i]) - 1 : lane;
+      first[i] = 0;
+      if (valid[i] && lane == leader[i])
+        first[i] = atomicAdd(&cursor[key[i]], (int32_t)__popcll(peers[i]));
+    });
+    static_for<kPrepRounds>([&](auto i) { first[i] = __shfl(first[i], leader[i]); });
+    static_for<kPrepRounds>([&](auto i) {
       const int64_t s = base + i * kWave + lane;
       if (s < routes) {
-        const int64_t row = (int64_t)first + __popcll(peers & lanes_below);
-        const bool keep = valid && row < d.cap;
+        const int64_t row = (int64_t)first[i] + __popcll(peers[i] & lanes_below);
+        const bool keep = valid[i] && row < d.cap;
         hv.slot[s] = keep ? (int32_t)row : -1;
         if (keep) hv.row_src[row] = (int32_t)s;
       }
-    }
+    });
   }
 
-  // 6. Pad rows of the experts this block owns: row_src = -1 and the list of
-  //    live pad rows (ascending, so the live ones form a prefix).
-  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+  // 6. Pad rows: row_src = -1 and the list of live pad rows (ascending, so
+  //    the live ones form a prefix). One wavefront per expert, spread over
+  //    every wavefront of the grid; its lanes cover the expert's pad rows.
+  for (int e = blockIdx.x * nw + w; e < E; e += gridDim.x * nw) {
     const int64_t lo = (int64_t)s_offs[e] + s_counts[e];
     const int64_t hi_full = s_offs[e + 1];
     const int64_t hi = hi_full < d.cap ? hi_full : d.cap;
-    for (int64_t r = lo + tid; r < hi; r += nthr) {
+    const int32_t p0 = s_padoff[e];
+    for (int64_t r = lo + lane; r < hi; r += kWave) {
       hv.row_src[r] = -1;
-      hv.pad_rows[s_padoff[e] + (r - lo)] = (int32_t)r;
+      hv.pad_rows[p0 + (r - lo)] = (int32_t)r;
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// row vectors and tunables
+// ---------------------------------------------------------------------------
+
+// 16 bytes = 8 bf16 per lane; a wavefront moves 1 KiB per instruction.
+typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
+
+// Work-item width in 1 KiB column blocks, launch shape and cache policy.
+// Rows are streamed through once, so both kernels load and store with the
+// non-temporal hint: it keeps one op's dirty lines from being written back
+// during the next op and measured there.
+#ifndef EP_SCATTER_CH
+#define EP_SCATTER_CH 8
+#endif
+#ifndef EP_REDUCE_CH
+#define EP_REDUCE_CH 2
+#endif
+#ifndef EP_BLOCKS_PER_CU
+#define EP_BLOCKS_PER_CU 64
+#endif
+#ifndef EP_SCATTER_NT_STORE
+#define EP_SCATTER_NT_STORE 1
+#endif
+#ifndef EP_SCATTER_NT_LOAD
+#define EP_SCATTER_NT_LOAD 1
+#endif
+#ifndef EP_REDUCE_NT_STORE
+#define EP_REDUCE_NT_STORE 1
+#endif
+#ifndef EP_REDUCE_NT_LOAD
+#define EP_REDUCE_NT_LOAD 1
+#endif
+#ifndef EP_SCATTER_FENCE
+#define EP_SCATTER_FENCE 1
+#endif
+
+namespace {
+
+template <bool NT>
+__device__ __forceinline__ row16_t load_row16(const row16_t* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_row16(row16_t* p, row16_t v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
+constexpr bool kScatterNtStore = EP_SCATTER_NT_STORE;
+constexpr bool kScatterNtLoad = EP_SCATTER_NT_LOAD;
+constexpr bool kReduceNtStore = EP_REDUCE_NT_STORE;
+constexpr bool kReduceNtLoad = EP_REDUCE_NT_LOAD;
+
+// Lanes past the end of a row (a ragged last column block) load the row's
+// last vector instead, so every load is unconditional and never reads out of
+// bounds; their stores are skipped. No register is zero-filled ahead of a
+// load, which would make the compiler wait for all loads in flight.
+
+// Marks the loaded registers as used, so the compiler waits for the loads
+// once here instead of before every conditional store that follows.
+template <int N>
+__device__ __forceinline__ void consume(const row16_t (&buf)[N]) {
+#if EP_SCATTER_FENCE
+#pragma unroll
+  for (int j = 0; j < N; ++j) asm volatile("" ::"v"(buf[j]));
+#endif
+}
+
+// Index of this wavefront among all wavefronts of the grid, as a scalar.
+__device__ __forceinline__ int64_t wave_index() {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  return (int64_t)blockIdx.x * (blockDim.x / kWave) + w;
+}
+
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // D: dispatch (token rows + weights) and combine_bwd (gradient rows)
 // ---------------------------------------------------------------------------
 
 // Items: (token, column block) for every token, then (pad row, column block)
-// for every live pad row. A token item reads its 1 KiB x CH slice of the row
-// once and stores it to the received row of each valid route.
+// for every live pad row. A token item reads its CH KiB slice of the row
+// once and stores it to the received row of each valid route. With a
+// compile-time top-k the token's slots are wave-uniform scalars.
 template <int KT, int CH>
 __global__ void __launch_bounds__(256)
-scatter_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
+scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
+                    const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
+                    uint32_t* status, const uint16_t* __restrict__ src,
                     const float* __restrict__ w, uint16_t* __restrict__ dst,
                     float* __restrict__ dst_w) {
-  const HandleHeader* h = hv.header;
-  if (!handle_matches(h, d)) {
-    flag_layout_mismatch(hv);
+  const HandleHeader hh = *h;
+  if (!handle_matches(hh, d)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
   const int K = KT > 0 ? KT : d.K;
@@ -364,49 +499,81 @@ scatter_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
   constexpr int64_t CB = (int64_t)kWave * CH;
   const int64_t ncb = (V + CB - 1) / CB;
   const int64_t tok_items = d.T * ncb;
-  const int64_t n_items = tok_items + (int64_t)h->pads_live * ncb;
-  const int64_t wpb = blockDim.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * wpb;
-  const uint4* __restrict__ src4 = reinterpret_cast<const uint4*>(src);
-  uint4* __restrict__ dst4 = reinterpret_cast<uint4*>(dst);
+  const int64_t n_items = tok_items + (int64_t)hh.pads_live * ncb;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const row16_t* __restrict__ src4 = reinterpret_cast<const row16_t*>(src);
+  row16_t* __restrict__ dst4 = reinterpret_cast<row16_t*>(dst);
+  const bool weights = w != nullptr && dst_w != nullptr;
 
-  for (int64_t it = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave; it < n_items;
-       it += nwaves) {
+  for (int64_t it = wave_index(); it < n_items; it += nwaves) {
     if (it < tok_items) {
       const int64_t t = it / ncb;
       const int64_t cb = it - t * ncb;
-      const int32_t sl = lane < K ? hv.slot[t * K + lane] : -1;
-      uint64_t vm = wave_ballot(sl >= 0);
-      if (vm == 0) continue;
-      if (cb == 0 && w != nullptr && dst_w != nullptr && sl >= 0) dst_w[sl] = w[t * K + lane];
       const int64_t v0 = cb * CB + lane;
-      const uint4* srow = src4 + t * V;
-      uint4 buf[CH];
-      static_for<CH>([&](auto j) {
-        const int64_t v = v0 + j * kWave;
-        buf[j] = v < V ? srow[v] : make_uint4(0u, 0u, 0u, 0u);
-      });
-      while (vm) {
-        const int k = __ffsll((unsigned long long)vm) - 1;
-        vm &= vm - 1;
-        const int32_t r = __builtin_amdgcn_readlane(sl, k);
-        uint4* drow = dst4 + (int64_t)r * V;
+      const row16_t* srow = src4 + t * V;
+      if constexpr (KT > 0) {
+        int32_t sl[KT];
+        bool any = false;
+        static_for<KT>([&](auto k) {
+          sl[k] = slot[t * KT + k];
+          any |= sl[k] >= 0;
+        });
+        if (!any) continue;
+        if (cb == 0 && weights) {
+          int32_t mine = -1;
+          static_for<KT>([&](auto k) {
+            if (lane == k) mine = sl[k];
+          });
+          if (mine >= 0) dst_w[mine] = w[t * KT + lane];
+        }
+        row16_t buf[CH];
         static_for<CH>([&](auto j) {
           const int64_t v = v0 + j * kWave;
-          if (v < V) drow[v] = buf[j];
+          buf[j] = load_row16<kScatterNtLoad>(srow + (v < V ? v : V - 1));
         });
+        consume(buf);
+        static_for<KT>([&](auto k) {
+          if (sl[k] >= 0) {
+            row16_t* drow = dst4 + (int64_t)sl[k] * V;
+            static_for<CH>([&](auto j) {
+              const int64_t v = v0 + j * kWave;
+              if (v < V) store_row16<kScatterNtStore>(drow + v, buf[j]);
+            });
+          }
+        });
+      } else {
+        const int32_t sl = lane < K ? slot[t * K + lane] : -1;
+        uint64_t vm = wave_ballot(sl >= 0);
+        if (vm == 0) continue;
+        if (cb == 0 && weights && sl >= 0) dst_w[sl] = w[t * K + lane];
+        row16_t buf[CH];
+        static_for<CH>([&](auto j) {
+          const int64_t v = v0 + j * kWave;
+          buf[j] = load_row16<kScatterNtLoad>(srow + (v < V ? v : V - 1));
+        });
+        consume(buf);
+        while (vm) {
+          const int k = __ffsll((unsigned long long)vm) - 1;
+          vm &= vm - 1;
+          const int32_t r = __builtin_amdgcn_readlane(sl, k);
+          row16_t* drow = dst4 + (int64_t)r * V;
+          static_for<CH>([&](auto j) {
+            const int64_t v = v0 + j * kWave;
+            if (v < V) store_row16<kScatterNtStore>(drow + v, buf[j]);
+          });
+        }
       }
     } else {
       const int64_t pit = it - tok_items;
       const int64_t p = pit / ncb;
       const int64_t cb = pit - p * ncb;
-      const int32_t r = hv.pad_rows[p];
+      const int32_t r = pad_rows[p];
       if (cb == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
-      uint4* drow = dst4 + (int64_t)r * V;
+      row16_t* drow = dst4 + (int64_t)r * V;
       const int64_t v0 = cb * CB + lane;
       static_for<CH>([&](auto j) {
         const int64_t v = v0 + j * kWave;
-        if (v < V) drow[v] = make_uint4(0u, 0u, 0u, 0u);
+        if (v < V) store_row16<kScatterNtStore>(drow + v, row16_t{0u, 0u, 0u, 0u});
       });
     }
   }
@@ -416,19 +583,42 @@ scatter_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
 // D^T: combine (expert rows -> token rows) and dispatch_bwd
 // ---------------------------------------------------------------------------
 
+namespace {
+
+// acc (+)= the 8 bf16 of one 16-byte vector, widened exactly to fp32, with
+// the term kept only if `use`: acc = use ? (have ? acc + x : x) : acc,
+// written as selects so that every buffer is read on every path.
+__device__ __forceinline__ void accumulate8_sel(float (&acc)[8], row16_t v, bool use,
+                                                bool have) {
+  static_for<4>([&](auto q) {
+    constexpr int i = q;
+    const float lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
+    const float slo = acc[2 * i] + lo, shi = acc[2 * i + 1] + hi;
+    acc[2 * i] = use ? (have ? slo : lo) : acc[2 * i];
+    acc[2 * i + 1] = use ? (have ? shi : hi) : acc[2 * i + 1];
+  });
+}
+
+__device__ __forceinline__ row16_t round8(const float (&acc)[8]) {
+  row16_t o;
+  static_for<4>([&](auto q) {
+    constexpr int i = q;
+    o[i] = rne_bf16(acc[2 * i]) | (rne_bf16(acc[2 * i + 1]) << 16);
+  });
+  return o;
+}
+
+}  // namespace
+
 // Items: (token, column block). The valid rows' slices are all loaded first
 // (up to G of them in flight per lane), then summed in fp32 in ascending k
 // from the first valid one, then rounded once.
 template <int KT, int CH>
 __global__ void __launch_bounds__(256)
-reduce_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
-                   const float* __restrict__ g_w, uint16_t* __restrict__ dst,
-                   float* __restrict__ dst_w) {
-  const HandleHeader* h = hv.header;
-  if (!handle_matches(h, d)) {
-    flag_layout_mismatch(hv);
-    return;
-  }
+reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
+                   const int32_t* __restrict__ slot, uint32_t* status,
+                   const uint16_t* __restrict__ src, const float* __restrict__ g_w,
+                   uint16_t* __restrict__ dst, float* __restrict__ dst_w) {
   constexpr int G = KT > 0 ? KT : 8;
   const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
@@ -436,68 +626,90 @@ reduce_rows_kernel(Dims d, HandleView hv, const uint16_t* __restrict__ src,
   constexpr int64_t CB = (int64_t)kWave * CH;
   const int64_t ncb = (V + CB - 1) / CB;
   const int64_t n_items = d.T * ncb;
-  const int64_t wpb = blockDim.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * wpb;
-  const uint4* __restrict__ src4 = reinterpret_cast<const uint4*>(src);
-  uint4* __restrict__ dst4 = reinterpret_cast<uint4*>(dst);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const row16_t* __restrict__ src4 = reinterpret_cast<const row16_t*>(src);
+  row16_t* __restrict__ dst4 = reinterpret_cast<row16_t*>(dst);
+  int64_t it = wave_index();
+  if (it >= n_items) return;
+  // The first item's slots are loaded together with the header (both in
+  // bounds: the slot region has T*K entries whatever the header holds).
+  const HandleHeader hh = *h;
+  int32_t sl_first[KT > 0 ? KT : 1];
+  if constexpr (KT > 0) {
+    const int64_t t = it / ncb;
+    static_for<KT>([&](auto k) { sl_first[k] = slot[t * KT + k]; });
+  }
+  if (!handle_matches(hh, d)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+    return;
+  }
 
-  for (int64_t it = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave; it < n_items;
-       it += nwaves) {
+  bool first = true;
+  for (; it < n_items; it += nwaves) {
     const int64_t t = it / ncb;
     const int64_t cb = it - t * ncb;
-    const int32_t sl = lane < K ? hv.slot[t * K + lane] : -1;
-    const uint64_t vm = wave_ballot(sl >= 0);
-    if (cb == 0 && dst_w != nullptr && lane < K)
-      dst_w[t * K + lane] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
     const int64_t v0 = cb * CB + lane;
     float acc[CH][8];
     bool have = false;
-    for (int k0 = 0; k0 < K; k0 += G) {
-      uint4 buf[G][CH];
-      static_for<G>([&](auto g) {
-        const int k = k0 + g;
-        if (k < K && ((vm >> k) & 1ull)) {
-          const int32_t r = __builtin_amdgcn_readlane(sl, k);
-          const uint4* srow = src4 + (int64_t)r * V;
+    if constexpr (KT > 0) {
+      int32_t sl[KT];
+      static_for<KT>([&](auto k) { sl[k] = first ? sl_first[k] : slot[t * KT + k]; });
+      first = false;
+      if (cb == 0 && dst_w != nullptr) {
+        int32_t mine = -1;
+        static_for<KT>([&](auto k) {
+          if (lane == k) mine = sl[k];
+        });
+        if (lane < KT) dst_w[t * KT + lane] = (mine >= 0 && g_w != nullptr) ? g_w[mine] : 0.0f;
+      }
+      // Loads only for valid routes (uniform branches); the sums below read
+      // every buffer and keep or drop each term with a select, so no buffer
+      // is left possibly in flight at the end of an item.
+      row16_t buf[KT][CH];
+      static_for<KT>([&](auto k) {
+        if (sl[k] >= 0) {
+          const row16_t* srow = src4 + (int64_t)sl[k] * V;
           static_for<CH>([&](auto j) {
             const int64_t v = v0 + j * kWave;
-            buf[g][j] = v < V ? srow[v] : make_uint4(0u, 0u, 0u, 0u);
+            buf[k][j] = load_row16<kReduceNtLoad>(srow + (v < V ? v : V - 1));
           });
         }
       });
-      static_for<G>([&](auto g) {
-        const int k = k0 + g;
-        if (k < K && ((vm >> k) & 1ull)) {
-          static_for<CH>([&](auto j) {
-            const uint32_t wd[4] = {buf[g][j].x, buf[g][j].y, buf[g][j].z, buf[g][j].w};
-            static_for<4>([&](auto q) {
-              const float lo = bf16_lo(wd[q]), hi = bf16_hi(wd[q]);
-              if (have) {
-                acc[j][2 * q] += lo;
-                acc[j][2 * q + 1] += hi;
-              } else {
-                acc[j][2 * q] = lo;
-                acc[j][2 * q + 1] = hi;
-              }
+      static_for<KT>([&](auto k) {
+        const bool use = sl[k] >= 0;
+        static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[k][j], use, have); });
+        have |= use;
+      });
+    } else {
+      const int32_t sl = lane < K ? slot[t * K + lane] : -1;
+      const uint64_t vm = wave_ballot(sl >= 0);
+      if (cb == 0 && dst_w != nullptr && lane < K)
+        dst_w[t * K + lane] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
+      for (int k0 = 0; k0 < K; k0 += G) {
+        row16_t buf[G][CH];
+        static_for<G>([&](auto g) {
+          const int k = k0 + g;
+          if (k < K && ((vm >> k) & 1ull)) {
+            const int32_t r = __builtin_amdgcn_readlane(sl, k);
+            const row16_t* srow = src4 + (int64_t)r * V;
+            static_for<CH>([&](auto j) {
+              const int64_t v = v0 + j * kWave;
+              buf[g][j] = load_row16<kReduceNtLoad>(srow + (v < V ? v : V - 1));
             });
-          });
-          have = true;
-        }
-      });
+          }
+        });
+        static_for<G>([&](auto g) {
+          const int k = k0 + g;
+          const bool use = k < K && ((vm >> k) & 1ull);
+          static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[g][j], use, have); });
+          have |= use;
+        });
+      }
     }
-    uint4* drow = dst4 + t * V;
+    row16_t* drow = dst4 + t * V;
     static_for<CH>([&](auto j) {
       const int64_t v = v0 + j * kWave;
-      if (v < V) {
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
-        if (have) {
-          o.x = rne_bf16(acc[j][0]) | (rne_bf16(acc[j][1]) << 16);
-          o.y = rne_bf16(acc[j][2]) | (rne_bf16(acc[j][3]) << 16);
-          o.z = rne_bf16(acc[j][4]) | (rne_bf16(acc[j][5]) << 16);
-          o.w = rne_bf16(acc[j][6]) | (rne_bf16(acc[j][7]) << 16);
-        }
-        drow[v] = o;
-      }
+      if (v < V) store_row16<kReduceNtStore>(drow + v, have ? round8(acc[j]) : row16_t{0u, 0u, 0u, 0u});
     });
   }
 }
@@ -520,10 +732,10 @@ size_t slots_lds_bytes(int E, int nw) {
   return sizeof(int32_t) * (size_t)(4 * E + 2 + 2 * kWave * nw + nw * E);
 }
 
-constexpr int kScatterCH = 2;
-constexpr int kReduceCH = 1;
+constexpr int kScatterCH = EP_SCATTER_CH;
+constexpr int kReduceCH = EP_REDUCE_CH;
 constexpr int kBlock = 256;
-constexpr int kBlocksPerCU = 8;
+constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
 
 int grid_for(int64_t items, int num_cus) {
   const int64_t waves_per_block = kBlock / kWave;
@@ -538,7 +750,8 @@ template <int KT>
 hipError_t scatter_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* w,
                      uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((scatter_rows_kernel<KT, kScatterCH>), dim3(grid), dim3(kBlock), 0,
-                     stream, d, hv, src, w, dst, dst_w);
+                     stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status, src, w,
+                     dst, dst_w);
   return hipGetLastError();
 }
 
@@ -546,7 +759,7 @@ template <int KT>
 hipError_t reduce_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* g_w,
                     uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH>), dim3(grid), dim3(kBlock), 0,
-                     stream, d, hv, src, g_w, dst, dst_w);
+                     stream, d, hv.header, hv.slot, &hv.header->status, src, g_w, dst, dst_w);
   return hipGetLastError();
 }
 
