@@ -63,6 +63,10 @@ class Layout(C.Structure):
         return self.num_experts
 
     @property
+    def A(self):
+        return self.alignment
+
+    @property
     def H(self):
         return self.hidden
 

@@ -1,0 +1,104 @@
+"""Autograd-aware dispatch and combine on top of the C ABI.
+
+The PyTorch page of the pages ("[PyTorch] Expert Parallelism: PyTorch
+wrapper + autograd ops with symm-mem zero-copy", section "Public Python API")
+exposes dispatch and combine as differentiable ops with a per-call routing
+state (one per in-flight microbatch). This module does the same for the
+one-GPU library: `EpRouting` holds the layout and the handle of one prepared
+routing, `dispatch` and `combine` are `torch.autograd.Function`s whose
+backward passes call `ep_dispatch_bwd` and `ep_combine_bwd`.
+
+Outputs are allocated with PyTorch; every step of the computation runs in the
+library's kernels. A gradient that does not flow into the received weights
+arrives here as None and is passed to the library as NULL (the weight
+gradient is then zero), the case the pages' review flagged (section
+"Greptile Summary").
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (Layout, combine as _combine, combine_bwd as _combine_bwd,
+               dispatch as _dispatch, dispatch_bwd as _dispatch_bwd, new_handle, prepare,
+               recv_capacity_worst)
+
+
+class EpRouting:
+    """One prepared routing: layout, handle, token counts and segment offsets."""
+
+    def __init__(self, topk_idx: torch.Tensor, num_experts: int, alignment: int, hidden: int,
+                 recv_capacity: Optional[int] = None):
+        if topk_idx.dtype != torch.int64:
+            raise TypeError("topk_idx must be int64")
+        T, K = topk_idx.shape
+        if recv_capacity is None:
+            recv_capacity = recv_capacity_worst(T, K, num_experts, alignment)
+        self.layout = Layout(T, K, num_experts, alignment, hidden, recv_capacity)
+        self.handle = new_handle(self.layout, device=topk_idx.device)
+        self.token_counts = torch.empty(num_experts, dtype=torch.int32, device=topk_idx.device)
+        self.expert_offsets = torch.empty(num_experts + 1, dtype=torch.int32,
+                                          device=topk_idx.device)
+        prepare(self.layout, topk_idx.contiguous(), self.token_counts, self.handle,
+                self.expert_offsets)
+
+
+class _Dispatch(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, tokens, topk_weights, routing: EpRouting):
+        L = routing.layout
+        recv = torch.empty(L.cap, L.H, dtype=tokens.dtype, device=tokens.device)
+        recv_w = torch.empty(L.cap, dtype=torch.float32, device=tokens.device)
+        _dispatch(L, routing.handle, tokens.contiguous(), topk_weights.contiguous(), recv,
+                  recv_w)
+        ctx.routing = routing
+        ctx.set_materialize_grads(False)      # an unused output's gradient stays None
+        return recv, recv_w
+
+    @staticmethod
+    def backward(ctx, g_recv, g_recv_w):
+        routing = ctx.routing
+        L = routing.layout
+        grad_tokens = None
+        grad_w = None
+        want_tokens, want_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if want_tokens or want_w:
+            if g_recv is None:
+                g_recv = torch.zeros(L.cap, L.H, dtype=torch.bfloat16,
+                                     device=routing.handle.device)
+            grad_tokens = torch.empty(L.T, L.H, dtype=g_recv.dtype, device=g_recv.device)
+            grad_w = torch.empty(L.T, L.K, dtype=torch.float32, device=g_recv.device)
+            _dispatch_bwd(L, routing.handle, g_recv.contiguous(),
+                          None if g_recv_w is None else g_recv_w.contiguous(), grad_tokens,
+                          grad_w)
+        return (grad_tokens if want_tokens else None, grad_w if want_w else None, None)
+
+
+class _Combine(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, expert_out, routing: EpRouting):
+        L = routing.layout
+        result = torch.empty(L.T, L.H, dtype=expert_out.dtype, device=expert_out.device)
+        _combine(L, routing.handle, expert_out.contiguous(), result)
+        ctx.routing = routing
+        return result
+
+    @staticmethod
+    def backward(ctx, g_result):
+        routing = ctx.routing
+        L = routing.layout
+        grad = torch.empty(L.cap, L.H, dtype=g_result.dtype, device=g_result.device)
+        _combine_bwd(L, routing.handle, g_result.contiguous(), grad)
+        return grad, None
+
+
+def dispatch(tokens: torch.Tensor, topk_weights: torch.Tensor, routing: EpRouting):
+    """(recv_tokens [cap,H], recv_topk_weights [cap]); rows past the live total
+    are unspecified."""
+    return _Dispatch.apply(tokens, topk_weights, routing)
+
+
+def combine(expert_out: torch.Tensor, routing: EpRouting) -> torch.Tensor:
+    """Unweighted sum of each token's expert rows, [T,H]."""
+    return _Combine.apply(expert_out, routing)

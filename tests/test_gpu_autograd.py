@@ -1,0 +1,114 @@
+"""Autograd dispatch/combine: forward + backward round trips and the VJP.
+
+Follows the test list of "[PyTorch] Expert Parallelism: PyTorch wrapper +
+autograd ops with symm-mem zero-copy", section "Testing": identity round trip,
+dispatch forward+backward VJP, full forward+backward round trip, multi-
+iteration bit stability, several routings in flight at once (a pipeline's
+microbatches); and the None weight-gradient case of its review.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from combine_ep_prepare_amd import autograd as epa
+from combine_ep_prepare_amd import handle_maps
+from gpu_harness import host_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+
+
+def _setup(name="dsv3", T=600, H=512, seed=0, small_ints=False):
+    cfg = workloads.scaled(workloads.CONFIGS[name], T=T, H=H)
+    r = workloads.make_routing(cfg, seed)
+    if small_ints:
+        rng = np.random.default_rng(seed)
+        x = torch.from_numpy(workloads.small_int_bf16(rng, (T, H)).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    else:
+        x = workloads.randn_bf16_torch((T, H), 10 + seed)
+    idx = torch.from_numpy(r.topk_idx).cuda()
+    w = torch.from_numpy(r.topk_weights).cuda()
+    return cfg, r, idx, x, w
+
+
+def test_identity_round_trip_and_none_weight_grad():
+    cfg, r, idx, x, w = _setup(small_ints=True)
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H)
+    x = x.clone().requires_grad_(True)
+    w = w.clone().requires_grad_(True)
+    recv, recv_w = epa.dispatch(x, w, routing)
+    y = epa.combine(recv, routing)              # identity experts, weights unused
+    n = (r.topk_idx >= 0).sum(axis=1)
+    want = (x.detach().float() * torch.from_numpy(n).cuda()[:, None].float()).to(torch.bfloat16)
+    assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+    g = torch.from_numpy(workloads.small_int_bf16(np.random.default_rng(5),
+                                                  (cfg.T, cfg.H)).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    y.backward(g)
+    # d(combine(dispatch(x)))/dx applied to g is n_valid * g, exactly for small ints
+    want_g = (g.float() * torch.from_numpy(n).cuda()[:, None].float()).to(torch.bfloat16)
+    assert torch.equal(x.grad.view(torch.int16), want_g.view(torch.int16))
+    # no gradient reached the received weights: the weight gradient is zero
+    assert w.grad is not None and torch.count_nonzero(w.grad) == 0
+
+
+def test_weighted_round_trip_grads_match_oracle():
+    cfg, r, idx, x, w = _setup(name="qwen3", T=500, H=256, seed=1)
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H)
+    x = x.clone().requires_grad_(True)
+    w = w.clone().requires_grad_(True)
+    recv, recv_w = epa.dispatch(x, w, routing)
+    recv.retain_grad()
+    recv_w.retain_grad()
+    expert_out = (recv.float() * recv_w[:, None]).to(torch.bfloat16)   # caller's pre-multiply
+    y = epa.combine(expert_out, routing)
+    g = workloads.randn_bf16_torch((cfg.T, cfg.H), 77)
+    (y.float() * g.float()).sum().backward()
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, routing.layout.cap)
+    live = p.live
+    # forward
+    o_recv, o_recv_w = oracle.dispatch(p, host_bf16(x.detach()), r.topk_weights)
+    assert np.array_equal(host_bf16(recv.detach())[:live], o_recv[:live])
+    assert np.array_equal(recv_w.detach().cpu().numpy()[:live].view(np.uint32),
+                          o_recv_w[:live].view(np.uint32))
+    assert np.array_equal(host_bf16(y.detach()), oracle.combine(p, host_bf16(expert_out)))
+    # backward: the token and weight grads are dispatch_bwd of what reached recv
+    g_recv = host_bf16(recv.grad)
+    g_recv_w = recv_w.grad.cpu().numpy()
+    o_gt, o_gw = oracle.dispatch_bwd(p, g_recv, g_recv_w)
+    assert np.array_equal(host_bf16(x.grad), o_gt)
+    assert np.array_equal(w.grad.cpu().numpy().view(np.uint32), o_gw.view(np.uint32))
+    # and recv.grad itself came from combine_bwd of g, then the multiply's backward
+    m = handle_maps(routing.layout, routing.handle)
+    slot = m["slot"].cpu().numpy()
+    assert (slot[(r.topk_idx < 0).reshape(-1)] == -1).all()
+
+
+def test_bit_stable_and_interleaved_routings():
+    # three routings in flight at once (as a pipeline's microbatches would be),
+    # run in interleaved order, repeated: results are bit-identical each time
+    states = [_setup(name="dsv3", T=300 + 50 * i, H=256, seed=i) for i in range(3)]
+    first = None
+    for rep in range(3):
+        routings = [epa.EpRouting(idx, cfg.E, cfg.A, cfg.H) for cfg, r, idx, x, w in states]
+        recvs = [epa.dispatch(s[3], s[4], rt)[0] for s, rt in zip(states, routings)]
+        outs = [epa.combine(rv, rt) for rv, rt in zip(reversed(recvs), reversed(routings))]
+        outs = [o.clone() for o in reversed(outs)]
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for (cfg, r, idx, x, w), o in zip(states, first):
+        n = torch.from_numpy((r.topk_idx >= 0).sum(axis=1)).cuda()
+        want = (x.float() * n[:, None].float()).to(torch.bfloat16)
+        assert torch.equal(o.view(torch.int16), want.view(torch.int16))

@@ -1,0 +1,125 @@
+"""The whole path captured in a HIP graph and replayed.
+
+The per-step calls are allocation-free and never synchronise ("[PyTorch]
+Expert Parallelism: PyTorch wrapper + autograd ops with symm-mem zero-copy",
+section "Testing": CUDA graph capture; "Expert Parallelism: common C API +
+NCCL EP backend", section "Per-step (allocation-free, CUDA-graph
+capturable)"). The graph is replayed several times on new routing and new
+token rows written into its static input buffers, with eager work and
+synchronisations in between, and every replay is compared bit for bit with an
+eager run and with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_prepare_amd as ep
+import oracle
+import workloads
+from gpu_harness import host_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+
+
+class Step:
+    """Static buffers of one step: prepare, dispatch, combine, combine_bwd,
+    dispatch_bwd on a fixed layout."""
+
+    def __init__(self, L: ep.Layout):
+        d = "cuda"
+        self.L = L
+        self.handle = ep.new_handle(L)
+        self.idx = torch.zeros(L.T, L.K, dtype=torch.int64, device=d)
+        self.w = torch.zeros(L.T, L.K, dtype=torch.float32, device=d)
+        self.x = torch.zeros(L.T, L.H, dtype=torch.bfloat16, device=d)
+        self.expert_out = torch.zeros(L.cap, L.H, dtype=torch.bfloat16, device=d)
+        self.g_res = torch.zeros(L.T, L.H, dtype=torch.bfloat16, device=d)
+        self.g_recv = torch.zeros(L.cap, L.H, dtype=torch.bfloat16, device=d)
+        self.g_recv_w = torch.zeros(L.cap, dtype=torch.float32, device=d)
+        self.counts = torch.zeros(L.E, dtype=torch.int32, device=d)
+        self.offsets = torch.zeros(L.E + 1, dtype=torch.int32, device=d)
+        self.recv = torch.zeros(L.cap, L.H, dtype=torch.bfloat16, device=d)
+        self.recv_w = torch.zeros(L.cap, dtype=torch.float32, device=d)
+        self.res = torch.zeros(L.T, L.H, dtype=torch.bfloat16, device=d)
+        self.g_exp = torch.zeros(L.cap, L.H, dtype=torch.bfloat16, device=d)
+        self.g_tok = torch.zeros(L.T, L.H, dtype=torch.bfloat16, device=d)
+        self.g_w = torch.zeros(L.T, L.K, dtype=torch.float32, device=d)
+
+    def run(self):
+        L = self.L
+        ep.prepare(L, self.idx, self.counts, self.handle, self.offsets)
+        ep.dispatch(L, self.handle, self.x, self.w, self.recv, self.recv_w)
+        ep.combine(L, self.handle, self.expert_out, self.res)
+        ep.combine_bwd(L, self.handle, self.g_res, self.g_exp)
+        ep.dispatch_bwd(L, self.handle, self.g_recv, self.g_recv_w, self.g_tok, self.g_w)
+
+    def load(self, other: "Step"):
+        for name in ("idx", "w", "x", "expert_out", "g_res", "g_recv", "g_recv_w"):
+            getattr(self, name).copy_(getattr(other, name))
+
+    def outputs(self):
+        return [self.counts, self.offsets, self.recv, self.recv_w, self.res, self.g_exp,
+                self.g_tok, self.g_w]
+
+
+def _fill(step: Step, cfg, seed: int):
+    c = workloads.scaled(cfg, T=step.L.T, H=step.L.H)
+    r = workloads.make_routing(c, seed)
+    step.idx.copy_(torch.from_numpy(r.topk_idx))
+    step.w.copy_(torch.from_numpy(r.topk_weights))
+    step.x.copy_(workloads.randn_bf16_torch((step.L.T, step.L.H), 100 + seed))
+    step.expert_out.copy_(workloads.randn_bf16_torch((step.L.cap, step.L.H), 200 + seed))
+    step.g_res.copy_(workloads.randn_bf16_torch((step.L.T, step.L.H), 300 + seed))
+    step.g_recv.copy_(workloads.randn_bf16_torch((step.L.cap, step.L.H), 400 + seed))
+    step.g_recv_w.copy_(workloads.randn_bf16_torch((step.L.cap,), 500 + seed).float())
+    return r
+
+
+def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("name,T,H", [("dsv3", 700, 1024), ("masked_hot", 2048, 512)])
+def test_graph_replays_match_eager_and_oracle(name, T, H):
+    cfg = workloads.CONFIGS[name]
+    cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
+    L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap)
+    g_step, e_step = Step(L), Step(L)
+    _fill(g_step, cfg, 0)
+    # warm up on a side stream, then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g_step.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_step.run()
+    torch.cuda.synchronize()
+    for seed in range(1, 5):
+        log(f"graph {name}: replay with routing seed {seed}")
+        r = _fill(g_step, cfg, seed)
+        e_step.load(g_step)
+        e_step.run()                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(g_step.outputs(), e_step.outputs()):
+            assert _same(a, b), f"replay {seed} differs from eager"
+        assert ep.read_status(g_step.handle) == 0
+        if seed == 2:
+            p = oracle.prepare(r.topk_idx, L.E, L.A, cap)
+            assert np.array_equal(g_step.counts.cpu().numpy(), p.counts)
+            live = p.live
+            o_recv, _ = oracle.dispatch(p, host_bf16(g_step.x), r.topk_weights)
+            assert np.array_equal(host_bf16(g_step.recv)[:live], o_recv[:live])
+            assert np.array_equal(host_bf16(g_step.res),
+                                  oracle.combine(p, host_bf16(g_step.expert_out)))
