@@ -55,6 +55,11 @@ def _load():
         lib.ep_oracle_combine.restype = C.c_int
         lib.ep_oracle_dispatch_bwd.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp]
         lib.ep_oracle_dispatch_bwd.restype = C.c_int
+        lib.ep_oracle_combine_weighted.argtypes = [i64, i32, i64, vp, vp, vp, vp]
+        lib.ep_oracle_combine_weighted.restype = C.c_int
+        lib.ep_oracle_combine_weighted_bwd.argtypes = [i64, i32, i64, i64, i64, vp, vp, vp, vp,
+                                                       vp, vp, vp]
+        lib.ep_oracle_combine_weighted_bwd.restype = C.c_int
         lib.ep_oracle_f32_to_bf16.argtypes = [C.c_float]
         lib.ep_oracle_f32_to_bf16.restype = C.c_uint16
         lib.ep_oracle_bf16_to_f32.argtypes = [C.c_uint16]
@@ -176,3 +181,38 @@ def dispatch_bwd(prep: Prepared, g_recv: np.ndarray, g_recv_w: np.ndarray | None
                                         _p(gt), _p(gw))
     _check(rc, "dispatch_bwd")
     return gt, gw
+
+
+def combine_weighted(prep: Prepared, rows: np.ndarray, w: np.ndarray, T: int | None = None):
+    """bf16 [T,H]: sum over valid k (ascending) of w[r] * rows[r], first term a
+    product, later terms fused multiply-adds, one rounding to bf16."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    H = rows.shape[1]
+    T = prep.T if T is None else T
+    out = np.empty((T, H), np.uint16)
+    rc = _load().ep_oracle_combine_weighted(T, prep.K, H, _p(prep.slot), _p(rows), _p(w),
+                                            _p(out))
+    _check(rc, "combine_weighted")
+    return out
+
+
+def combine_weighted_bwd(prep: Prepared, g: np.ndarray, rows: np.ndarray | None,
+                         w: np.ndarray, init: np.ndarray | None = None):
+    """(grad_rows bf16 [cap,H] with rows past the live total left at ``init``,
+    grad_w float64 [cap] or None, sum of |terms| float64 [cap] or None)."""
+    g = np.ascontiguousarray(g, dtype=np.uint16)
+    T, H = g.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    grad_rows = (np.zeros((prep.cap, H), np.uint16) if init is None
+                 else np.array(init, dtype=np.uint16, copy=True))
+    gw = aw = None
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.uint16)
+        gw = np.zeros(prep.cap, np.float64)
+        aw = np.zeros(prep.cap, np.float64)
+    rc = _load().ep_oracle_combine_weighted_bwd(T, prep.K, H, prep.cap, prep.total,
+                                                _p(prep.row_src), _p(g), _p(rows), _p(w),
+                                                _p(grad_rows), _p(gw), _p(aw))
+    _check(rc, "combine_weighted_bwd")
+    return grad_rows, gw, aw

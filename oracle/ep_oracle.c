@@ -48,6 +48,7 @@
  *    for any NaN (the sign of a NaN produced by an add is not portable).
  */
 #include <fenv.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -266,6 +267,85 @@ int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, const int32_t* slot,
   for (int64_t s = 0; s < T * (int64_t)K; ++s) {
     int32_t r = slot[s];
     grad_w[s] = (r >= 0 && g_recv_w) ? g_recv_w[r] : 0.0f;
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Weighted combine (the weight multiply folded into combine, as the review
+ * of "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with
+ * symm-mem zero-copy" asks, so the caller no longer pre-multiplies; the
+ * transformers EP implementations return this weighted output directly).
+ * For each token, over its valid routes in ascending k with received row r:
+ *   acc = w[r] * y[r]                     (first valid route: one fp32 product)
+ *   acc = fmaf(w[r], y[r], acc)           (later routes: one fused rounding)
+ * then one round-to-nearest-even to bf16; +0 if no valid route.
+ *   rows  bf16 [cap*H], w f32 [cap], out bf16 [T*H]
+ */
+int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, const int32_t* slot,
+                               const uint16_t* rows, const float* w, uint16_t* out) {
+  if (T < 0 || K < 1 || H < 1) return ORACLE_ERR_ARGS;
+  if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      int have = 0;
+      for (int32_t k = 0; k < K; ++k) {
+        int32_t r = slot[t * K + k];
+        if (r < 0) continue;
+        float y = bf16_to_float(rows[(int64_t)r * H + h]);
+        if (!have) {
+          acc = w[r] * y;
+          have = 1;
+        } else {
+          acc = fmaf(w[r], y, acc);
+        }
+      }
+      out[t * H + h] = have ? ep_oracle_f32_to_bf16(acc) : (uint16_t)0;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Backward of the weighted combine, for every live received row r holding
+ * route s of token t = s / K:
+ *   grad_rows[r, h] = bf16(fp32(w[r] * g[t, h]))       (pads: +0)
+ *   grad_w[r]       = sum over h of g[t, h] * rows[r, h] (pads: +0)
+ * The weight gradient is a dot product whose summation order the method does
+ * not fix; the oracle returns it exactly rounded from a double-precision sum
+ * (grad_w64), and the tests compare the GPU's fp32 result within the
+ * summation error bound. grad_w64 may be NULL (then rows is not read).
+ */
+int ep_oracle_combine_weighted_bwd(int64_t T, int32_t K, int64_t H, int64_t cap,
+                                   int64_t total, const int32_t* row_src, const uint16_t* g,
+                                   const uint16_t* rows, const float* w, uint16_t* grad_rows,
+                                   double* grad_w64, double* abs_dot64) {
+  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0) return ORACLE_ERR_ARGS;
+  if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
+  const int64_t live = total < cap ? total : cap;
+  for (int64_t r = 0; r < live; ++r) {
+    int32_t s = row_src[r];
+    if (s < 0) {
+      for (int64_t h = 0; h < H; ++h) grad_rows[r * H + h] = 0;
+      if (grad_w64) grad_w64[r] = 0.0;
+      if (abs_dot64) abs_dot64[r] = 0.0;
+      continue;
+    }
+    int64_t t = s / K;
+    double dot = 0.0, adot = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      float gv = bf16_to_float(g[t * H + h]);
+      float p = w[r] * gv;
+      grad_rows[r * H + h] = ep_oracle_f32_to_bf16(p);
+      if (grad_w64) {
+        double term = (double)gv * (double)bf16_to_float(rows[r * H + h]);
+        dot += term;
+        adot += term < 0 ? -term : term;
+      }
+    }
+    if (grad_w64) grad_w64[r] = dot;
+    if (abs_dot64) abs_dot64[r] = adot;
   }
   return ORACLE_OK;
 }

@@ -427,3 +427,84 @@ def test_reversed_accumulation_order_is_caught():
     rev = np.float32(np.float32(rows[2] + rows[1]) + rows[0])
     assert brute.f32_to_bf16_torch(np.array([fwd]))[0] == int(c["combine"][0][0], 16)
     assert brute.f32_to_bf16_torch(np.array([rev]))[0] != int(c["combine"][0][0], 16)
+
+
+# --------------------------------------------------------------------------
+# weighted combine and its backward
+# --------------------------------------------------------------------------
+
+def _wbits(a):
+    return np.array([int(v, 16) for v in a], np.uint32).view(np.float32)
+
+
+def test_golden_combine_weighted():
+    g = json.load(open(os.path.join(GOLDEN, "combine_weighted.json")))
+    for c in g["forward_cases"]:
+        p = oracle.prepare(np.array(c["topk_idx"], np.int64), c["E"], c["A"], 16)
+        w = np.zeros(16, np.float32)
+        w[:len(c["w_bits"])] = _wbits(c["w_bits"])
+        rows = np.zeros((16, c["H"]), np.uint16)
+        rows[:len(c["rows"])] = _hex(c["rows"])
+        assert np.array_equal(oracle.combine_weighted(p, rows, w), _hex(c["combine_weighted"])), \
+            c["name"]
+    for c in g["backward_cases"]:
+        p = oracle.prepare(np.array(c["topk_idx"], np.int64), c["E"], c["A"], 16)
+        w = np.zeros(16, np.float32)
+        w[:len(c["w_bits"])] = _wbits(c["w_bits"])
+        gr, _, _ = oracle.combine_weighted_bwd(p, _hex(c["g"]), None, w)
+        assert np.array_equal(gr[:p.live], _hex(c["grad_rows"])), c["name"]
+
+
+def test_weighted_with_unit_and_power_of_two_weights():
+    # w = 1: the weighted ops are the unweighted ones; w = 2^m: exact scaling,
+    # so they equal the unweighted ops on exactly pre-scaled rows.
+    cfg = workloads.scaled(workloads.CONFIGS["dsv3"], T=300, H=64)
+    r = workloads.make_routing(cfg)
+    idx = r.topk_idx.copy()
+    idx[::9, 2] = -1
+    cap = oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A)
+    p = oracle.prepare(idx, cfg.E, cfg.A, cap)
+    rng = np.random.default_rng(21)
+    Y = workloads.randn_bf16(rng, (cap, cfg.H))
+    g = workloads.randn_bf16(rng, (cfg.T, cfg.H))
+    ones = np.ones(cap, np.float32)
+    assert np.array_equal(oracle.combine_weighted(p, Y, ones), oracle.combine(p, Y))
+    gr, _, _ = oracle.combine_weighted_bwd(p, g, None, ones)
+    assert np.array_equal(gr[:p.live], oracle.combine_bwd(p, g)[:p.live])
+    m = rng.integers(-3, 4, size=cap)
+    w2 = (2.0 ** m).astype(np.float32)
+    Ys = brute.f32_to_bf16_torch(brute.bf16_to_f32_np(Y) * w2[:, None])     # exact
+    assert np.array_equal(oracle.combine_weighted(p, Y, w2), oracle.combine(p, Ys))
+    gr2, _, _ = oracle.combine_weighted_bwd(p, g, None, w2)
+    want = brute.f32_to_bf16_torch(brute.bf16_to_f32_np(oracle.combine_bwd(p, g)) *
+                                   w2[:, None])
+    live = p.live
+    pad = p.row_src[:live] < 0
+    assert np.array_equal(gr2[:live][~pad], want[:live][~pad])
+    assert (gr2[:live][pad] == 0).all()
+
+
+def test_weighted_adjoints_exact_small_ints():
+    # For small-integer rows, gradients and weights every product and sum is
+    # exact, so <combine_w(Y), g> = <Y, dY> = sum_r w_r dw_r exactly.
+    cfg = workloads.scaled(workloads.CONFIGS["qwen3"], T=200, H=16)
+    r = workloads.make_routing(cfg)
+    cap = oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A)
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, cap)
+    rng = np.random.default_rng(8)
+    Y = workloads.small_int_bf16(rng, (cap, cfg.H), 8)
+    g = workloads.small_int_bf16(rng, (cfg.T, cfg.H), 8)
+    w = rng.integers(-4, 5, size=cap).astype(np.float32)
+    out = oracle.combine_weighted(p, Y, w)
+    lhs = pins.dot_f64(_f32_of(out), _f32_of(g))
+    gr, gw, _ = oracle.combine_weighted_bwd(p, g, Y, w)
+    live = p.live
+    assert lhs == pins.dot_f64(_f32_of(Y[:live]), _f32_of(gr[:live]))
+    assert lhs == float(np.dot(w[:live].astype(np.float64), gw[:live]))
+    # the weight gradient by an independent integer dot
+    Yi = _f32_of(Y).astype(np.int64)
+    gi = _f32_of(g).astype(np.int64)
+    for rr in range(live):
+        s = p.row_src[rr]
+        want = 0 if s < 0 else int(np.dot(gi[s // cfg.K], Yi[rr]))
+        assert gw[rr] == want
