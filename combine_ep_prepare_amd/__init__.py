@@ -37,8 +37,8 @@ STATUS_LAYOUT = 4
 
 ENTRY_POINTS = ("ep_recv_capacity_worst", "ep_handle_mem_size", "ep_handle_regions",
                 "ep_prepare", "ep_dispatch",
-                "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_read_status",
-                "ep_status_str")
+                "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_weighted",
+                "ep_combine_weighted_bwd", "ep_read_status", "ep_status_str")
 
 
 class Layout(C.Structure):
@@ -106,9 +106,12 @@ def _load_library(path: str = LIB_PATH):
     lib.ep_combine.argtypes = [lp, vp, sz, vp, vp, vp]
     lib.ep_dispatch_bwd.argtypes = [lp, vp, sz, vp, vp, vp, vp, vp]
     lib.ep_combine_bwd.argtypes = [lp, vp, sz, vp, vp, vp]
+    lib.ep_combine_weighted.argtypes = [lp, vp, sz, vp, vp, vp, vp]
+    lib.ep_combine_weighted_bwd.argtypes = [lp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.ep_read_status.argtypes = [vp, C.POINTER(C.c_uint32), vp]
     for name in ("ep_prepare", "ep_dispatch", "ep_combine", "ep_dispatch_bwd",
-                 "ep_combine_bwd", "ep_read_status"):
+                 "ep_combine_bwd", "ep_combine_weighted", "ep_combine_weighted_bwd",
+                 "ep_read_status"):
         getattr(lib, name).restype = C.c_int
     lib.ep_status_str.argtypes = [C.c_int]
     lib.ep_status_str.restype = C.c_char_p
@@ -247,6 +250,34 @@ def combine_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
     _need(grad_expert_out, "grad_expert_out", torch.bfloat16, (layout.cap, layout.H))
     _check(lib.ep_combine_bwd(C.byref(layout), _ptr(handle), handle.numel(), _ptr(grad),
                               _ptr(grad_expert_out), _stream(stream)), "ep_combine_bwd")
+
+
+def combine_weighted(layout: Layout, handle: torch.Tensor, expert_out: torch.Tensor,
+                     recv_topk_weights: torch.Tensor, result: torch.Tensor, stream=None):
+    _need(handle, "handle", torch.uint8)
+    _need(expert_out, "expert_out", torch.bfloat16, (layout.cap, layout.H))
+    _need(recv_topk_weights, "recv_topk_weights", torch.float32, (layout.cap,))
+    _need(result, "result", torch.bfloat16, (layout.T, layout.H))
+    _check(lib.ep_combine_weighted(C.byref(layout), _ptr(handle), handle.numel(),
+                                   _ptr(expert_out), _ptr(recv_topk_weights), _ptr(result),
+                                   _stream(stream)), "ep_combine_weighted")
+
+
+def combine_weighted_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
+                         expert_out: Optional[torch.Tensor], recv_topk_weights: torch.Tensor,
+                         grad_expert_out: torch.Tensor,
+                         grad_recv_topk_weights: Optional[torch.Tensor] = None, stream=None):
+    _need(handle, "handle", torch.uint8)
+    _need(grad, "grad", torch.bfloat16, (layout.T, layout.H))
+    _need(expert_out, "expert_out", torch.bfloat16, (layout.cap, layout.H), allow_none=True)
+    _need(recv_topk_weights, "recv_topk_weights", torch.float32, (layout.cap,))
+    _need(grad_expert_out, "grad_expert_out", torch.bfloat16, (layout.cap, layout.H))
+    _need(grad_recv_topk_weights, "grad_recv_topk_weights", torch.float32, (layout.cap,),
+          allow_none=True)
+    _check(lib.ep_combine_weighted_bwd(C.byref(layout), _ptr(handle), handle.numel(),
+                                       _ptr(grad), _ptr(expert_out), _ptr(recv_topk_weights),
+                                       _ptr(grad_expert_out), _ptr(grad_recv_topk_weights),
+                                       _stream(stream)), "ep_combine_weighted_bwd")
 
 
 def read_status(handle: torch.Tensor, stream=None) -> int:

@@ -179,8 +179,8 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(expert_out) || !aligned16(result)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  if (launch_reduce_rows(d, hv, expert_out, nullptr, result, nullptr, num_cus, stream) !=
-      hipSuccess)
+  if (launch_reduce_rows(d, hv, expert_out, nullptr, nullptr, result, nullptr, num_cus,
+                         stream) != hipSuccess)
     return EP_ERR_HIP;
   return EP_OK;
 }
@@ -198,8 +198,8 @@ ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(grad) || !aligned16(grad_tokens)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  if (launch_reduce_rows(d, hv, grad, g_recv_topk_weights, grad_tokens, grad_topk_weights,
-                         num_cus, stream) != hipSuccess)
+  if (launch_reduce_rows(d, hv, grad, nullptr, g_recv_topk_weights, grad_tokens,
+                         grad_topk_weights, num_cus, stream) != hipSuccess)
     return EP_ERR_HIP;
   return EP_OK;
 }
@@ -218,6 +218,54 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
   if (st != EP_OK) return st;
   if (launch_scatter_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, num_cus, stream) !=
       hipSuccess)
+    return EP_ERR_HIP;
+  return EP_OK;
+}
+
+ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_mem,
+                                size_t handle_bytes, const uint16_t* expert_out,
+                                const float* recv_topk_weights, uint16_t* result,
+                                hipStream_t stream) {
+  Dims d;
+  HandleView hv;
+  int num_cus = 0;
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  if (st != EP_OK) return st;
+  if (d.T > 0 && (!result || (d.cap > 0 && (!expert_out || !recv_topk_weights))))
+    return EP_ERR_NULL;
+  if (!aligned16(expert_out) || !aligned16(result)) return EP_ERR_ALIGN;
+  st = current_device(&num_cus);
+  if (st != EP_OK) return st;
+  // a non-null weight pointer selects the weighted sum; with no received
+  // rows there is nothing to weight and the unweighted kernel writes zeros
+  const float* rw = (d.cap > 0) ? recv_topk_weights : nullptr;
+  if (launch_reduce_rows(d, hv, expert_out, rw, nullptr, result, nullptr, num_cus, stream) !=
+      hipSuccess)
+    return EP_ERR_HIP;
+  return EP_OK;
+}
+
+ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handle_mem,
+                                    size_t handle_bytes, const uint16_t* grad,
+                                    const uint16_t* expert_out, const float* recv_topk_weights,
+                                    uint16_t* grad_expert_out, float* grad_recv_topk_weights,
+                                    hipStream_t stream) {
+  Dims d;
+  HandleView hv;
+  int num_cus = 0;
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  if (st != EP_OK) return st;
+  if (d.cap > 0) {
+    if (!grad_expert_out || !recv_topk_weights) return EP_ERR_NULL;
+    if (d.T > 0 && !grad) return EP_ERR_NULL;
+    if (grad_recv_topk_weights && !expert_out) return EP_ERR_NULL;
+  }
+  if (!aligned16(grad) || !aligned16(expert_out) || !aligned16(grad_expert_out))
+    return EP_ERR_ALIGN;
+  st = current_device(&num_cus);
+  if (st != EP_OK) return st;
+  if (launch_weighted_bwd(d, hv, grad, expert_out, recv_topk_weights, grad_expert_out,
+                          grad_recv_topk_weights, num_cus, stream) != hipSuccess)
     return EP_ERR_HIP;
   return EP_OK;
 }

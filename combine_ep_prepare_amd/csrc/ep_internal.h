@@ -110,8 +110,12 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
 hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
                                const float* w, uint16_t* dst, float* dst_w, int num_cus,
                                hipStream_t stream);
+// rw != nullptr selects the weighted sum (weights of the received rows).
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                              const float* g_w, uint16_t* dst, float* dst_w,
+                              const float* rw, const float* g_w, uint16_t* dst, float* dst_w,
                               int num_cus, hipStream_t stream);
+hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const uint16_t* g,
+                               const uint16_t* y, const float* rw, uint16_t* grad_rows,
+                               float* grad_w, int num_cus, hipStream_t stream);
 
 }  // namespace epmi

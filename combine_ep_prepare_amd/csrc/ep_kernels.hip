@@ -599,6 +599,21 @@ __device__ __forceinline__ void accumulate8_sel(float (&acc)[8], row16_t v, bool
   });
 }
 
+// Weighted form: the first kept term is the product w * x, later kept terms
+// are fused multiply-adds fma(w, x, acc) (one rounding each).
+__device__ __forceinline__ void accumulate8_wsel(float (&acc)[8], row16_t v, bool use,
+                                                 bool have, float w) {
+  static_for<4>([&](auto q) {
+    constexpr int i = q;
+    const float lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
+    const float flo = __builtin_fmaf(w, lo, acc[2 * i]);
+    const float fhi = __builtin_fmaf(w, hi, acc[2 * i + 1]);
+    const float plo = w * lo, phi = w * hi;
+    acc[2 * i] = use ? (have ? flo : plo) : acc[2 * i];
+    acc[2 * i + 1] = use ? (have ? fhi : phi) : acc[2 * i + 1];
+  });
+}
+
 __device__ __forceinline__ row16_t round8(const float (&acc)[8]) {
   row16_t o;
   static_for<4>([&](auto q) {
@@ -613,12 +628,13 @@ __device__ __forceinline__ row16_t round8(const float (&acc)[8]) {
 // Items: (token, column block). The valid rows' slices are all loaded first
 // (up to G of them in flight per lane), then summed in fp32 in ascending k
 // from the first valid one, then rounded once.
-template <int KT, int CH>
+template <int KT, int CH, bool WEIGHTED>
 __global__ void __launch_bounds__(256)
 reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                    const int32_t* __restrict__ slot, uint32_t* status,
-                   const uint16_t* __restrict__ src, const float* __restrict__ g_w,
-                   uint16_t* __restrict__ dst, float* __restrict__ dst_w) {
+                   const uint16_t* __restrict__ src, const float* __restrict__ rw,
+                   const float* __restrict__ g_w, uint16_t* __restrict__ dst,
+                   float* __restrict__ dst_w) {
   constexpr int G = KT > 0 ? KT : 8;
   const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
@@ -655,12 +671,18 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       int32_t sl[KT];
       static_for<KT>([&](auto k) { sl[k] = first ? sl_first[k] : slot[t * KT + k]; });
       first = false;
+      int32_t mine = -1;
+      static_for<KT>([&](auto k) {
+        if (lane == k) mine = sl[k];
+      });
       if (cb == 0 && dst_w != nullptr) {
-        int32_t mine = -1;
-        static_for<KT>([&](auto k) {
-          if (lane == k) mine = sl[k];
-        });
         if (lane < KT) dst_w[t * KT + lane] = (mine >= 0 && g_w != nullptr) ? g_w[mine] : 0.0f;
+      }
+      // weighted form: lane k fetches the weight of route k, then every lane
+      // reads it back as a scalar
+      float wl = 0.0f;
+      if constexpr (WEIGHTED) {
+        if (lane < KT && mine >= 0) wl = rw[mine];
       }
       // Loads only for valid routes (uniform branches); the sums below read
       // every buffer and keep or drop each term with a select, so no buffer
@@ -677,7 +699,12 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       });
       static_for<KT>([&](auto k) {
         const bool use = sl[k] >= 0;
-        static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[k][j], use, have); });
+        if constexpr (WEIGHTED) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+          static_for<CH>([&](auto j) { accumulate8_wsel(acc[j], buf[k][j], use, have, wk); });
+        } else {
+          static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[k][j], use, have); });
+        }
         have |= use;
       });
     } else {
@@ -685,6 +712,10 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       const uint64_t vm = wave_ballot(sl >= 0);
       if (cb == 0 && dst_w != nullptr && lane < K)
         dst_w[t * K + lane] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
+      float wl = 0.0f;
+      if constexpr (WEIGHTED) {
+        if (sl >= 0) wl = rw[sl];
+      }
       for (int k0 = 0; k0 < K; k0 += G) {
         row16_t buf[G][CH];
         static_for<G>([&](auto g) {
@@ -701,7 +732,13 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
         static_for<G>([&](auto g) {
           const int k = k0 + g;
           const bool use = k < K && ((vm >> k) & 1ull);
-          static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[g][j], use, have); });
+          if constexpr (WEIGHTED) {
+            const float wk = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(wl), k < K ? k : 0));
+            static_for<CH>([&](auto j) { accumulate8_wsel(acc[j], buf[g][j], use, have, wk); });
+          } else {
+            static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[g][j], use, have); });
+          }
           have |= use;
         });
       }
@@ -711,6 +748,113 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       const int64_t v = v0 + j * kWave;
       if (v < V) store_row16<kReduceNtStore>(drow + v, have ? round8(acc[j]) : row16_t{0u, 0u, 0u, 0u});
     });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward of the weighted combine
+// ---------------------------------------------------------------------------
+
+// One block of kBwdThreads per item: tokens first, then live pad rows. For
+// token t with valid routes k (received rows r_k, weights w_k):
+//   grad_rows[r_k] = bf16(fp32(w_k * g_t))
+//   grad_w[r_k]    = sum_h g_t[h] * y[r_k][h]
+// Each lane accumulates its share of every dot product with fused
+// multiply-adds in a fixed element order; the block then reduces the lanes
+// with a fixed butterfly and the wavefronts in index order, so the weight
+// gradient is the same bits on every run. Pad rows get zeros.
+constexpr int kBwdThreads = 256;
+
+template <int KT>
+__global__ void __launch_bounds__(kBwdThreads)
+weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
+                    const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
+                    uint32_t* status, const uint16_t* __restrict__ g,
+                    const uint16_t* __restrict__ y, const float* __restrict__ rw,
+                    uint16_t* __restrict__ grad_rows, float* __restrict__ grad_w) {
+  // routes are handled G at a time (all of them at once for a compile-time K)
+  constexpr int G = KT > 0 ? KT : 8;
+  __shared__ float s_part[kBwdThreads / kWave][G];
+  const HandleHeader hh = *h;
+  if (!handle_matches(hh, d)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+    return;
+  }
+  const int K = KT > 0 ? KT : d.K;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const int64_t V = d.H / 8;
+  const int64_t n_items = d.T + (int64_t)hh.pads_live;
+  const row16_t* __restrict__ g4 = reinterpret_cast<const row16_t*>(g);
+  const row16_t* __restrict__ y4 = reinterpret_cast<const row16_t*>(y);
+  row16_t* __restrict__ o4 = reinterpret_cast<row16_t*>(grad_rows);
+  const bool want_w = grad_w != nullptr;
+
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    if (it < d.T) {
+      const int64_t t = it;
+      for (int k0 = 0; k0 < K; k0 += G) {
+        int32_t sl[G];
+        float wk[G];
+        bool any = false;
+        static_for<G>([&](auto k) {
+          sl[k] = k0 + k < K ? slot[t * K + k0 + k] : -1;
+          any |= sl[k] >= 0;
+        });
+        if (!any) continue;                        // uniform over the block
+        static_for<G>([&](auto k) { wk[k] = sl[k] >= 0 ? rw[sl[k]] : 0.0f; });
+        float pd[G];
+        static_for<G>([&](auto k) { pd[k] = 0.0f; });
+        for (int64_t v = tid; v < V; v += kBwdThreads) {
+          const row16_t gv = load_row16<kReduceNtLoad>(g4 + t * V + v);
+          row16_t yv[G];
+          if (want_w) {
+            static_for<G>([&](auto k) {
+              if (sl[k] >= 0) yv[k] = load_row16<kReduceNtLoad>(y4 + (int64_t)sl[k] * V + v);
+            });
+          }
+          static_for<G>([&](auto k) {
+            if (sl[k] >= 0) {
+              row16_t o;
+              static_for<4>([&](auto q) {
+                constexpr int i = q;
+                const float glo = bf16_lo(gv[i]), ghi = bf16_hi(gv[i]);
+                o[i] = rne_bf16(wk[k] * glo) | (rne_bf16(wk[k] * ghi) << 16);
+                if (want_w) {
+                  pd[k] = __builtin_fmaf(glo, bf16_lo(yv[k][i]), pd[k]);
+                  pd[k] = __builtin_fmaf(ghi, bf16_hi(yv[k][i]), pd[k]);
+                }
+              });
+              store_row16<kScatterNtStore>(o4 + (int64_t)sl[k] * V + v, o);
+            }
+          });
+        }
+        if (want_w) {
+          static_for<G>([&](auto k) {
+            float x = pd[k];
+            for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+            if (lane == 0) s_part[wv][k] = x;
+          });
+          __syncthreads();
+          if (tid < G) {
+            float tot = 0.0f;
+            int32_t r = -1;
+            static_for<G>([&](auto k) {
+              if (tid == k) r = sl[k];
+            });
+            for (int q = 0; q < kBwdThreads / kWave; ++q) tot += s_part[q][tid];
+            if (r >= 0) grad_w[r] = tot;
+          }
+          __syncthreads();
+        }
+      }
+    } else {
+      const int32_t r = pad_rows[it - d.T];
+      for (int64_t v = tid; v < V; v += kBwdThreads)
+        store_row16<kScatterNtStore>(o4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
+      if (want_w && tid == 0) grad_w[r] = 0.0f;
+    }
   }
 }
 
@@ -755,11 +899,23 @@ hipError_t scatter_k(const Dims& d, const HandleView& hv, const uint16_t* src, c
   return hipGetLastError();
 }
 
+template <int KT, bool WEIGHTED>
+hipError_t reduce_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* rw,
+                    const float* g_w, uint16_t* dst, float* dst_w, int grid,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, WEIGHTED>), dim3(grid), dim3(kBlock), 0,
+                     stream, d, hv.header, hv.slot, &hv.header->status, src, rw, g_w, dst,
+                     dst_w);
+  return hipGetLastError();
+}
+
 template <int KT>
-hipError_t reduce_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* g_w,
-                    uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH>), dim3(grid), dim3(kBlock), 0,
-                     stream, d, hv.header, hv.slot, &hv.header->status, src, g_w, dst, dst_w);
+hipError_t weighted_bwd_k(const Dims& d, const HandleView& hv, const uint16_t* g,
+                          const uint16_t* y, const float* rw, uint16_t* grad_rows,
+                          float* grad_w, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((weighted_bwd_kernel<KT>), dim3(grid), dim3(kBwdThreads), 0, stream, d,
+                     hv.header, hv.slot, hv.pad_rows, &hv.header->status, g, y, rw, grad_rows,
+                     grad_w);
   return hipGetLastError();
 }
 
@@ -810,21 +966,49 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16
 }
 
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                              const float* g_w, uint16_t* dst, float* dst_w, int num_cus,
-                              hipStream_t stream) {
+                              const float* rw, const float* g_w, uint16_t* dst, float* dst_w,
+                              int num_cus, hipStream_t stream) {
   const int64_t V = d.H / 8;
   const int64_t CB = (int64_t)kWave * kReduceCH;
   const int64_t ncb = (V + CB - 1) / CB;
   const int64_t items = d.T * ncb;
   if (items == 0) return hipSuccess;
   const int grid = grid_for(items, num_cus);
+  if (rw != nullptr) {
+    switch (d.K) {
+      case 1: return reduce_k<1, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+      case 2: return reduce_k<2, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+      case 4: return reduce_k<4, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+      case 6: return reduce_k<6, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+      case 8: return reduce_k<8, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+      default: return reduce_k<0, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
+    }
+  }
   switch (d.K) {
-    case 1: return reduce_k<1>(d, hv, src, g_w, dst, dst_w, grid, stream);
-    case 2: return reduce_k<2>(d, hv, src, g_w, dst, dst_w, grid, stream);
-    case 4: return reduce_k<4>(d, hv, src, g_w, dst, dst_w, grid, stream);
-    case 6: return reduce_k<6>(d, hv, src, g_w, dst, dst_w, grid, stream);
-    case 8: return reduce_k<8>(d, hv, src, g_w, dst, dst_w, grid, stream);
-    default: return reduce_k<0>(d, hv, src, g_w, dst, dst_w, grid, stream);
+    case 1: return reduce_k<1, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+    case 2: return reduce_k<2, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+    case 4: return reduce_k<4, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+    case 6: return reduce_k<6, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+    case 8: return reduce_k<8, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+    default: return reduce_k<0, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
+  }
+}
+
+hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const uint16_t* g,
+                               const uint16_t* y, const float* rw, uint16_t* grad_rows,
+                               float* grad_w, int num_cus, hipStream_t stream) {
+  const int64_t max_items = d.T + d.cap;
+  if (max_items == 0) return hipSuccess;
+  int64_t grid = max_items;
+  const int64_t limit = (int64_t)num_cus * 32;
+  if (grid > limit) grid = limit;
+  switch (d.K) {
+    case 1: return weighted_bwd_k<1>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
+    case 2: return weighted_bwd_k<2>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
+    case 4: return weighted_bwd_k<4>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
+    case 6: return weighted_bwd_k<6>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
+    case 8: return weighted_bwd_k<8>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
+    default: return weighted_bwd_k<0>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
   }
 }
 

@@ -201,6 +201,48 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
                            size_t handle_bytes, const uint16_t* grad,
                            uint16_t* grad_expert_out, hipStream_t stream);
 
+/*
+ * Weighted combine: the weight multiply folded into combine, which the review
+ * of "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with
+ * symm-mem zero-copy" (thread on the weight multiply) asks for so that the
+ * caller's separate pre-multiply pass disappears. For each token, over its
+ * valid routes in ascending k with received row r: the first term is the
+ * fp32 product w[r] * y[r], each later term is a fused multiply-add
+ * fma(w[r], y[r], acc); the fp32 sum is rounded once to bf16 (nearest-even,
+ * NaN -> 0x7FC0); a token with no valid route gets +0.
+ *   expert_out         bf16 [recv_capacity,H] (y; only live rows are read)
+ *   recv_topk_weights  fp32 [recv_capacity]   (w, e.g. dispatch's output)
+ *   result             bf16 [T,H]
+ */
+ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_mem,
+                                size_t handle_bytes, const uint16_t* expert_out,
+                                const float* recv_topk_weights, uint16_t* result,
+                                hipStream_t stream);
+
+/*
+ * Backward of the weighted combine. For every live received row r holding
+ * route s of token t = s/K:
+ *   grad_expert_out[r,:]    = bf16(fp32(w[r] * grad[t,:]))   (pad rows: +0)
+ *   grad_recv_topk_weights[r] = sum over h of grad[t,h] * expert_out[r,h]
+ *                               (pad rows: +0)
+ * The weight gradient is an fp32 dot product over H accumulated in a fixed
+ * order (bit-identical from run to run, but not the sequential order: it is
+ * within the summation error bound of the exact dot product). With
+ * grad_recv_topk_weights NULL only the row gradient is computed and
+ * expert_out may be NULL. Rows at or past min(total, recv_capacity) are not
+ * written.
+ *   grad                    bf16 [T,H]
+ *   expert_out              bf16 [recv_capacity,H] or NULL
+ *   recv_topk_weights       fp32 [recv_capacity]
+ *   grad_expert_out         bf16 [recv_capacity,H]
+ *   grad_recv_topk_weights  fp32 [recv_capacity] or NULL
+ */
+ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handle_mem,
+                                    size_t handle_bytes, const uint16_t* grad,
+                                    const uint16_t* expert_out, const float* recv_topk_weights,
+                                    uint16_t* grad_expert_out, float* grad_recv_topk_weights,
+                                    hipStream_t stream);
+
 /* Copy the handle's status word (EP_STATUS_* bits) to *host_out. Waits for
  * `stream`; not for the hot path. host_out is a host pointer. */
 ep_status_t ep_read_status(const void* handle_mem, uint32_t* host_out, hipStream_t stream);
