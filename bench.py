@@ -10,7 +10,9 @@ The headline is dispatch+combine throughput in algorithmic HBM GB/s (bytes
 the method must move, see ``algorithmic_bytes``) over their kernel time,
 measured with HIP events recorded on the stream the kernels run on. The line
 also carries the roofline of the dominant kernel and the CPU oracle timed on a
-bounded sample of the same workload on this host.
+bounded sample of the same workload on this host. The fused weighted combine
+and its backward are timed after the step, the same way, and reported beside
+it ("ops_outside_step").
 
     python bench.py [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
 """
@@ -54,6 +56,10 @@ def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np):
       combine_bwd   T_act*B + (R+P)*B + 4(R+P)        rows in/out, row map
       dispatch_bwd  R*B + 4R + T*B + 8TK              rows in/out, weights, slot map
       prepare       8TK + 4TK + 4(R+P) + 8E           ids, slots, row map, counts
+      combine_weighted      R*B + 4R + T*B + 4TK      rows and weights in, rows out, slot map
+      combine_weighted_bwd  T_act*B + R*B + 4R + (R+P)*B + 4(R+P) + 4TK + 4P
+                            grads in, expert rows and weights in, row and weight
+                            grads out, slot map, pad-row list
     """
     import numpy as np
     B = 2 * H
@@ -67,6 +73,9 @@ def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np):
         "combine_bwd": T_act * B + (R + P) * B + 4 * (R + P),
         "dispatch_bwd": R * B + 4 * R + T * B + 8 * T * K,
         "prepare": 8 * T * K + 4 * T * K + 4 * (R + P) + 8 * E,
+        "combine_weighted": R * B + 4 * R + T * B + 4 * T * K,
+        "combine_weighted_bwd": (T_act * B + R * B + 4 * R + (R + P) * B + 4 * (R + P)
+                                 + 4 * T * K + 4 * P),
         "_R": R, "_P": P, "_T_act": T_act, "_total": total,
     }
 
@@ -103,7 +112,33 @@ def _read_csv_rows(directory: str, suffix: str):
 
 
 KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
-                "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel"}
+                "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel",
+                "combine_weighted": "reduce_rows_kernel",
+                "combine_weighted_bwd": "weighted_bwd_kernel"}
+
+
+def op_sequence(names):
+    """Attribute each payload-kernel dispatch (demangled names, in dispatch
+    order) to its op. Within a step the unweighted scatter runs for dispatch,
+    then combine_bwd; the unweighted reduce for combine, then dispatch_bwd.
+    The weighted reduce (template flag true) and the weighted backward kernel
+    each serve one op. Other kernels map to None."""
+    out = []
+    n_scatter = n_reduce = 0
+    for name in names:
+        if "scatter_rows_kernel" in name:
+            out.append(("dispatch", "combine_bwd")[n_scatter % 2])
+            n_scatter += 1
+        elif "reduce_rows_kernel" in name and "true" in name:
+            out.append("combine_weighted")
+        elif "reduce_rows_kernel" in name:
+            out.append(("combine", "dispatch_bwd")[n_reduce % 2])
+            n_reduce += 1
+        elif "weighted_bwd_kernel" in name:
+            out.append("combine_weighted_bwd")
+        else:
+            out.append(None)
+    return out
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
@@ -135,16 +170,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         # before it (to build the expert outputs) is left out
         last_copy = max(int(r.get("Dispatch_Id", 0)) for r in calib)
         seq = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows
-               if int(r.get("Dispatch_Id", 0)) > last_copy
-               and ("scatter_rows_kernel" in r["Kernel_Name"]
-                    or "reduce_rows_kernel" in r["Kernel_Name"])]
+               if int(r.get("Dispatch_Id", 0)) > last_copy]
         per_op = {op: [] for op in KERNEL_OF_OP}
-        # steps alternate scatter, reduce, scatter, reduce
-        order = ["dispatch", "combine", "combine_bwd", "dispatch_bwd"]
-        for i, (name, kib) in enumerate(seq):
-            op = order[i % 4]
-            assert KERNEL_OF_OP[op] in name, (op, name)
-            per_op[op].append(kib / factor * 1024.0)
+        for (name, kib), op in zip(seq, op_sequence([nm for nm, _ in seq])):
+            if op is not None:
+                per_op[op].append(kib / factor * 1024.0)
         res[counter] = {"factor": factor,
                         "per_op_bytes": {op: float(np.median(v)) for op, v in per_op.items() if v}}
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
@@ -236,6 +266,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-ops", action="store_true",
+                    help="skip timing the weighted combine and its backward")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
@@ -355,6 +387,38 @@ def main():
     avg = {op: float(np.mean(v)) for op, v in per_op_ms.items()}
     med = {op: float(np.median(v)) for op, v in per_op_ms.items()}
 
+    # The fused weighted combine and its backward: not part of the step (the
+    # step's combine is the unweighted one), timed the same way after it.
+    extra_ops = [] if args.no_extra_ops else ["combine_weighted", "combine_weighted_bwd"]
+    if extra_ops:
+        result_w = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        g_rows_w = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+        g_recv_w2 = torch.empty(cap, dtype=torch.float32, device=dev)
+
+        def extra(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            ep.combine_weighted(L, handle, recv, recv_w, result_w)
+            if ev is not None:
+                ev[1].record(stream)
+            ep.combine_weighted_bwd(L, handle, g_result, recv, recv_w, g_rows_w, g_recv_w2)
+            if ev is not None:
+                ev[2].record(stream)
+
+        for _ in range(args.warmup):
+            extra()
+        xev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            extra(xev[i])
+        torch.cuda.synchronize()
+        assert ep.read_status(handle) == 0, "unexpected status bits"
+        for j, op in enumerate(extra_ops):
+            v = [ev[j].elapsed_time(ev[j + 1]) for ev in xev]
+            avg[op] = float(np.mean(v))
+            med[op] = float(np.median(v))
+
     def gbs(op):
         return nbytes[op] / (avg[op] * 1e-3) / 1e9
 
@@ -414,6 +478,11 @@ def main():
                      "algorithmic_bytes": nbytes[op],
                      "GBps": round(gbs(op), 1) if op != "prepare" else None}
                 for op in ops},
+        "ops_outside_step": {op: {"avg_us": round(avg[op] * 1e3, 2),
+                                  "median_us": round(med[op] * 1e3, 2),
+                                  "algorithmic_bytes": nbytes[op],
+                                  "GBps": round(gbs(op), 1)}
+                             for op in extra_ops},
         "routing": {"R": nbytes["_R"], "P": nbytes["_P"], "total": nbytes["_total"],
                     "T_act": nbytes["_T_act"]},
         "roofline": roofline,

@@ -6,7 +6,11 @@ exposes dispatch and combine as differentiable ops with a per-call routing
 state (one per in-flight microbatch). This module does the same for the
 one-GPU library: `EpRouting` holds the layout and the handle of one prepared
 routing, `dispatch` and `combine` are `torch.autograd.Function`s whose
-backward passes call `ep_dispatch_bwd` and `ep_combine_bwd`.
+backward passes call `ep_dispatch_bwd` and `ep_combine_bwd`. Given the
+received weights, `combine` applies them itself (the fused weighted combine,
+made optional in the same page's review thread on the weight multiply); its
+backward calls `ep_combine_weighted_bwd` for both the rows' and the weights'
+gradients.
 
 Outputs are allocated with PyTorch; every step of the computation runs in the
 library's kernels. A gradient that does not flow into the received weights
@@ -21,8 +25,9 @@ from typing import Optional
 import torch
 
 from . import (Layout, combine as _combine, combine_bwd as _combine_bwd,
-               dispatch as _dispatch, dispatch_bwd as _dispatch_bwd, new_handle, prepare,
-               recv_capacity_worst)
+               combine_weighted as _combine_weighted,
+               combine_weighted_bwd as _combine_weighted_bwd, dispatch as _dispatch,
+               dispatch_bwd as _dispatch_bwd, new_handle, prepare, recv_capacity_worst)
 
 
 class EpRouting:
@@ -93,12 +98,45 @@ class _Combine(torch.autograd.Function):
         return grad, None
 
 
+class _CombineWeighted(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, expert_out, recv_topk_weights, routing: EpRouting):
+        L = routing.layout
+        expert_out = expert_out.contiguous()
+        recv_topk_weights = recv_topk_weights.contiguous()
+        result = torch.empty(L.T, L.H, dtype=expert_out.dtype, device=expert_out.device)
+        _combine_weighted(L, routing.handle, expert_out, recv_topk_weights, result)
+        ctx.routing = routing
+        ctx.save_for_backward(expert_out, recv_topk_weights)
+        return result
+
+    @staticmethod
+    def backward(ctx, g_result):
+        expert_out, recv_topk_weights = ctx.saved_tensors
+        routing = ctx.routing
+        L = routing.layout
+        want_rows, want_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (want_rows or want_w):
+            return None, None, None
+        grad_rows = torch.empty(L.cap, L.H, dtype=g_result.dtype, device=g_result.device)
+        grad_w = (torch.empty(L.cap, dtype=torch.float32, device=g_result.device)
+                  if want_w else None)
+        _combine_weighted_bwd(L, routing.handle, g_result.contiguous(),
+                              expert_out if want_w else None, recv_topk_weights, grad_rows,
+                              grad_w)
+        return grad_rows if want_rows else None, grad_w, None
+
+
 def dispatch(tokens: torch.Tensor, topk_weights: torch.Tensor, routing: EpRouting):
     """(recv_tokens [cap,H], recv_topk_weights [cap]); rows past the live total
     are unspecified."""
     return _Dispatch.apply(tokens, topk_weights, routing)
 
 
-def combine(expert_out: torch.Tensor, routing: EpRouting) -> torch.Tensor:
-    """Unweighted sum of each token's expert rows, [T,H]."""
-    return _Combine.apply(expert_out, routing)
+def combine(expert_out: torch.Tensor, routing: EpRouting,
+            recv_topk_weights: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sum of each token's expert rows, [T,H]: unweighted, or, given the
+    received weights, each row scaled by its route's weight inside the sum."""
+    if recv_topk_weights is None:
+        return _Combine.apply(expert_out, routing)
+    return _CombineWeighted.apply(expert_out, recv_topk_weights, routing)

@@ -1,0 +1,45 @@
+"""Host-side logic of the benchmark: algorithmic byte counts on a tiny
+hand-worked routing, and the attribution of profiled kernel dispatches to ops."""
+import numpy as np
+
+import bench
+
+
+def test_algorithmic_bytes_hand_worked():
+    # T=3, K=2, E=2, H=8 (B = 16 bytes per row). Token 0 -> experts 0,1;
+    # token 1 -> expert 1 and a masked route; token 2 masked entirely.
+    idx = np.array([[0, 1], [1, -1], [-1, -1]], np.int64)
+    counts = np.array([1, 2], np.int32)
+    # alignment 4: segments of 4 rows each, so 8 rows in all, 5 of them pads
+    offsets = np.array([0, 4, 8], np.int32)
+    b = bench.algorithmic_bytes(3, 2, 2, 8, idx, counts, offsets)
+    R, P, T_act, B = 3, 5, 2, 16
+    assert (b["_R"], b["_P"], b["_T_act"], b["_total"]) == (R, P, T_act, 8)
+    assert b["dispatch"] == T_act * B + 8 * B + 4 * R + 8 * 8
+    assert b["combine"] == R * B + 3 * B + 4 * 6
+    assert b["combine_bwd"] == T_act * B + 8 * B + 4 * 8
+    assert b["dispatch_bwd"] == R * B + 4 * R + 3 * B + 8 * 6
+    assert b["prepare"] == 8 * 6 + 4 * 6 + 4 * 8 + 8 * 2
+    assert b["combine_weighted"] == R * B + 4 * R + 3 * B + 4 * 6
+    assert b["combine_weighted_bwd"] == (T_act * B + R * B + 4 * R + 8 * B + 4 * 8 + 4 * 6
+                                         + 4 * P)
+
+
+def test_op_sequence_attribution():
+    names = ["epmi::prepare_hist_kernel", "epmi::scatter_rows_kernel<8, 8>",
+             "epmi::reduce_rows_kernel<8, 2, false>", "epmi::scatter_rows_kernel<8, 8>",
+             "epmi::reduce_rows_kernel<8, 2, false>", "at::native::copy",
+             "epmi::scatter_rows_kernel<8, 8>", "epmi::reduce_rows_kernel<8, 2, false>",
+             "epmi::reduce_rows_kernel<8, 2, true>", "epmi::weighted_bwd_kernel<8>"]
+    assert bench.op_sequence(names) == [
+        None, "dispatch", "combine", "combine_bwd", "dispatch_bwd", None, "dispatch",
+        "combine", "combine_weighted", "combine_weighted_bwd"]
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr

@@ -112,3 +112,33 @@ def test_bit_stable_and_interleaved_routings():
         n = torch.from_numpy((r.topk_idx >= 0).sum(axis=1)).cuda()
         want = (x.float() * n[:, None].float()).to(torch.bfloat16)
         assert torch.equal(o.view(torch.int16), want.view(torch.int16))
+
+
+def test_fused_weighted_combine_grads():
+    # combine with the weights applied inside: forward bit-exact, the row grads
+    # and token grads bit-exact, the weight grads within the dot's fp32 bound
+    cfg, r, idx, x, w = _setup(name="dsv3", T=400, H=1024, seed=2)
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H)
+    x = x.clone().requires_grad_(True)
+    w = w.clone().requires_grad_(True)
+    recv, recv_w = epa.dispatch(x, w, routing)
+    recv.retain_grad()
+    recv_w.retain_grad()
+    y = epa.combine(recv, routing, recv_w)          # identity experts, fused weights
+    g = workloads.randn_bf16_torch((cfg.T, cfg.H), 78)
+    y.backward(g)
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, routing.layout.cap)
+    live = p.live
+    h_recv = host_bf16(recv.detach())
+    h_recv_w = recv_w.detach().cpu().numpy()
+    assert np.array_equal(host_bf16(y.detach()), oracle.combine_weighted(p, h_recv, h_recv_w))
+    o_gr, o_gw, o_abs = oracle.combine_weighted_bwd(p, host_bf16(g), h_recv, h_recv_w)
+    assert np.array_equal(host_bf16(recv.grad)[:live], o_gr[:live])
+    got = recv_w.grad.cpu().numpy()[:live].astype(np.float64)
+    n = 8 * -(-cfg.H // 2048) + 9
+    gamma = n * 2.0 ** -24 / (1 - n * 2.0 ** -24)
+    assert (np.abs(got - o_gw[:live]) <= gamma * o_abs[:live] + 1e-45).all()
+    # then through dispatch's backward, bit for bit
+    o_gt, o_gwt = oracle.dispatch_bwd(p, host_bf16(recv.grad), recv_w.grad.cpu().numpy())
+    assert np.array_equal(host_bf16(x.grad), o_gt)
+    assert np.array_equal(w.grad.cpu().numpy().view(np.uint32), o_gwt.view(np.uint32))
