@@ -35,6 +35,17 @@ STATUS_BAD_EXPERT = 1
 STATUS_OVERFLOW = 2
 STATUS_LAYOUT = 4
 
+DTYPE_BF16 = 0
+DTYPE_FP16 = 1
+DTYPE_FP32 = 2
+LAYOUT_NO_PAD_FILL = 1
+
+# payload type code -> torch dtype of the rows
+TORCH_DTYPE = {DTYPE_BF16: torch.bfloat16, DTYPE_FP16: torch.float16,
+               DTYPE_FP32: torch.float32}
+_CODE_OF = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32: DTYPE_FP32,
+            "bf16": DTYPE_BF16, "fp16": DTYPE_FP16, "fp32": DTYPE_FP32}
+
 ENTRY_POINTS = ("ep_recv_capacity_worst", "ep_handle_mem_size", "ep_handle_regions",
                 "ep_prepare", "ep_dispatch",
                 "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_weighted",
@@ -42,13 +53,23 @@ ENTRY_POINTS = ("ep_recv_capacity_worst", "ep_handle_mem_size", "ep_handle_regio
 
 
 class Layout(C.Structure):
-    """ep_layout_t."""
+    """ep_layout_t. ``dtype`` is the payload type (a torch dtype, "bf16",
+    "fp16", "fp32" or a DTYPE_* code); ``fill_pads=False`` sets
+    LAYOUT_NO_PAD_FILL."""
     _fields_ = [("num_tokens", C.c_int64), ("topk", C.c_int32), ("num_experts", C.c_int32),
-                ("alignment", C.c_int32), ("reserved", C.c_int32), ("hidden", C.c_int64),
-                ("recv_capacity", C.c_int64)]
+                ("alignment", C.c_int32), ("dtype", C.c_uint16), ("flags", C.c_uint16),
+                ("hidden", C.c_int64), ("recv_capacity", C.c_int64)]
 
-    def __init__(self, num_tokens, topk, num_experts, alignment, hidden, recv_capacity):
-        super().__init__(num_tokens, topk, num_experts, alignment, 0, hidden, recv_capacity)
+    def __init__(self, num_tokens, topk, num_experts, alignment, hidden, recv_capacity,
+                 dtype=DTYPE_BF16, fill_pads=True):
+        code = dtype if isinstance(dtype, int) else _CODE_OF[dtype]
+        super().__init__(num_tokens, topk, num_experts, alignment, code,
+                         0 if fill_pads else LAYOUT_NO_PAD_FILL, hidden, recv_capacity)
+
+    @property
+    def payload_dtype(self) -> torch.dtype:
+        """torch dtype of the payload rows (bfloat16 for an unknown code)."""
+        return TORCH_DTYPE.get(self.dtype, torch.bfloat16)
 
     @property
     def T(self):
@@ -209,9 +230,9 @@ def dispatch(layout: Layout, handle: torch.Tensor, tokens: torch.Tensor,
              topk_weights: Optional[torch.Tensor], recv_tokens: torch.Tensor,
              recv_topk_weights: Optional[torch.Tensor] = None, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(tokens, "tokens", torch.bfloat16, (layout.T, layout.H))
+    _need(tokens, "tokens", layout.payload_dtype, (layout.T, layout.H))
     _need(topk_weights, "topk_weights", torch.float32, (layout.T, layout.K), allow_none=True)
-    _need(recv_tokens, "recv_tokens", torch.bfloat16, (layout.cap, layout.H))
+    _need(recv_tokens, "recv_tokens", layout.payload_dtype, (layout.cap, layout.H))
     _need(recv_topk_weights, "recv_topk_weights", torch.float32, (layout.cap,),
           allow_none=True)
     _check(lib.ep_dispatch(C.byref(layout), _ptr(handle), handle.numel(), _ptr(tokens),
@@ -222,8 +243,8 @@ def dispatch(layout: Layout, handle: torch.Tensor, tokens: torch.Tensor,
 def combine(layout: Layout, handle: torch.Tensor, expert_out: torch.Tensor,
             result: torch.Tensor, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(expert_out, "expert_out", torch.bfloat16, (layout.cap, layout.H))
-    _need(result, "result", torch.bfloat16, (layout.T, layout.H))
+    _need(expert_out, "expert_out", layout.payload_dtype, (layout.cap, layout.H))
+    _need(result, "result", layout.payload_dtype, (layout.T, layout.H))
     _check(lib.ep_combine(C.byref(layout), _ptr(handle), handle.numel(), _ptr(expert_out),
                           _ptr(result), _stream(stream)), "ep_combine")
 
@@ -232,10 +253,10 @@ def dispatch_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
                  g_recv_topk_weights: Optional[torch.Tensor], grad_tokens: torch.Tensor,
                  grad_topk_weights: Optional[torch.Tensor] = None, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(grad, "grad", torch.bfloat16, (layout.cap, layout.H))
+    _need(grad, "grad", layout.payload_dtype, (layout.cap, layout.H))
     _need(g_recv_topk_weights, "g_recv_topk_weights", torch.float32, (layout.cap,),
           allow_none=True)
-    _need(grad_tokens, "grad_tokens", torch.bfloat16, (layout.T, layout.H))
+    _need(grad_tokens, "grad_tokens", layout.payload_dtype, (layout.T, layout.H))
     _need(grad_topk_weights, "grad_topk_weights", torch.float32, (layout.T, layout.K),
           allow_none=True)
     _check(lib.ep_dispatch_bwd(C.byref(layout), _ptr(handle), handle.numel(), _ptr(grad),
@@ -246,8 +267,8 @@ def dispatch_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
 def combine_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
                 grad_expert_out: torch.Tensor, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(grad, "grad", torch.bfloat16, (layout.T, layout.H))
-    _need(grad_expert_out, "grad_expert_out", torch.bfloat16, (layout.cap, layout.H))
+    _need(grad, "grad", layout.payload_dtype, (layout.T, layout.H))
+    _need(grad_expert_out, "grad_expert_out", layout.payload_dtype, (layout.cap, layout.H))
     _check(lib.ep_combine_bwd(C.byref(layout), _ptr(handle), handle.numel(), _ptr(grad),
                               _ptr(grad_expert_out), _stream(stream)), "ep_combine_bwd")
 
@@ -255,9 +276,9 @@ def combine_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tensor,
 def combine_weighted(layout: Layout, handle: torch.Tensor, expert_out: torch.Tensor,
                      recv_topk_weights: torch.Tensor, result: torch.Tensor, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(expert_out, "expert_out", torch.bfloat16, (layout.cap, layout.H))
+    _need(expert_out, "expert_out", layout.payload_dtype, (layout.cap, layout.H))
     _need(recv_topk_weights, "recv_topk_weights", torch.float32, (layout.cap,))
-    _need(result, "result", torch.bfloat16, (layout.T, layout.H))
+    _need(result, "result", layout.payload_dtype, (layout.T, layout.H))
     _check(lib.ep_combine_weighted(C.byref(layout), _ptr(handle), handle.numel(),
                                    _ptr(expert_out), _ptr(recv_topk_weights), _ptr(result),
                                    _stream(stream)), "ep_combine_weighted")
@@ -268,10 +289,10 @@ def combine_weighted_bwd(layout: Layout, handle: torch.Tensor, grad: torch.Tenso
                          grad_expert_out: torch.Tensor,
                          grad_recv_topk_weights: Optional[torch.Tensor] = None, stream=None):
     _need(handle, "handle", torch.uint8)
-    _need(grad, "grad", torch.bfloat16, (layout.T, layout.H))
-    _need(expert_out, "expert_out", torch.bfloat16, (layout.cap, layout.H), allow_none=True)
+    _need(grad, "grad", layout.payload_dtype, (layout.T, layout.H))
+    _need(expert_out, "expert_out", layout.payload_dtype, (layout.cap, layout.H), allow_none=True)
     _need(recv_topk_weights, "recv_topk_weights", torch.float32, (layout.cap,))
-    _need(grad_expert_out, "grad_expert_out", torch.bfloat16, (layout.cap, layout.H))
+    _need(grad_expert_out, "grad_expert_out", layout.payload_dtype, (layout.cap, layout.H))
     _need(grad_recv_topk_weights, "grad_recv_topk_weights", torch.float32, (layout.cap,),
           allow_none=True)
     _check(lib.ep_combine_weighted_bwd(C.byref(layout), _ptr(handle), handle.numel(),

@@ -28,7 +28,10 @@ ep_status_t check_layout(const ep_layout_t* L) {
   if (L->num_tokens < 0 || L->num_tokens >= kInt32Limit) return EP_ERR_SHAPE;
   if (L->topk < 1 || L->topk > kMaxTopk) return EP_ERR_SHAPE;
   if (L->num_experts < 1 || L->num_experts > kMaxExperts) return EP_ERR_SHAPE;
-  if (L->alignment < 1 || L->reserved != 0) return EP_ERR_SHAPE;
+  if (L->alignment < 1) return EP_ERR_SHAPE;
+  if (L->dtype != EP_DTYPE_BF16 && L->dtype != EP_DTYPE_FP16 && L->dtype != EP_DTYPE_FP32)
+    return EP_ERR_SHAPE;
+  if ((L->flags & ~(uint32_t)EP_LAYOUT_NO_PAD_FILL) != 0) return EP_ERR_SHAPE;
   if (L->hidden < 8 || L->hidden % 8 != 0 || L->hidden >= kInt32Limit) return EP_ERR_SHAPE;
   const int64_t routes = L->num_tokens * (int64_t)L->topk;
   const int64_t worst = routes + (int64_t)L->num_experts * ((int64_t)L->alignment - 1);
@@ -67,6 +70,10 @@ Dims dims_of(const ep_layout_t* L, int32_t num_units) {
   d.num_units = num_units;
   d.cap = L->recv_capacity;
   d.H = L->hidden;
+  const int64_t esize = L->dtype == EP_DTYPE_FP32 ? 4 : 2;
+  d.V = L->hidden * esize / 16;
+  d.dtype = L->dtype;
+  d.fill_pads = (L->flags & EP_LAYOUT_NO_PAD_FILL) ? 0 : 1;
   return d;
 }
 
@@ -144,8 +151,8 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
 }
 
 ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
-                        size_t handle_bytes, const uint16_t* tokens,
-                        const float* topk_weights, uint16_t* recv_tokens,
+                        size_t handle_bytes, const void* tokens,
+                        const float* topk_weights, void* recv_tokens,
                         float* recv_topk_weights, hipStream_t stream) {
   Dims d;
   HandleView hv;
@@ -168,7 +175,7 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
 }
 
 ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
-                       size_t handle_bytes, const uint16_t* expert_out, uint16_t* result,
+                       size_t handle_bytes, const void* expert_out, void* result,
                        hipStream_t stream) {
   Dims d;
   HandleView hv;
@@ -186,8 +193,8 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
 }
 
 ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
-                            size_t handle_bytes, const uint16_t* grad,
-                            const float* g_recv_topk_weights, uint16_t* grad_tokens,
+                            size_t handle_bytes, const void* grad,
+                            const float* g_recv_topk_weights, void* grad_tokens,
                             float* grad_topk_weights, hipStream_t stream) {
   Dims d;
   HandleView hv;
@@ -205,8 +212,8 @@ ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
 }
 
 ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
-                           size_t handle_bytes, const uint16_t* grad,
-                           uint16_t* grad_expert_out, hipStream_t stream) {
+                           size_t handle_bytes, const void* grad, void* grad_expert_out,
+                           hipStream_t stream) {
   Dims d;
   HandleView hv;
   int num_cus = 0;
@@ -223,8 +230,8 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
 }
 
 ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_mem,
-                                size_t handle_bytes, const uint16_t* expert_out,
-                                const float* recv_topk_weights, uint16_t* result,
+                                size_t handle_bytes, const void* expert_out,
+                                const float* recv_topk_weights, void* result,
                                 hipStream_t stream) {
   Dims d;
   HandleView hv;
@@ -246,9 +253,9 @@ ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_me
 }
 
 ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handle_mem,
-                                    size_t handle_bytes, const uint16_t* grad,
-                                    const uint16_t* expert_out, const float* recv_topk_weights,
-                                    uint16_t* grad_expert_out, float* grad_recv_topk_weights,
+                                    size_t handle_bytes, const void* grad,
+                                    const void* expert_out, const float* recv_topk_weights,
+                                    void* grad_expert_out, float* grad_recv_topk_weights,
                                     hipStream_t stream) {
   Dims d;
   HandleView hv;

@@ -101,21 +101,25 @@ struct Dims {
   int32_t num_units;
   int64_t cap;
   int64_t H;
+  int64_t V;          // 16-byte vectors per payload row: H * element size / 16
+  int32_t dtype;      // EP_DTYPE_* of the payload rows
+  int32_t fill_pads;  // 1: payload ops zero the live pad rows; 0: leave them
 };
 
 // Launchers (ep_kernels.hip). Each returns the hipError_t of its launch.
 hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
                           int32_t* user_counts, int32_t* user_offsets, int num_cus,
                           hipStream_t stream);
-hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                               const float* w, uint16_t* dst, float* dst_w, int num_cus,
+// Payload pointers are raw rows of d.dtype.
+hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,
+                               const float* w, void* dst, float* dst_w, int num_cus,
                                hipStream_t stream);
 // rw != nullptr selects the weighted sum (weights of the received rows).
-hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                              const float* rw, const float* g_w, uint16_t* dst, float* dst_w,
+hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
+                              const float* rw, const float* g_w, void* dst, float* dst_w,
                               int num_cus, hipStream_t stream);
-hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const uint16_t* g,
-                               const uint16_t* y, const float* rw, uint16_t* grad_rows,
-                               float* grad_w, int num_cus, hipStream_t stream);
+hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* g,
+                               const void* y, const float* rw, void* grad_rows, float* grad_w,
+                               int num_cus, hipStream_t stream);
 
 }  // namespace epmi

@@ -393,7 +393,8 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
 // row vectors and tunables
 // ---------------------------------------------------------------------------
 
-// 16 bytes = 8 bf16 per lane; a wavefront moves 1 KiB per instruction.
+// 16 bytes per lane (8 bf16 or fp16, or 4 fp32); a wavefront moves 1 KiB per
+// instruction.
 typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 
 // Work-item width in 1 KiB column blocks, launch shape and cache policy.
@@ -471,6 +472,84 @@ __device__ __forceinline__ int64_t wave_index() {
   return (int64_t)blockIdx.x * (blockDim.x / kWave) + w;
 }
 
+// fp32 -> fp16 bits: the hardware conversion rounds to nearest even and keeps
+// fp16 subnormals; any NaN -> 0x7E00. The fp32 value is first made opaque to
+// the compiler: otherwise it may fold the multiply or fused multiply-add that
+// produced it into one mixed-precision instruction (v_fma_mixlo_f16) that
+// rounds the exact result straight to fp16, skipping the fp32 rounding the
+// result is defined by.
+__device__ __forceinline__ uint32_t rne_f16(float f) {
+  asm("" : "+v"(f));
+  if (__builtin_isnan(f)) return 0x7E00u;
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(bits16)));
+}
+
+// fp32 result bits: the value itself, any NaN -> 0x7FC00000.
+__device__ __forceinline__ uint32_t canon_f32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC00000u : u;
+}
+
+// Payload element types. A 16-byte vector holds N elements; get<I> widens
+// element I exactly to fp32 and pack rounds N fp32 values once to the type.
+template <int DT>
+struct Payload;
+
+template <>
+struct Payload<EP_DTYPE_BF16> {
+  static constexpr int N = 8;
+  template <int I>
+  __device__ static __forceinline__ float get(const row16_t& v) {
+    return (I & 1) ? bf16_hi(v[I >> 1]) : bf16_lo(v[I >> 1]);
+  }
+  __device__ static __forceinline__ row16_t pack(const float (&a)[N]) {
+    row16_t o;
+    static_for<4>([&](auto q) {
+      constexpr int i = q;
+      o[i] = rne_bf16(a[2 * i]) | (rne_bf16(a[2 * i + 1]) << 16);
+    });
+    return o;
+  }
+};
+
+template <>
+struct Payload<EP_DTYPE_FP16> {
+  static constexpr int N = 8;
+  template <int I>
+  __device__ static __forceinline__ float get(const row16_t& v) {
+    return f16_to_f32((I & 1) ? (v[I >> 1] >> 16) : (v[I >> 1] & 0xFFFFu));
+  }
+  __device__ static __forceinline__ row16_t pack(const float (&a)[N]) {
+    row16_t o;
+    static_for<4>([&](auto q) {
+      constexpr int i = q;
+      o[i] = rne_f16(a[2 * i]) | (rne_f16(a[2 * i + 1]) << 16);
+    });
+    return o;
+  }
+};
+
+template <>
+struct Payload<EP_DTYPE_FP32> {
+  static constexpr int N = 4;
+  template <int I>
+  __device__ static __forceinline__ float get(const row16_t& v) {
+    return __uint_as_float(v[I]);
+  }
+  __device__ static __forceinline__ row16_t pack(const float (&a)[N]) {
+    row16_t o;
+    static_for<4>([&](auto q) {
+      constexpr int i = q;
+      o[i] = canon_f32(a[i]);
+    });
+    return o;
+  }
+};
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -478,15 +557,16 @@ __device__ __forceinline__ int64_t wave_index() {
 // ---------------------------------------------------------------------------
 
 // Items: (token, column block) for every token, then (pad row, column block)
-// for every live pad row. A token item reads its CH KiB slice of the row
-// once and stores it to the received row of each valid route. With a
-// compile-time top-k the token's slots are wave-uniform scalars.
+// for every live pad row when pads are filled. A token item reads its CH KiB
+// slice of the row once and stores it to the received row of each valid
+// route. With a compile-time top-k the token's slots are wave-uniform
+// scalars. A bit copy: the payload type only sets the row length d.V.
 template <int KT, int CH>
 __global__ void __launch_bounds__(256)
 scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                     const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
-                    uint32_t* status, const uint16_t* __restrict__ src,
-                    const float* __restrict__ w, uint16_t* __restrict__ dst,
+                    uint32_t* status, const row16_t* __restrict__ src4,
+                    const float* __restrict__ w, row16_t* __restrict__ dst4,
                     float* __restrict__ dst_w) {
   const HandleHeader hh = *h;
   if (!handle_matches(hh, d)) {
@@ -495,14 +575,13 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
   }
   const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
-  const int64_t V = d.H / 8;
+  const int64_t V = d.V;
   constexpr int64_t CB = (int64_t)kWave * CH;
   const int64_t ncb = (V + CB - 1) / CB;
   const int64_t tok_items = d.T * ncb;
-  const int64_t n_items = tok_items + (int64_t)hh.pads_live * ncb;
+  const int64_t pad_items = d.fill_pads ? (int64_t)hh.pads_live * ncb : 0;
+  const int64_t n_items = tok_items + pad_items;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const row16_t* __restrict__ src4 = reinterpret_cast<const row16_t*>(src);
-  row16_t* __restrict__ dst4 = reinterpret_cast<row16_t*>(dst);
   const bool weights = w != nullptr && dst_w != nullptr;
 
   for (int64_t it = wave_index(); it < n_items; it += nwaves) {
@@ -585,66 +664,55 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 
 namespace {
 
-// acc (+)= the 8 bf16 of one 16-byte vector, widened exactly to fp32, with
-// the term kept only if `use`: acc = use ? (have ? acc + x : x) : acc,
+// acc (+)= the N elements of one 16-byte vector, widened exactly to fp32,
+// with the term kept only if `use`: acc = use ? (have ? acc + x : x) : acc,
 // written as selects so that every buffer is read on every path.
-__device__ __forceinline__ void accumulate8_sel(float (&acc)[8], row16_t v, bool use,
-                                                bool have) {
-  static_for<4>([&](auto q) {
+template <int DT>
+__device__ __forceinline__ void accumulate_sel(float (&acc)[Payload<DT>::N], row16_t v,
+                                               bool use, bool have) {
+  static_for<Payload<DT>::N>([&](auto q) {
     constexpr int i = q;
-    const float lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
-    const float slo = acc[2 * i] + lo, shi = acc[2 * i + 1] + hi;
-    acc[2 * i] = use ? (have ? slo : lo) : acc[2 * i];
-    acc[2 * i + 1] = use ? (have ? shi : hi) : acc[2 * i + 1];
+    const float x = Payload<DT>::template get<i>(v);
+    const float s = acc[i] + x;
+    acc[i] = use ? (have ? s : x) : acc[i];
   });
 }
 
 // Weighted form: the first kept term is the product w * x, later kept terms
 // are fused multiply-adds fma(w, x, acc) (one rounding each).
-__device__ __forceinline__ void accumulate8_wsel(float (&acc)[8], row16_t v, bool use,
-                                                 bool have, float w) {
-  static_for<4>([&](auto q) {
+template <int DT>
+__device__ __forceinline__ void accumulate_wsel(float (&acc)[Payload<DT>::N], row16_t v,
+                                                bool use, bool have, float w) {
+  static_for<Payload<DT>::N>([&](auto q) {
     constexpr int i = q;
-    const float lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
-    const float flo = __builtin_fmaf(w, lo, acc[2 * i]);
-    const float fhi = __builtin_fmaf(w, hi, acc[2 * i + 1]);
-    const float plo = w * lo, phi = w * hi;
-    acc[2 * i] = use ? (have ? flo : plo) : acc[2 * i];
-    acc[2 * i + 1] = use ? (have ? fhi : phi) : acc[2 * i + 1];
+    const float x = Payload<DT>::template get<i>(v);
+    const float f = __builtin_fmaf(w, x, acc[i]);
+    const float p = w * x;
+    acc[i] = use ? (have ? f : p) : acc[i];
   });
-}
-
-__device__ __forceinline__ row16_t round8(const float (&acc)[8]) {
-  row16_t o;
-  static_for<4>([&](auto q) {
-    constexpr int i = q;
-    o[i] = rne_bf16(acc[2 * i]) | (rne_bf16(acc[2 * i + 1]) << 16);
-  });
-  return o;
 }
 
 }  // namespace
 
 // Items: (token, column block). The valid rows' slices are all loaded first
 // (up to G of them in flight per lane), then summed in fp32 in ascending k
-// from the first valid one, then rounded once.
-template <int KT, int CH, bool WEIGHTED>
+// from the first valid one, then rounded once to the payload type.
+template <int KT, int CH, bool WEIGHTED, int DT>
 __global__ void __launch_bounds__(256)
 reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                    const int32_t* __restrict__ slot, uint32_t* status,
-                   const uint16_t* __restrict__ src, const float* __restrict__ rw,
-                   const float* __restrict__ g_w, uint16_t* __restrict__ dst,
+                   const row16_t* __restrict__ src4, const float* __restrict__ rw,
+                   const float* __restrict__ g_w, row16_t* __restrict__ dst4,
                    float* __restrict__ dst_w) {
+  using P = Payload<DT>;
   constexpr int G = KT > 0 ? KT : 8;
   const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
-  const int64_t V = d.H / 8;
+  const int64_t V = d.V;
   constexpr int64_t CB = (int64_t)kWave * CH;
   const int64_t ncb = (V + CB - 1) / CB;
   const int64_t n_items = d.T * ncb;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const row16_t* __restrict__ src4 = reinterpret_cast<const row16_t*>(src);
-  row16_t* __restrict__ dst4 = reinterpret_cast<row16_t*>(dst);
   int64_t it = wave_index();
   if (it >= n_items) return;
   // The first item's slots are loaded together with the header (both in
@@ -665,7 +733,7 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
     const int64_t t = it / ncb;
     const int64_t cb = it - t * ncb;
     const int64_t v0 = cb * CB + lane;
-    float acc[CH][8];
+    float acc[CH][P::N];
     bool have = false;
     if constexpr (KT > 0) {
       int32_t sl[KT];
@@ -701,9 +769,9 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
         const bool use = sl[k] >= 0;
         if constexpr (WEIGHTED) {
           const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
-          static_for<CH>([&](auto j) { accumulate8_wsel(acc[j], buf[k][j], use, have, wk); });
+          static_for<CH>([&](auto j) { accumulate_wsel<DT>(acc[j], buf[k][j], use, have, wk); });
         } else {
-          static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[k][j], use, have); });
+          static_for<CH>([&](auto j) { accumulate_sel<DT>(acc[j], buf[k][j], use, have); });
         }
         have |= use;
       });
@@ -735,9 +803,11 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
           if constexpr (WEIGHTED) {
             const float wk = __int_as_float(
                 __builtin_amdgcn_readlane(__float_as_int(wl), k < K ? k : 0));
-            static_for<CH>([&](auto j) { accumulate8_wsel(acc[j], buf[g][j], use, have, wk); });
+            static_for<CH>([&](auto j) {
+              accumulate_wsel<DT>(acc[j], buf[g][j], use, have, wk);
+            });
           } else {
-            static_for<CH>([&](auto j) { accumulate8_sel(acc[j], buf[g][j], use, have); });
+            static_for<CH>([&](auto j) { accumulate_sel<DT>(acc[j], buf[g][j], use, have); });
           }
           have |= use;
         });
@@ -746,7 +816,8 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
     row16_t* drow = dst4 + t * V;
     static_for<CH>([&](auto j) {
       const int64_t v = v0 + j * kWave;
-      if (v < V) store_row16<kReduceNtStore>(drow + v, have ? round8(acc[j]) : row16_t{0u, 0u, 0u, 0u});
+      if (v < V)
+        store_row16<kReduceNtStore>(drow + v, have ? P::pack(acc[j]) : row16_t{0u, 0u, 0u, 0u});
     });
   }
 }
@@ -755,9 +826,10 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // backward of the weighted combine
 // ---------------------------------------------------------------------------
 
-// One block of kBwdThreads per item: tokens first, then live pad rows. For
-// token t with valid routes k (received rows r_k, weights w_k):
-//   grad_rows[r_k] = bf16(fp32(w_k * g_t))
+// One block of kBwdThreads per item: tokens first, then live pad rows (when
+// pads are filled). For token t with valid routes k (received rows r_k,
+// weights w_k):
+//   grad_rows[r_k] = payload(fp32(w_k * g_t))
 //   grad_w[r_k]    = sum_h g_t[h] * y[r_k][h]
 // Each lane accumulates its share of every dot product with fused
 // multiply-adds in a fixed element order; the block then reduces the lanes
@@ -765,13 +837,14 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // gradient is the same bits on every run. Pad rows get zeros.
 constexpr int kBwdThreads = 256;
 
-template <int KT>
+template <int KT, int DT>
 __global__ void __launch_bounds__(kBwdThreads)
 weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
                     const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
-                    uint32_t* status, const uint16_t* __restrict__ g,
-                    const uint16_t* __restrict__ y, const float* __restrict__ rw,
-                    uint16_t* __restrict__ grad_rows, float* __restrict__ grad_w) {
+                    uint32_t* status, const row16_t* __restrict__ g4,
+                    const row16_t* __restrict__ y4, const float* __restrict__ rw,
+                    row16_t* __restrict__ o4, float* __restrict__ grad_w) {
+  using P = Payload<DT>;
   // routes are handled G at a time (all of them at once for a compile-time K)
   constexpr int G = KT > 0 ? KT : 8;
   __shared__ float s_part[kBwdThreads / kWave][G];
@@ -784,11 +857,8 @@ weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wv = tid / kWave;
-  const int64_t V = d.H / 8;
-  const int64_t n_items = d.T + (int64_t)hh.pads_live;
-  const row16_t* __restrict__ g4 = reinterpret_cast<const row16_t*>(g);
-  const row16_t* __restrict__ y4 = reinterpret_cast<const row16_t*>(y);
-  row16_t* __restrict__ o4 = reinterpret_cast<row16_t*>(grad_rows);
+  const int64_t V = d.V;
+  const int64_t n_items = d.T + (d.fill_pads ? (int64_t)hh.pads_live : 0);
   const bool want_w = grad_w != nullptr;
 
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
@@ -816,17 +886,14 @@ weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
           }
           static_for<G>([&](auto k) {
             if (sl[k] >= 0) {
-              row16_t o;
-              static_for<4>([&](auto q) {
+              float prod[P::N];
+              static_for<P::N>([&](auto q) {
                 constexpr int i = q;
-                const float glo = bf16_lo(gv[i]), ghi = bf16_hi(gv[i]);
-                o[i] = rne_bf16(wk[k] * glo) | (rne_bf16(wk[k] * ghi) << 16);
-                if (want_w) {
-                  pd[k] = __builtin_fmaf(glo, bf16_lo(yv[k][i]), pd[k]);
-                  pd[k] = __builtin_fmaf(ghi, bf16_hi(yv[k][i]), pd[k]);
-                }
+                const float gi = P::template get<i>(gv);
+                prod[i] = wk[k] * gi;
+                if (want_w) pd[k] = __builtin_fmaf(gi, P::template get<i>(yv[k]), pd[k]);
               });
-              store_row16<kScatterNtStore>(o4 + (int64_t)sl[k] * V + v, o);
+              store_row16<kScatterNtStore>(o4 + (int64_t)sl[k] * V + v, P::pack(prod));
             }
           });
         }
@@ -890,34 +957,31 @@ int grid_for(int64_t items, int num_cus) {
   return (int)blocks;
 }
 
-template <int KT>
-hipError_t scatter_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* w,
-                     uint16_t* dst, float* dst_w, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scatter_rows_kernel<KT, kScatterCH>), dim3(grid), dim3(kBlock), 0,
-                     stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status, src, w,
-                     dst, dst_w);
-  return hipGetLastError();
+// Calls f(std::integral_constant<int, K>) for the top-k values that have a
+// compile-time kernel, f(integral_constant<int, 0>) for any other.
+template <typename F>
+hipError_t with_topk(int K, F&& f) {
+  switch (K) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return f(std::integral_constant<int, 0>{});
+  }
 }
 
-template <int KT, bool WEIGHTED>
-hipError_t reduce_k(const Dims& d, const HandleView& hv, const uint16_t* src, const float* rw,
-                    const float* g_w, uint16_t* dst, float* dst_w, int grid,
-                    hipStream_t stream) {
-  hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, WEIGHTED>), dim3(grid), dim3(kBlock), 0,
-                     stream, d, hv.header, hv.slot, &hv.header->status, src, rw, g_w, dst,
-                     dst_w);
-  return hipGetLastError();
+template <typename F>
+hipError_t with_dtype(int dt, F&& f) {
+  switch (dt) {
+    case EP_DTYPE_FP16: return f(std::integral_constant<int, EP_DTYPE_FP16>{});
+    case EP_DTYPE_FP32: return f(std::integral_constant<int, EP_DTYPE_FP32>{});
+    default: return f(std::integral_constant<int, EP_DTYPE_BF16>{});
+  }
 }
 
-template <int KT>
-hipError_t weighted_bwd_k(const Dims& d, const HandleView& hv, const uint16_t* g,
-                          const uint16_t* y, const float* rw, uint16_t* grad_rows,
-                          float* grad_w, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((weighted_bwd_kernel<KT>), dim3(grid), dim3(kBwdThreads), 0, stream, d,
-                     hv.header, hv.slot, hv.pad_rows, &hv.header->status, g, y, rw, grad_rows,
-                     grad_w);
-  return hipGetLastError();
-}
+const row16_t* rows_in(const void* p) { return static_cast<const row16_t*>(p); }
+row16_t* rows_out(void* p) { return static_cast<row16_t*>(p); }
 
 }  // namespace
 
@@ -946,70 +1010,67 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                               const float* w, uint16_t* dst, float* dst_w, int num_cus,
+hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,
+                               const float* w, void* dst, float* dst_w, int num_cus,
                                hipStream_t stream) {
-  const int64_t V = d.H / 8;
   const int64_t CB = (int64_t)kWave * kScatterCH;
-  const int64_t ncb = (V + CB - 1) / CB;
-  const int64_t max_items = (d.T + d.cap) * ncb;
+  const int64_t ncb = (d.V + CB - 1) / CB;
+  const int64_t max_items = (d.T + (d.fill_pads ? d.cap : 0)) * ncb;
   if (max_items == 0) return hipSuccess;
   const int grid = grid_for(max_items, num_cus);
-  switch (d.K) {
-    case 1: return scatter_k<1>(d, hv, src, w, dst, dst_w, grid, stream);
-    case 2: return scatter_k<2>(d, hv, src, w, dst, dst_w, grid, stream);
-    case 4: return scatter_k<4>(d, hv, src, w, dst, dst_w, grid, stream);
-    case 6: return scatter_k<6>(d, hv, src, w, dst, dst_w, grid, stream);
-    case 8: return scatter_k<8>(d, hv, src, w, dst, dst_w, grid, stream);
-    default: return scatter_k<0>(d, hv, src, w, dst, dst_w, grid, stream);
-  }
+  return with_topk(d.K, [&](auto kt) {
+    constexpr int KT = decltype(kt)::value;
+    hipLaunchKernelGGL((scatter_rows_kernel<KT, kScatterCH>), dim3(grid), dim3(kBlock), 0,
+                       stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status,
+                       rows_in(src), w, rows_out(dst), dst_w);
+    return hipGetLastError();
+  });
 }
 
-hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const uint16_t* src,
-                              const float* rw, const float* g_w, uint16_t* dst, float* dst_w,
+hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
+                              const float* rw, const float* g_w, void* dst, float* dst_w,
                               int num_cus, hipStream_t stream) {
-  const int64_t V = d.H / 8;
   const int64_t CB = (int64_t)kWave * kReduceCH;
-  const int64_t ncb = (V + CB - 1) / CB;
+  const int64_t ncb = (d.V + CB - 1) / CB;
   const int64_t items = d.T * ncb;
   if (items == 0) return hipSuccess;
   const int grid = grid_for(items, num_cus);
-  if (rw != nullptr) {
-    switch (d.K) {
-      case 1: return reduce_k<1, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-      case 2: return reduce_k<2, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-      case 4: return reduce_k<4, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-      case 6: return reduce_k<6, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-      case 8: return reduce_k<8, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-      default: return reduce_k<0, true>(d, hv, src, rw, g_w, dst, dst_w, grid, stream);
-    }
-  }
-  switch (d.K) {
-    case 1: return reduce_k<1, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-    case 2: return reduce_k<2, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-    case 4: return reduce_k<4, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-    case 6: return reduce_k<6, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-    case 8: return reduce_k<8, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-    default: return reduce_k<0, false>(d, hv, src, nullptr, g_w, dst, dst_w, grid, stream);
-  }
+  return with_dtype(d.dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    return with_topk(d.K, [&](auto kt) {
+      constexpr int KT = decltype(kt)::value;
+      if (rw != nullptr) {
+        hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, true, DT>), dim3(grid),
+                           dim3(kBlock), 0, stream, d, hv.header, hv.slot, &hv.header->status,
+                           rows_in(src), rw, g_w, rows_out(dst), dst_w);
+      } else {
+        hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, false, DT>), dim3(grid),
+                           dim3(kBlock), 0, stream, d, hv.header, hv.slot, &hv.header->status,
+                           rows_in(src), nullptr, g_w, rows_out(dst), dst_w);
+      }
+      return hipGetLastError();
+    });
+  });
 }
 
-hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const uint16_t* g,
-                               const uint16_t* y, const float* rw, uint16_t* grad_rows,
-                               float* grad_w, int num_cus, hipStream_t stream) {
-  const int64_t max_items = d.T + d.cap;
+hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* g,
+                               const void* y, const float* rw, void* grad_rows, float* grad_w,
+                               int num_cus, hipStream_t stream) {
+  const int64_t max_items = d.T + (d.fill_pads ? d.cap : 0);
   if (max_items == 0) return hipSuccess;
   int64_t grid = max_items;
   const int64_t limit = (int64_t)num_cus * 32;
   if (grid > limit) grid = limit;
-  switch (d.K) {
-    case 1: return weighted_bwd_k<1>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-    case 2: return weighted_bwd_k<2>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-    case 4: return weighted_bwd_k<4>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-    case 6: return weighted_bwd_k<6>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-    case 8: return weighted_bwd_k<8>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-    default: return weighted_bwd_k<0>(d, hv, g, y, rw, grad_rows, grad_w, (int)grid, stream);
-  }
+  return with_dtype(d.dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    return with_topk(d.K, [&](auto kt) {
+      constexpr int KT = decltype(kt)::value;
+      hipLaunchKernelGGL((weighted_bwd_kernel<KT, DT>), dim3((int)grid), dim3(kBwdThreads), 0,
+                         stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status,
+                         rows_in(g), rows_in(y), rw, rows_out(grad_rows), grad_w);
+      return hipGetLastError();
+    });
+  });
 }
 
 }  // namespace epmi

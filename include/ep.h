@@ -1,6 +1,7 @@
 /*
  * ep.h -- MoE expert-parallel token routing on one AMD Instinct MI355X
- * (gfx950): prepare, dispatch, combine and their two backward ops.
+ * (gfx950): prepare, dispatch, combine and their two backward ops, plus a
+ * fused weighted combine and its backward.
  *
  * The five per-step calls follow the per-step part of the common C API in
  * "Expert Parallelism: common C API + NCCL EP backend" (section "Per-step
@@ -20,12 +21,22 @@
  *    EP_STATUS_BAD_EXPERT and the route is then treated as masked.
  *  - Expert e owns the received rows [offsets[e], offsets[e+1]). Its valid
  *    routes fill the first counts[e] rows in ascending s; the segment is then
- *    padded with zero rows up to a multiple of the alignment A. An expert
- *    with no route has an empty segment. total = offsets[E].
- *  - Payloads are bf16 passed as uint16_t bit patterns ("[PyTorch] Expert
- *    Parallelism: PyTorch wrapper + autograd ops with symm-mem zero-copy",
- *    section "Public Python API": bf16 only, int64 routing ids); routing
- *    weights are fp32. Rows are contiguous, H elements each, row-major.
+ *    padded up to a multiple of the alignment A. The pad rows of every
+ *    expert-major output are written as zeros, unless the layout sets
+ *    EP_LAYOUT_NO_PAD_FILL: then they are not written at all. An expert with
+ *    no route has an empty segment. total = offsets[E].
+ *  - Payload rows hold the layout's payload type: bf16 (the default, and the
+ *    only type of the PyTorch wrapper in "[PyTorch] Expert Parallelism:
+ *    PyTorch wrapper + autograd ops with symm-mem zero-copy", section
+ *    "Public Python API"), fp16 or fp32 (the types the C++ tests of "Expert
+ *    Parallelism: common C API + NCCL EP backend" cover, per its section
+ *    "Important Files Changed"). They are passed as raw bit patterns through
+ *    void pointers. Routing ids are int64, routing weights fp32. Rows are
+ *    contiguous, H elements each, row-major.
+ *  - Sums are taken in fp32 and rounded once to the payload type: round to
+ *    nearest, ties to even, subnormals kept, overflow to infinity, and any
+ *    NaN becomes the canonical quiet NaN (bf16 0x7FC0, fp16 0x7E00, fp32
+ *    0x7FC00000). For fp32 payloads the only change is that NaN rule.
  *  - All pointers are device pointers unless stated otherwise. Payload
  *    pointers must be 16-byte aligned and H must be a multiple of 8. A
  *    pointer to a buffer with no element (T == 0 for [T,...] buffers,
@@ -73,24 +84,50 @@ enum {
                                 that was never prepared; the op wrote nothing */
 };
 
+/* Payload element types (ep_layout_t.dtype). */
+enum {
+  EP_DTYPE_BF16 = 0,
+  EP_DTYPE_FP16 = 1,
+  EP_DTYPE_FP32 = 2
+};
+
+/* Layout flags (ep_layout_t.flags). EP_LAYOUT_NO_PAD_FILL: the payload ops
+ * leave pad rows unwritten instead of zeroing them (dispatch's rows and
+ * weights, combine_bwd's rows, the weighted backward's rows and weight
+ * gradients), saving their writes when the consumer never reads pad rows
+ * (combine and dispatch_bwd never do). The pages zero the pads of
+ * combine_bwd's output only, and the review of "[PyTorch] Expert
+ * Parallelism: PyTorch wrapper + autograd ops with symm-mem zero-copy"
+ * weighs what the padded expert-major buffer costs (its buffer-sizing
+ * thread); this flag makes the pad writes a choice. It does not change the
+ * routing maps: one prepared handle serves both policies. */
+enum {
+  EP_LAYOUT_NO_PAD_FILL = 1u
+};
+
 /*
  * Per-layer sizes (the role of the layer configuration in the common C API,
- * passed by pointer as plain data).
+ * passed by pointer as plain data). A zero-initialised dtype/flags pair
+ * means bf16 payloads with zero-filled pads.
  *   num_tokens    T >= 0
  *   topk          K in [1, 64]
  *   num_experts   E in [1, 2048], local experts
  *   alignment     A >= 1 rows (the per-expert dispatch output alignment)
- *   reserved      must be 0
- *   hidden        H >= 8, a multiple of 8 (bf16 elements per row)
+ *   dtype         EP_DTYPE_* of every payload row
+ *   flags         EP_LAYOUT_* bits; other bits must be 0
+ *   hidden        H >= 8, a multiple of 8 (elements per row)
  *   recv_capacity rows of every expert-major buffer, 0 <= cap < 2^31
- * T*K + E*(A-1) must be below 2^31 (every offset fits an int32).
+ * T*K + E*(A-1) must be below 2^31 (every offset fits an int32). The handle
+ * depends on num_tokens, topk, num_experts, alignment and recv_capacity
+ * only; dtype, flags and hidden may differ between the ops that use it.
  */
 typedef struct ep_layout {
   int64_t num_tokens;
   int32_t topk;
   int32_t num_experts;
   int32_t alignment;
-  int32_t reserved;
+  uint16_t dtype;
+  uint16_t flags;
   int64_t hidden;
   int64_t recv_capacity;
 } ep_layout_t;
@@ -149,29 +186,30 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
 /*
  * dispatch: recv_tokens[r,:] = tokens[s/K,:] and recv_topk_weights[r] =
  * topk_weights[s] for every live row r holding route s (bit copies); pad
- * rows get +0 in both. Rows at or past min(total, recv_capacity) are not
- * written.
- *   tokens             bf16 [T,H]
+ * rows get +0 in both (not written with EP_LAYOUT_NO_PAD_FILL). Rows at or
+ * past min(total, recv_capacity) are not written.
+ *   tokens             payload [T,H]
  *   topk_weights       fp32 [T,K] or NULL
- *   recv_tokens        bf16 [recv_capacity,H]
+ *   recv_tokens        payload [recv_capacity,H]
  *   recv_topk_weights  fp32 [recv_capacity]; must be NULL iff topk_weights is
  *                      (when T > 0 and recv_capacity > 0)
  */
 ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
-                        size_t handle_bytes, const uint16_t* tokens,
-                        const float* topk_weights, uint16_t* recv_tokens,
+                        size_t handle_bytes, const void* tokens,
+                        const float* topk_weights, void* recv_tokens,
                         float* recv_topk_weights, hipStream_t stream);
 
 /*
- * combine: result[t,:] = bf16(sum over the valid routes of t, k ascending,
- * of expert_out[slot(t,k),:]), accumulated in fp32 starting from the first
- * valid row and rounded once to nearest-even (NaN -> 0x7FC0). A token with
- * no valid route gets +0. Unweighted.
- *   expert_out  bf16 [recv_capacity,H] (only live rows are read)
- *   result      bf16 [T,H]
+ * combine: result[t,:] = the sum over the valid routes of t, k ascending, of
+ * expert_out[slot(t,k),:], accumulated in fp32 starting from the first valid
+ * row and rounded once to the payload type (see the rounding convention
+ * above). A token with no valid route gets +0. Unweighted.
+ *   expert_out  payload [recv_capacity,H] (only the rows of valid routes are
+ *               read)
+ *   result      payload [T,H]
  */
 ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
-                       size_t handle_bytes, const uint16_t* expert_out, uint16_t* result,
+                       size_t handle_bytes, const void* expert_out, void* result,
                        hipStream_t stream);
 
 /*
@@ -180,67 +218,70 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
  * for the row r of a valid route s, else +0. A NULL g_recv_topk_weights
  * (no gradient flowed into the received weights) gives +0 everywhere; a NULL
  * grad_topk_weights skips the weight gradient.
- *   grad                 bf16 [recv_capacity,H]
+ *   grad                 payload [recv_capacity,H]
  *   g_recv_topk_weights  fp32 [recv_capacity] or NULL
- *   grad_tokens          bf16 [T,H]
+ *   grad_tokens          payload [T,H]
  *   grad_topk_weights    fp32 [T,K] or NULL
  */
 ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
-                            size_t handle_bytes, const uint16_t* grad,
-                            const float* g_recv_topk_weights, uint16_t* grad_tokens,
+                            size_t handle_bytes, const void* grad,
+                            const float* g_recv_topk_weights, void* grad_tokens,
                             float* grad_topk_weights, hipStream_t stream);
 
 /*
  * combine_bwd (adjoint of combine): grad_expert_out[r,:] = grad[s/K,:] for
- * every live row r holding route s; pad rows are zeroed. Rows at or past
- * min(total, recv_capacity) are not written.
- *   grad             bf16 [T,H]
- *   grad_expert_out  bf16 [recv_capacity,H]
+ * every live row r holding route s; pad rows are zeroed (not written with
+ * EP_LAYOUT_NO_PAD_FILL). Rows at or past min(total, recv_capacity) are not
+ * written.
+ *   grad             payload [T,H]
+ *   grad_expert_out  payload [recv_capacity,H]
  */
 ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
-                           size_t handle_bytes, const uint16_t* grad,
-                           uint16_t* grad_expert_out, hipStream_t stream);
+                           size_t handle_bytes, const void* grad, void* grad_expert_out,
+                           hipStream_t stream);
 
 /*
  * Weighted combine: the weight multiply folded into combine, which the review
  * of "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with
- * symm-mem zero-copy" (thread on the weight multiply) asks for so that the
- * caller's separate pre-multiply pass disappears. For each token, over its
- * valid routes in ascending k with received row r: the first term is the
- * fp32 product w[r] * y[r], each later term is a fused multiply-add
- * fma(w[r], y[r], acc); the fp32 sum is rounded once to bf16 (nearest-even,
- * NaN -> 0x7FC0); a token with no valid route gets +0.
- *   expert_out         bf16 [recv_capacity,H] (y; only live rows are read)
+ * symm-mem zero-copy" (thread on the weight multiply) settles on as an
+ * option, so that the caller's separate pre-multiply pass disappears. For
+ * each token, over its valid routes in ascending k with received row r: the
+ * first term is the fp32 product w[r] * y[r], each later term is a fused
+ * multiply-add fma(w[r], y[r], acc); the fp32 sum is rounded once to the
+ * payload type; a token with no valid route gets +0.
+ *   expert_out         payload [recv_capacity,H] (y; only the rows of valid
+ *                      routes are read)
  *   recv_topk_weights  fp32 [recv_capacity]   (w, e.g. dispatch's output)
- *   result             bf16 [T,H]
+ *   result             payload [T,H]
  */
 ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_mem,
-                                size_t handle_bytes, const uint16_t* expert_out,
-                                const float* recv_topk_weights, uint16_t* result,
+                                size_t handle_bytes, const void* expert_out,
+                                const float* recv_topk_weights, void* result,
                                 hipStream_t stream);
 
 /*
  * Backward of the weighted combine. For every live received row r holding
  * route s of token t = s/K:
- *   grad_expert_out[r,:]    = bf16(fp32(w[r] * grad[t,:]))   (pad rows: +0)
+ *   grad_expert_out[r,:]      = payload(fp32(w[r] * grad[t,:]))  (one fp32
+ *                               product, then the payload rounding)
  *   grad_recv_topk_weights[r] = sum over h of grad[t,h] * expert_out[r,h]
- *                               (pad rows: +0)
- * The weight gradient is an fp32 dot product over H accumulated in a fixed
- * order (bit-identical from run to run, but not the sequential order: it is
- * within the summation error bound of the exact dot product). With
+ * Pad rows get +0 in both (not written with EP_LAYOUT_NO_PAD_FILL). The
+ * weight gradient is an fp32 dot product over H accumulated in a fixed order
+ * (bit-identical from run to run, but not the sequential order: it is within
+ * the summation error bound of the exact dot product). With
  * grad_recv_topk_weights NULL only the row gradient is computed and
  * expert_out may be NULL. Rows at or past min(total, recv_capacity) are not
  * written.
- *   grad                    bf16 [T,H]
- *   expert_out              bf16 [recv_capacity,H] or NULL
+ *   grad                    payload [T,H]
+ *   expert_out              payload [recv_capacity,H] or NULL
  *   recv_topk_weights       fp32 [recv_capacity]
- *   grad_expert_out         bf16 [recv_capacity,H]
+ *   grad_expert_out         payload [recv_capacity,H]
  *   grad_recv_topk_weights  fp32 [recv_capacity] or NULL
  */
 ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handle_mem,
-                                    size_t handle_bytes, const uint16_t* grad,
-                                    const uint16_t* expert_out, const float* recv_topk_weights,
-                                    uint16_t* grad_expert_out, float* grad_recv_topk_weights,
+                                    size_t handle_bytes, const void* grad,
+                                    const void* expert_out, const float* recv_topk_weights,
+                                    void* grad_expert_out, float* grad_recv_topk_weights,
                                     hipStream_t stream);
 
 /* Copy the handle's status word (EP_STATUS_* bits) to *host_out. Waits for

@@ -47,19 +47,25 @@ def _load():
         i64, i32, u32p, vp = C.c_int64, C.c_int32, C.POINTER(C.c_uint32), C.c_void_p
         lib.ep_oracle_prepare.argtypes = [i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, u32p]
         lib.ep_oracle_prepare.restype = C.c_int
-        lib.ep_oracle_dispatch.argtypes = [i64, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+        lib.ep_oracle_dispatch.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64, i64, vp, vp,
+                                           vp, vp, vp]
         lib.ep_oracle_dispatch.restype = C.c_int
-        lib.ep_oracle_combine_bwd.argtypes = [i64, i32, i64, i64, i64, vp, vp, vp]
+        lib.ep_oracle_combine_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64, i64, vp,
+                                              vp, vp]
         lib.ep_oracle_combine_bwd.restype = C.c_int
-        lib.ep_oracle_combine.argtypes = [i64, i32, i64, vp, vp, vp]
+        lib.ep_oracle_combine.argtypes = [i64, i32, i64, C.c_int, vp, vp, vp]
         lib.ep_oracle_combine.restype = C.c_int
-        lib.ep_oracle_dispatch_bwd.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp]
+        lib.ep_oracle_dispatch_bwd.argtypes = [i64, i32, i64, C.c_int, vp, vp, vp, vp, vp]
         lib.ep_oracle_dispatch_bwd.restype = C.c_int
-        lib.ep_oracle_combine_weighted.argtypes = [i64, i32, i64, vp, vp, vp, vp]
+        lib.ep_oracle_combine_weighted.argtypes = [i64, i32, i64, C.c_int, vp, vp, vp, vp]
         lib.ep_oracle_combine_weighted.restype = C.c_int
-        lib.ep_oracle_combine_weighted_bwd.argtypes = [i64, i32, i64, i64, i64, vp, vp, vp, vp,
-                                                       vp, vp, vp]
+        lib.ep_oracle_combine_weighted_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64,
+                                                       i64, vp, vp, vp, vp, vp, vp, vp]
         lib.ep_oracle_combine_weighted_bwd.restype = C.c_int
+        lib.ep_oracle_f16_to_f32.argtypes = [C.c_uint16]
+        lib.ep_oracle_f16_to_f32.restype = C.c_float
+        lib.ep_oracle_f32_to_f16.argtypes = [C.c_float]
+        lib.ep_oracle_f32_to_f16.restype = C.c_uint16
         lib.ep_oracle_f32_to_bf16.argtypes = [C.c_float]
         lib.ep_oracle_f32_to_bf16.restype = C.c_uint16
         lib.ep_oracle_bf16_to_f32.argtypes = [C.c_uint16]
@@ -113,6 +119,23 @@ def bf16_to_f32(h: int) -> float:
     return float(_load().ep_oracle_bf16_to_f32(C.c_uint16(h)))
 
 
+def f32_to_f16(f: float) -> int:
+    return int(_load().ep_oracle_f32_to_f16(C.c_float(f)))
+
+
+def f16_to_f32(h: int) -> float:
+    return float(_load().ep_oracle_f16_to_f32(C.c_uint16(h)))
+
+
+# Payload types: name -> (code of the C oracle, NumPy storage type of a row
+# element). bf16 and fp16 rows are held as their 16-bit patterns.
+DTYPES = {"bf16": (0, np.uint16), "fp16": (1, np.uint16), "fp32": (2, np.float32)}
+
+
+def _rows(a, dtype):
+    return np.ascontiguousarray(a, dtype=DTYPES[dtype][1])
+
+
 def prepare(topk_idx: np.ndarray, E: int, A: int, cap: int, fill: int = -7) -> Prepared:
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
     T, K = topk_idx.shape
@@ -129,90 +152,102 @@ def prepare(topk_idx: np.ndarray, E: int, A: int, cap: int, fill: int = -7) -> P
 
 
 def dispatch(prep: Prepared, x: np.ndarray, w: np.ndarray | None,
-             recv_init: np.ndarray | None = None, recv_w_init: np.ndarray | None = None):
-    """Returns (recv bf16 [cap,H], recv_w f32 [cap] or None). Rows past the
-    live total keep the values of ``recv_init`` (zeros if not given)."""
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+             recv_init: np.ndarray | None = None, recv_w_init: np.ndarray | None = None,
+             dtype: str = "bf16", fill_pads: bool = True):
+    """Returns (recv [cap,H], recv_w f32 [cap] or None). Rows past the live
+    total (and pad rows when fill_pads is False) keep the values of the
+    ``*_init`` arrays (zeros if not given)."""
+    x = _rows(x, dtype)
     T, H = x.shape
-    recv = (np.zeros((prep.cap, H), np.uint16) if recv_init is None
-            else np.array(recv_init, dtype=np.uint16, copy=True))
+    st = DTYPES[dtype][1]
+    recv = (np.zeros((prep.cap, H), st) if recv_init is None
+            else np.array(recv_init, dtype=st, copy=True))
     recv_w = None
     if w is not None:
         w = np.ascontiguousarray(w, dtype=np.float32)
         recv_w = (np.zeros(prep.cap, np.float32) if recv_w_init is None
                   else np.array(recv_w_init, dtype=np.float32, copy=True))
-    rc = _load().ep_oracle_dispatch(T, prep.K, H, prep.cap, prep.total, _p(prep.row_src),
-                                    _p(x), _p(w), _p(recv), _p(recv_w))
+    rc = _load().ep_oracle_dispatch(T, prep.K, H, DTYPES[dtype][0], int(fill_pads), prep.cap,
+                                    prep.total, _p(prep.row_src), _p(x), _p(w), _p(recv),
+                                    _p(recv_w))
     _check(rc, "dispatch")
     return recv, recv_w
 
 
-def combine_bwd(prep: Prepared, g_result: np.ndarray, init: np.ndarray | None = None):
-    g_result = np.ascontiguousarray(g_result, dtype=np.uint16)
+def combine_bwd(prep: Prepared, g_result: np.ndarray, init: np.ndarray | None = None,
+                dtype: str = "bf16", fill_pads: bool = True):
+    g_result = _rows(g_result, dtype)
     T, H = g_result.shape
-    out = (np.zeros((prep.cap, H), np.uint16) if init is None
-           else np.array(init, dtype=np.uint16, copy=True))
-    rc = _load().ep_oracle_combine_bwd(T, prep.K, H, prep.cap, prep.total,
-                                       _p(prep.row_src), _p(g_result), _p(out))
+    st = DTYPES[dtype][1]
+    out = (np.zeros((prep.cap, H), st) if init is None
+           else np.array(init, dtype=st, copy=True))
+    rc = _load().ep_oracle_combine_bwd(T, prep.K, H, DTYPES[dtype][0], int(fill_pads),
+                                       prep.cap, prep.total, _p(prep.row_src), _p(g_result),
+                                       _p(out))
     _check(rc, "combine_bwd")
     return out
 
 
-def combine(prep: Prepared, rows: np.ndarray, T: int | None = None):
-    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+def combine(prep: Prepared, rows: np.ndarray, T: int | None = None, dtype: str = "bf16"):
+    rows = _rows(rows, dtype)
     H = rows.shape[1]
     T = prep.T if T is None else T
-    out = np.empty((T, H), np.uint16)
-    rc = _load().ep_oracle_combine(T, prep.K, H, _p(prep.slot), _p(rows), _p(out))
+    out = np.empty((T, H), DTYPES[dtype][1])
+    rc = _load().ep_oracle_combine(T, prep.K, H, DTYPES[dtype][0], _p(prep.slot), _p(rows),
+                                   _p(out))
     _check(rc, "combine")
     return out
 
 
 def dispatch_bwd(prep: Prepared, g_recv: np.ndarray, g_recv_w: np.ndarray | None,
-                 want_grad_w: bool = True):
-    g_recv = np.ascontiguousarray(g_recv, dtype=np.uint16)
+                 want_grad_w: bool = True, dtype: str = "bf16"):
+    g_recv = _rows(g_recv, dtype)
     H = g_recv.shape[1]
     T, K = prep.T, prep.K
-    gt = np.empty((T, H), np.uint16)
+    gt = np.empty((T, H), DTYPES[dtype][1])
     gw = np.empty((T, K), np.float32) if want_grad_w else None
     if g_recv_w is not None:
         g_recv_w = np.ascontiguousarray(g_recv_w, dtype=np.float32)
-    rc = _load().ep_oracle_dispatch_bwd(T, K, H, _p(prep.slot), _p(g_recv), _p(g_recv_w),
-                                        _p(gt), _p(gw))
+    rc = _load().ep_oracle_dispatch_bwd(T, K, H, DTYPES[dtype][0], _p(prep.slot), _p(g_recv),
+                                        _p(g_recv_w), _p(gt), _p(gw))
     _check(rc, "dispatch_bwd")
     return gt, gw
 
 
-def combine_weighted(prep: Prepared, rows: np.ndarray, w: np.ndarray, T: int | None = None):
-    """bf16 [T,H]: sum over valid k (ascending) of w[r] * rows[r], first term a
-    product, later terms fused multiply-adds, one rounding to bf16."""
-    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+def combine_weighted(prep: Prepared, rows: np.ndarray, w: np.ndarray, T: int | None = None,
+                     dtype: str = "bf16"):
+    """[T,H]: sum over valid k (ascending) of w[r] * rows[r], first term a
+    product, later terms fused multiply-adds, one rounding to the payload type."""
+    rows = _rows(rows, dtype)
     w = np.ascontiguousarray(w, dtype=np.float32)
     H = rows.shape[1]
     T = prep.T if T is None else T
-    out = np.empty((T, H), np.uint16)
-    rc = _load().ep_oracle_combine_weighted(T, prep.K, H, _p(prep.slot), _p(rows), _p(w),
-                                            _p(out))
+    out = np.empty((T, H), DTYPES[dtype][1])
+    rc = _load().ep_oracle_combine_weighted(T, prep.K, H, DTYPES[dtype][0], _p(prep.slot),
+                                            _p(rows), _p(w), _p(out))
     _check(rc, "combine_weighted")
     return out
 
 
 def combine_weighted_bwd(prep: Prepared, g: np.ndarray, rows: np.ndarray | None,
-                         w: np.ndarray, init: np.ndarray | None = None):
-    """(grad_rows bf16 [cap,H] with rows past the live total left at ``init``,
-    grad_w float64 [cap] or None, sum of |terms| float64 [cap] or None)."""
-    g = np.ascontiguousarray(g, dtype=np.uint16)
+                         w: np.ndarray, init: np.ndarray | None = None, dtype: str = "bf16",
+                         fill_pads: bool = True):
+    """(grad_rows [cap,H] with rows past the live total, and pad rows when
+    fill_pads is False, left at ``init``; grad_w float64 [cap] or None; sum of
+    |terms| float64 [cap] or None)."""
+    g = _rows(g, dtype)
     T, H = g.shape
     w = np.ascontiguousarray(w, dtype=np.float32)
-    grad_rows = (np.zeros((prep.cap, H), np.uint16) if init is None
-                 else np.array(init, dtype=np.uint16, copy=True))
+    st = DTYPES[dtype][1]
+    grad_rows = (np.zeros((prep.cap, H), st) if init is None
+                 else np.array(init, dtype=st, copy=True))
     gw = aw = None
     if rows is not None:
-        rows = np.ascontiguousarray(rows, dtype=np.uint16)
+        rows = _rows(rows, dtype)
         gw = np.zeros(prep.cap, np.float64)
         aw = np.zeros(prep.cap, np.float64)
-    rc = _load().ep_oracle_combine_weighted_bwd(T, prep.K, H, prep.cap, prep.total,
-                                                _p(prep.row_src), _p(g), _p(rows), _p(w),
-                                                _p(grad_rows), _p(gw), _p(aw))
+    rc = _load().ep_oracle_combine_weighted_bwd(T, prep.K, H, DTYPES[dtype][0], int(fill_pads),
+                                                prep.cap, prep.total, _p(prep.row_src), _p(g),
+                                                _p(rows), _p(w), _p(grad_rows), _p(gw), _p(aw))
     _check(rc, "combine_weighted_bwd")
     return grad_rows, gw, aw

@@ -9,7 +9,9 @@
  *
  * Everything here is single-threaded scalar C, one loop per step of the
  * definition. Integer work is exact; the only floating point is an ordered
- * binary32 sum followed by one round-to-nearest-even to bf16.
+ * binary32 sum followed by one round-to-nearest-even to the payload type
+ * (bf16, fp16 or fp32), and, for the weighted combine, products and fused
+ * multiply-adds in binary32.
  *
  * Sources (the expert-parallel pull requests these ops come from):
  *  - "Expert Parallelism: common C API + NCCL EP backend", section "Per-step
@@ -23,6 +25,9 @@
  *    symm-mem zero-copy", section "Public Python API": payloads are bf16 and
  *    topk_idx is int64; section "Testing": identity round trip, VJP,
  *    bit stability.
+ *  - "Expert Parallelism: common C API + NCCL EP backend", section
+ *    "Important Files Changed": its C++ tests cover BF16, FP16 and FP32
+ *    payloads, so the oracle takes all three.
  *  - "Expert-parallel implementations for ep_dispatch_experts", table
  *    "Implementations": a rank masks the routes that go to other ranks'
  *    experts; here a masked route carries the id -1.
@@ -32,7 +37,8 @@
  *    s = t*K + k (a stable counting sort keyed by expert id).
  *  - An expert's segment is its route count rounded up to a multiple of the
  *    alignment A; pad rows sit at the end of the segment and are zero in
- *    every expert-major output. An expert with no routes has an empty segment.
+ *    every expert-major output (or, under the no-pad-fill policy, not
+ *    written). An expert with no routes has an empty segment.
  *  - token_counts are the raw (unpadded) per-expert route counts.
  *  - Exactly -1 marks a masked route. Any other id outside [0,E) raises the
  *    BAD_EXPERT status bit and is then treated as masked.
@@ -41,11 +47,13 @@
  *    dropped (slot -1); rows past the capacity are never written.
  *  - combine sums, in ascending k, the fp32 values of the rows of the token's
  *    valid routes, starting from the first valid row (so a single route is a
- *    bit copy, -0.0 included), then rounds once to bf16. A token with no
- *    valid route gets +0.
- *  - fp32 -> bf16 rounds to nearest, ties to even, keeps subnormals, carries
- *    into infinity on overflow, and returns the canonical quiet NaN 0x7FC0
- *    for any NaN (the sign of a NaN produced by an add is not portable).
+ *    bit copy, -0.0 included), then rounds once to the payload type. A token
+ *    with no valid route gets +0.
+ *  - fp32 -> bf16 and fp32 -> fp16 round to nearest, ties to even, keep
+ *    subnormals, carry into infinity on overflow, and return the canonical
+ *    quiet NaN (0x7FC0, 0x7E00) for any NaN (the sign and payload of a NaN
+ *    produced by an add are not portable). An fp32 result is the sum itself
+ *    with any NaN replaced by 0x7FC00000.
  */
 #include <fenv.h>
 #include <math.h>
@@ -106,6 +114,90 @@ uint16_t ep_oracle_f32_to_bf16(float f) {
 }
 
 float ep_oracle_bf16_to_f32(uint16_t h) { return bf16_to_float(h); }
+
+/* fp16 -> fp32 from the binary16 definition: sign, 5-bit exponent with bias
+ * 15, 10-bit fraction; exponent 0 holds the subnormals m * 2^-24, exponent
+ * 31 infinities and NaNs. Every binary16 value is exact in binary32. */
+float ep_oracle_f16_to_f32(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1F;
+  const int m = h & 0x3FF;
+  float mag;
+  if (e == 0x1F) {
+    mag = m ? NAN : INFINITY;
+  } else if (e == 0) {
+    mag = ldexpf((float)m, -24);
+  } else {
+    mag = ldexpf((float)(1024 + m), e - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+/* fp32 -> fp16, round to nearest, ties to even. The result is n * q where q
+ * is the spacing of binary16 values at the magnitude of f (2^(e-10) for a
+ * normal exponent e, the subnormal spacing 2^-24 below 2^-14) and n the
+ * integer nearest |f| / q, ties to even; n = 2048 moves to the next binade,
+ * past the largest finite value (65504) the result is infinity. */
+uint16_t ep_oracle_f32_to_f16(float f) {
+  if (isnan(f)) return 0x7E00u;
+  const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  const float a = fabsf(f);
+  if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+  if (a == 0.0f) return sign;
+  int ex;
+  frexpf(a, &ex);                /* a = m * 2^ex, m in [0.5, 1) */
+  int e = ex - 1;                /* a in [2^e, 2^(e+1)) */
+  if (e < -14) e = -14;          /* subnormal range: fixed spacing */
+  const float y = ldexpf(a, 10 - e);   /* a / q, exact (power-of-two scale) */
+  const float fl = floorf(y);
+  const float frac = y - fl;           /* exact: y has at most 24 bits */
+  long n = (long)fl;
+  if (frac > 0.5f || (frac == 0.5f && (n & 1))) n += 1;
+  if (n == 2048) {               /* rounded up into the next binade */
+    n = 1024;
+    e += 1;
+  }
+  if (e > 15) return (uint16_t)(sign | 0x7C00u);
+  if (n < 1024) return (uint16_t)(sign | (uint16_t)n);   /* subnormal (e == -14) */
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024));
+}
+
+/* Payload element types of the rows. */
+#define ORACLE_BF16 0
+#define ORACLE_FP16 1
+#define ORACLE_FP32 2
+
+static int dtype_ok(int dt) { return dt == ORACLE_BF16 || dt == ORACLE_FP16 || dt == ORACLE_FP32; }
+
+static size_t elem_bytes(int dt) { return dt == ORACLE_FP32 ? 4u : 2u; }
+
+/* Element i of a payload array, exactly as binary32. */
+static float load_elem(const void* base, int64_t i, int dt) {
+  if (dt == ORACLE_BF16) return bf16_to_float(((const uint16_t*)base)[i]);
+  if (dt == ORACLE_FP16) return ep_oracle_f16_to_f32(((const uint16_t*)base)[i]);
+  float f;
+  memcpy(&f, (const char*)base + 4 * i, sizeof f);
+  return f;
+}
+
+/* Store a binary32 value into element i, rounded once to the payload type. */
+static void store_elem(void* base, int64_t i, int dt, float f) {
+  if (dt == ORACLE_BF16) {
+    ((uint16_t*)base)[i] = ep_oracle_f32_to_bf16(f);
+  } else if (dt == ORACLE_FP16) {
+    ((uint16_t*)base)[i] = ep_oracle_f32_to_f16(f);
+  } else {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) u = 0x7FC00000u;
+    memcpy((char*)base + 4 * i, &u, sizeof u);
+  }
+}
+
+/* +0 in element i. */
+static void store_zero(void* base, int64_t i, int dt) {
+  memset((char*)base + (size_t)i * elem_bytes(dt), 0, elem_bytes(dt));
+}
 
 /* Worst-case number of received rows: every token sends min(K,E) distinct
  * routes and every expert adds up to A-1 pad rows. */
@@ -184,27 +276,32 @@ int ep_oracle_prepare(int64_t T, int32_t K, int32_t E, int32_t A, int64_t cap,
 
 /*
  * dispatch (token part and weight part): received row r holds the token row
- * of the route it came from, or zeros for a pad row. Rows at or past
- * min(total, cap) are not touched.
+ * of the route it came from (a bit copy of its elements), or zeros for a pad
+ * row (left as they are if fill_pads is 0). Rows at or past min(total, cap)
+ * are not touched.
  *
- *   x        bf16 [T*H]     token rows
+ *   x        payload [T*H]  token rows
  *   w        f32  [T*K]     routing weights (may be NULL: then no weight output)
- *   recv     bf16 [cap*H]
+ *   recv     payload [cap*H]
  *   recv_w   f32  [cap]
  */
-int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int64_t cap, int64_t total,
-                       const int32_t* row_src, const uint16_t* x, const float* w,
-                       uint16_t* recv, float* recv_w) {
-  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0) return ORACLE_ERR_ARGS;
+int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads, int64_t cap,
+                       int64_t total, const int32_t* row_src, const void* x, const float* w,
+                       void* recv, float* recv_w) {
+  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0 || !dtype_ok(dtype))
+    return ORACLE_ERR_ARGS;
+  const size_t eb = elem_bytes(dtype);
   const int64_t live = total < cap ? total : cap;
   for (int64_t r = 0; r < live; ++r) {
     int32_t s = row_src[r];
     if (s >= 0) {
       int64_t t = s / K;
-      for (int64_t h = 0; h < H; ++h) recv[r * H + h] = x[t * H + h];
+      for (int64_t h = 0; h < H; ++h)
+        memcpy((char*)recv + (size_t)(r * H + h) * eb, (const char*)x + (size_t)(t * H + h) * eb,
+               eb);
       if (w && recv_w) recv_w[r] = w[s];
-    } else {
-      for (int64_t h = 0; h < H; ++h) recv[r * H + h] = 0;
+    } else if (fill_pads) {
+      for (int64_t h = 0; h < H; ++h) store_zero(recv, r * H + h, dtype);
       if (w && recv_w) recv_w[r] = 0.0f;
     }
   }
@@ -213,23 +310,23 @@ int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int64_t cap, int64_t tot
 
 /* combine_bwd is the same row map as dispatch's token part, applied to the
  * gradient of the combined output. */
-int ep_oracle_combine_bwd(int64_t T, int32_t K, int64_t H, int64_t cap, int64_t total,
-                          const int32_t* row_src, const uint16_t* g_result,
-                          uint16_t* g_expert_out) {
-  return ep_oracle_dispatch(T, K, H, cap, total, row_src, g_result, NULL, g_expert_out,
-                            NULL);
+int ep_oracle_combine_bwd(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads,
+                          int64_t cap, int64_t total, const int32_t* row_src,
+                          const void* g_result, void* g_expert_out) {
+  return ep_oracle_dispatch(T, K, H, dtype, fill_pads, cap, total, row_src, g_result, NULL,
+                            g_expert_out, NULL);
 }
 
 /*
  * combine: for each token, the ordered binary32 sum over its valid routes
- * (k ascending) of the received rows, rounded once to bf16.
+ * (k ascending) of the received rows, rounded once to the payload type.
  *
- *   rows     bf16 [cap*H]   expert outputs, expert-major
- *   out      bf16 [T*H]
+ *   rows     payload [cap*H]   expert outputs, expert-major
+ *   out      payload [T*H]
  */
-int ep_oracle_combine(int64_t T, int32_t K, int64_t H, const int32_t* slot,
-                      const uint16_t* rows, uint16_t* out) {
-  if (T < 0 || K < 1 || H < 1) return ORACLE_ERR_ARGS;
+int ep_oracle_combine(int64_t T, int32_t K, int64_t H, int dtype, const int32_t* slot,
+                      const void* rows, void* out) {
+  if (T < 0 || K < 1 || H < 1 || !dtype_ok(dtype)) return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t h = 0; h < H; ++h) {
@@ -238,7 +335,7 @@ int ep_oracle_combine(int64_t T, int32_t K, int64_t H, const int32_t* slot,
       for (int32_t k = 0; k < K; ++k) {
         int32_t r = slot[t * K + k];
         if (r < 0) continue;
-        float v = bf16_to_float(rows[(int64_t)r * H + h]);
+        float v = load_elem(rows, (int64_t)r * H + h, dtype);
         if (!have) {
           acc = v;
           have = 1;
@@ -246,7 +343,11 @@ int ep_oracle_combine(int64_t T, int32_t K, int64_t H, const int32_t* slot,
           acc = acc + v;
         }
       }
-      out[t * H + h] = have ? ep_oracle_f32_to_bf16(acc) : (uint16_t)0;
+      if (have) {
+        store_elem(out, t * H + h, dtype, acc);
+      } else {
+        store_zero(out, t * H + h, dtype);
+      }
     }
   }
   return ORACLE_OK;
@@ -258,10 +359,10 @@ int ep_oracle_combine(int64_t T, int32_t K, int64_t H, const int32_t* slot,
  * received weight in its slot, or +0 when the route is masked or no weight
  * gradient is given (g_recv_w NULL).
  */
-int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, const int32_t* slot,
-                           const uint16_t* g_recv, const float* g_recv_w,
-                           uint16_t* grad_tokens, float* grad_w) {
-  int rc = ep_oracle_combine(T, K, H, slot, g_recv, grad_tokens);
+int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, int dtype, const int32_t* slot,
+                           const void* g_recv, const float* g_recv_w, void* grad_tokens,
+                           float* grad_w) {
+  int rc = ep_oracle_combine(T, K, H, dtype, slot, g_recv, grad_tokens);
   if (rc != ORACLE_OK) return rc;
   if (!grad_w) return ORACLE_OK;
   for (int64_t s = 0; s < T * (int64_t)K; ++s) {
@@ -272,19 +373,19 @@ int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, const int32_t* slot,
 }
 
 /*
- * Weighted combine (the weight multiply folded into combine, as the review
- * of "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with
- * symm-mem zero-copy" asks, so the caller no longer pre-multiplies; the
- * transformers EP implementations return this weighted output directly).
- * For each token, over its valid routes in ascending k with received row r:
+ * Weighted combine (the weight multiply folded into combine, the option the
+ * review of "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops
+ * with symm-mem zero-copy" settles on in its thread on the weight multiply,
+ * so the caller no longer pre-multiplies). For each token, over its valid
+ * routes in ascending k with received row r:
  *   acc = w[r] * y[r]                     (first valid route: one fp32 product)
  *   acc = fmaf(w[r], y[r], acc)           (later routes: one fused rounding)
- * then one round-to-nearest-even to bf16; +0 if no valid route.
- *   rows  bf16 [cap*H], w f32 [cap], out bf16 [T*H]
+ * then one rounding to the payload type; +0 if no valid route.
+ *   rows  payload [cap*H], w f32 [cap], out payload [T*H]
  */
-int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, const int32_t* slot,
-                               const uint16_t* rows, const float* w, uint16_t* out) {
-  if (T < 0 || K < 1 || H < 1) return ORACLE_ERR_ARGS;
+int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, int dtype, const int32_t* slot,
+                               const void* rows, const float* w, void* out) {
+  if (T < 0 || K < 1 || H < 1 || !dtype_ok(dtype)) return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t h = 0; h < H; ++h) {
@@ -293,7 +394,7 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, const int32_t* s
       for (int32_t k = 0; k < K; ++k) {
         int32_t r = slot[t * K + k];
         if (r < 0) continue;
-        float y = bf16_to_float(rows[(int64_t)r * H + h]);
+        float y = load_elem(rows, (int64_t)r * H + h, dtype);
         if (!have) {
           acc = w[r] * y;
           have = 1;
@@ -301,7 +402,11 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, const int32_t* s
           acc = fmaf(w[r], y, acc);
         }
       }
-      out[t * H + h] = have ? ep_oracle_f32_to_bf16(acc) : (uint16_t)0;
+      if (have) {
+        store_elem(out, t * H + h, dtype, acc);
+      } else {
+        store_zero(out, t * H + h, dtype);
+      }
     }
   }
   return ORACLE_OK;
@@ -310,24 +415,28 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, const int32_t* s
 /*
  * Backward of the weighted combine, for every live received row r holding
  * route s of token t = s / K:
- *   grad_rows[r, h] = bf16(fp32(w[r] * g[t, h]))       (pads: +0)
- *   grad_w[r]       = sum over h of g[t, h] * rows[r, h] (pads: +0)
- * The weight gradient is a dot product whose summation order the method does
- * not fix; the oracle returns it exactly rounded from a double-precision sum
- * (grad_w64), and the tests compare the GPU's fp32 result within the
- * summation error bound. grad_w64 may be NULL (then rows is not read).
+ *   grad_rows[r, h] = payload(fp32(w[r] * g[t, h]))       (pads: +0)
+ *   grad_w[r]       = sum over h of g[t, h] * rows[r, h]   (pads: +0)
+ * Pads are left as they are when fill_pads is 0. The weight gradient is a
+ * dot product whose summation order the method does not fix; the oracle
+ * returns it from a double-precision sum of the exact products (grad_w64)
+ * together with the sum of their magnitudes (abs_dot64), and the tests
+ * compare the GPU's fp32 result within the summation error bound. grad_w64
+ * may be NULL (then rows is not read).
  */
-int ep_oracle_combine_weighted_bwd(int64_t T, int32_t K, int64_t H, int64_t cap,
-                                   int64_t total, const int32_t* row_src, const uint16_t* g,
-                                   const uint16_t* rows, const float* w, uint16_t* grad_rows,
-                                   double* grad_w64, double* abs_dot64) {
-  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0) return ORACLE_ERR_ARGS;
+int ep_oracle_combine_weighted_bwd(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads,
+                                   int64_t cap, int64_t total, const int32_t* row_src,
+                                   const void* g, const void* rows, const float* w,
+                                   void* grad_rows, double* grad_w64, double* abs_dot64) {
+  if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0 || !dtype_ok(dtype))
+    return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
   const int64_t live = total < cap ? total : cap;
   for (int64_t r = 0; r < live; ++r) {
     int32_t s = row_src[r];
     if (s < 0) {
-      for (int64_t h = 0; h < H; ++h) grad_rows[r * H + h] = 0;
+      if (!fill_pads) continue;
+      for (int64_t h = 0; h < H; ++h) store_zero(grad_rows, r * H + h, dtype);
       if (grad_w64) grad_w64[r] = 0.0;
       if (abs_dot64) abs_dot64[r] = 0.0;
       continue;
@@ -335,11 +444,12 @@ int ep_oracle_combine_weighted_bwd(int64_t T, int32_t K, int64_t H, int64_t cap,
     int64_t t = s / K;
     double dot = 0.0, adot = 0.0;
     for (int64_t h = 0; h < H; ++h) {
-      float gv = bf16_to_float(g[t * H + h]);
+      float gv = load_elem(g, t * H + h, dtype);
       float p = w[r] * gv;
-      grad_rows[r * H + h] = ep_oracle_f32_to_bf16(p);
+      store_elem(grad_rows, r * H + h, dtype, p);
       if (grad_w64) {
-        double term = (double)gv * (double)bf16_to_float(rows[r * H + h]);
+        /* a product of two binary32 values is exact in binary64 */
+        double term = (double)gv * (double)load_elem(rows, r * H + h, dtype);
         dot += term;
         adot += term < 0 ? -term : term;
       }

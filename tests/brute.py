@@ -26,6 +26,35 @@ def bf16_to_f32_np(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_to_f32_np(b: np.ndarray) -> np.ndarray:
+    """NumPy's binary16 -> binary32 (exact)."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_np(a: np.ndarray) -> np.ndarray:
+    """NumPy's binary32 -> binary16 (round to nearest even); NaNs then set to
+    the canonical quiet NaN 0x7E00."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        out = a.astype(np.float16).view(np.uint16).copy()
+    out[np.isnan(a)] = 0x7E00
+    return out
+
+
+def f32_canon_np(a: np.ndarray) -> np.ndarray:
+    out = np.array(a, dtype=np.float32, copy=True)
+    out.view(np.uint32)[np.isnan(out)] = 0x7FC00000
+    return out
+
+
+# payload type -> (widen to fp32, round fp32 once to the type)
+CODECS = {
+    "bf16": (bf16_to_f32_np, f32_to_bf16_torch),
+    "fp16": (f16_to_f32_np, f32_to_f16_np),
+    "fp32": (lambda a: np.asarray(a, dtype=np.float32), f32_canon_np),
+}
+
+
 def prepare(topk_idx: np.ndarray, E: int, A: int, cap: int):
     idx = np.asarray(topk_idx, dtype=np.int64)
     T, K = idx.shape
@@ -56,7 +85,7 @@ def prepare(topk_idx: np.ndarray, E: int, A: int, cap: int):
 
 def dispatch(prep, x: np.ndarray, w: np.ndarray | None, K: int, cap: int):
     T, H = x.shape
-    recv = np.zeros((cap, H), np.uint16)
+    recv = np.zeros((cap, H), x.dtype)
     recv_w = np.zeros(cap, np.float32)
     for s, r in enumerate(prep["slot"]):
         if r >= 0:
@@ -66,7 +95,8 @@ def dispatch(prep, x: np.ndarray, w: np.ndarray | None, K: int, cap: int):
     return recv, recv_w
 
 
-def combine(prep, rows: np.ndarray, T: int, K: int):
+def combine(prep, rows: np.ndarray, T: int, K: int, dtype: str = "bf16"):
+    widen, narrow = CODECS[dtype]
     H = rows.shape[1]
     slot = prep["slot"].reshape(T, K)
     acc = np.zeros((T, H), np.float32)
@@ -74,14 +104,14 @@ def combine(prep, rows: np.ndarray, T: int, K: int):
     for k in range(K):
         r = slot[:, k]
         ok = r >= 0
-        v = bf16_to_f32_np(rows[np.where(ok, r, 0)])
+        v = widen(rows[np.where(ok, r, 0)])
         first = ok & ~have
         later = ok & have
         acc[first] = v[first]
         with np.errstate(over="ignore", invalid="ignore"):
             acc[later] = acc[later] + v[later]
         have |= ok
-    out = f32_to_bf16_torch(acc)
+    out = narrow(acc)
     out[~have] = 0
     return out
 

@@ -93,10 +93,32 @@ def test_bad_layouts_rejected(kw, code):
     assert ep.lib.ep_handle_regions(C.byref(L), C.byref(r)) == code
 
 
-def test_reserved_field_must_be_zero():
+@pytest.mark.parametrize("dtype,flags,ok", [
+    (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True),
+    (3, 0, False), (0xFFFF, 0, False), (0, 2, False), (0, 0x8001, False),
+])
+def test_payload_type_and_flags_validated(dtype, flags, ok):
     L = lay()
-    L.reserved = 1
-    assert ep.handle_mem_size(L) == 0
+    L.dtype = dtype
+    L.flags = flags
+    n = ep.handle_mem_size(L)
+    if ok:
+        # neither the payload type nor the pad policy changes the handle
+        assert n == ep.handle_mem_size(lay())
+    else:
+        assert n == 0
+        assert ep.lib.ep_dispatch(C.byref(L), P, 1 << 30, P, None, P2, None, None) == \
+            ep.EP_ERR_SHAPE
+
+
+def test_layout_struct_matches_header():
+    # field offsets of ep_layout_t as declared in include/ep.h
+    assert C.sizeof(ep.Layout) == 40
+    assert [getattr(ep.Layout, f).offset for f in
+            ("num_tokens", "topk", "num_experts", "alignment", "dtype", "flags", "hidden",
+             "recv_capacity")] == [0, 8, 12, 16, 20, 22, 24, 32]
+    L = ep.Layout(4, 2, 8, 16, 512, 100, dtype="fp16", fill_pads=False)
+    assert (L.dtype, L.flags) == (ep.DTYPE_FP16, ep.LAYOUT_NO_PAD_FILL)
 
 
 def test_null_layout_and_pointers():
