@@ -10,11 +10,22 @@ The headline is dispatch+combine throughput in algorithmic HBM GB/s (bytes
 the method must move, see ``algorithmic_bytes``) over their kernel time,
 measured with HIP events recorded on the stream the kernels run on. The line
 also carries the roofline of the dominant kernel and the CPU oracle timed on a
-bounded sample of the same workload on this host. The fused weighted combine
-and its backward are timed after the step, the same way, and reported beside
-it ("ops_outside_step").
+bounded sample of the same workload on this host.
+
+After the step, the variants outside it are timed the same way, one op at a
+time, and reported under "ops_outside_step": the fused weighted combine and
+its backward, dispatch and combine_bwd without the pad fill, combine on fp16
+payloads, dispatch and combine on fp32 payloads.
 
     python bench.py [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
+
+Profiling (rocprofv3 on the GPU machine, then summarised here):
+    --schedule-out FILE   record, in launch order, the op of every payload
+                          kernel launch (prepare excluded), so that profiled
+                          dispatches can be attributed to ops
+    --summarize-trace DIR / --summarize-pmc FETCH_DIR WRITE_DIR
+                          write the profiles/ summaries from rocprofv3 output
+                          directories that hold such a schedule.json
 """
 from __future__ import annotations
 
@@ -33,6 +44,27 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_ep_prepare_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_api.hip", "ep_internal.h")]
 
+STEP_OPS = ["prepare", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
+
+# op -> the library kernel that runs it
+KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
+                "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel",
+                "combine_weighted": "reduce_rows_kernel",
+                "combine_weighted_bwd": "weighted_bwd_kernel",
+                "dispatch_nopad": "scatter_rows_kernel",
+                "combine_bwd_nopad": "scatter_rows_kernel",
+                "combine_fp16": "reduce_rows_kernel",
+                "dispatch_fp32": "scatter_rows_kernel",
+                "combine_fp32": "reduce_rows_kernel"}
+PAYLOAD_KERNELS = ("scatter_rows_kernel", "reduce_rows_kernel", "weighted_bwd_kernel")
+
+# ops timed after the step: op -> (payload type, pads filled)
+EXTRA_OPS = {"combine_weighted": ("bf16", True), "combine_weighted_bwd": ("bf16", True),
+             "dispatch_nopad": ("bf16", False), "combine_bwd_nopad": ("bf16", False),
+             "combine_fp16": ("fp16", True), "dispatch_fp32": ("fp32", True),
+             "combine_fp32": ("fp32", True)}
+ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -46,38 +78,79 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np):
+def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np, esize=2, fill_pads=True):
     """Bytes each op must move at minimum (each row once).
 
-    B = 2H bytes per bf16 row, R valid routes, P pad rows, T_act tokens with
-    at least one valid route.
-      dispatch      T_act*B + (R+P)*B + 4R + 8(R+P)   rows, weights in/out, row map
-      combine       R*B + T*B + 4TK                   rows in/out, slot map
-      combine_bwd   T_act*B + (R+P)*B + 4(R+P)        rows in/out, row map
-      dispatch_bwd  R*B + 4R + T*B + 8TK              rows in/out, weights, slot map
-      prepare       8TK + 4TK + 4(R+P) + 8E           ids, slots, row map, counts
-      combine_weighted      R*B + 4R + T*B + 4TK      rows and weights in, rows out, slot map
-      combine_weighted_bwd  T_act*B + R*B + 4R + (R+P)*B + 4(R+P) + 4TK + 4P
+    B = esize*H bytes per row, R valid routes, P pad rows (Pw = P when pads
+    are filled, else 0), T_act tokens with at least one valid route.
+      dispatch      T_act*B + (R+Pw)*B + 4R + 8(R+Pw)  rows, weights in/out, row map
+      combine       R*B + T*B + 4TK                    rows in/out, slot map
+      combine_bwd   T_act*B + (R+Pw)*B + 4(R+Pw)       rows in/out, row map
+      dispatch_bwd  R*B + 4R + T*B + 8TK               rows in/out, weights, slot map
+      prepare       8TK + 4TK + 4(R+P) + 8E            ids, slots, row map, counts
+      combine_weighted      R*B + 4R + T*B + 4TK       rows and weights in, rows out,
+                                                       slot map
+      combine_weighted_bwd  T_act*B + R*B + 4R + (R+Pw)*B + 4(R+Pw) + 4TK + 4Pw
                             grads in, expert rows and weights in, row and weight
                             grads out, slot map, pad-row list
     """
-    import numpy as np
-    B = 2 * H
+    B = esize * H
     R = int(counts_np.sum())
     total = int(offsets_np[-1])
     P = total - R
+    Pw = P if fill_pads else 0
     T_act = int((topk_idx >= 0).any(axis=1).sum()) if T else 0
     return {
-        "dispatch": T_act * B + (R + P) * B + 4 * R + 8 * (R + P),
+        "dispatch": T_act * B + (R + Pw) * B + 4 * R + 8 * (R + Pw),
         "combine": R * B + T * B + 4 * T * K,
-        "combine_bwd": T_act * B + (R + P) * B + 4 * (R + P),
+        "combine_bwd": T_act * B + (R + Pw) * B + 4 * (R + Pw),
         "dispatch_bwd": R * B + 4 * R + T * B + 8 * T * K,
         "prepare": 8 * T * K + 4 * T * K + 4 * (R + P) + 8 * E,
         "combine_weighted": R * B + 4 * R + T * B + 4 * T * K,
-        "combine_weighted_bwd": (T_act * B + R * B + 4 * R + (R + P) * B + 4 * (R + P)
-                                 + 4 * T * K + 4 * P),
+        "combine_weighted_bwd": (T_act * B + R * B + 4 * R + (R + Pw) * B + 4 * (R + Pw)
+                                 + 4 * T * K + 4 * Pw),
         "_R": R, "_P": P, "_T_act": T_act, "_total": total,
     }
+
+
+def base_op(op: str) -> str:
+    """dispatch_fp32 -> dispatch, combine_bwd_nopad -> combine_bwd, ..."""
+    for suffix in ("_nopad", "_fp16", "_fp32"):
+        if op.endswith(suffix):
+            return op[:-len(suffix)]
+    return op
+
+
+def attribute(kernel_names, schedule):
+    """Pair the library's payload-kernel dispatches (demangled names in
+    dispatch order, all other kernels already left out) with the ops recorded
+    in launch order. Raises if the two do not line up."""
+    if len(kernel_names) != len(schedule):
+        raise SystemExit(f"{len(kernel_names)} payload dispatches profiled but "
+                         f"{len(schedule)} launches recorded")
+    for i, (name, op) in enumerate(zip(kernel_names, schedule)):
+        if KERNEL_OF_OP[op] not in name:
+            raise SystemExit(f"dispatch {i}: {name} does not run {op}")
+    return list(schedule)
+
+
+def _read_csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _schedule(directory: str):
+    with open(os.path.join(directory, "schedule.json")) as f:
+        return json.load(f)["ops"]
+
+
+def _is_payload(name: str) -> bool:
+    return any(k in name for k in PAYLOAD_KERNELS)
 
 
 def _pmc_path(op: str, workload: str) -> str:
@@ -101,82 +174,35 @@ def load_traffic(op: str, workload: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def _read_csv_rows(directory: str, suffix: str):
-    import csv
-    import glob
-    rows = []
-    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
-        with open(path, newline="") as f:
-            rows.extend(csv.DictReader(f))
-    return rows
-
-
-KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
-                "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel",
-                "combine_weighted": "reduce_rows_kernel",
-                "combine_weighted_bwd": "weighted_bwd_kernel"}
-
-
-def op_sequence(names):
-    """Attribute each payload-kernel dispatch (demangled names, in dispatch
-    order) to its op. Within a step the unweighted scatter runs for dispatch,
-    then combine_bwd; the unweighted reduce for combine, then dispatch_bwd.
-    The weighted reduce (template flag true) and the weighted backward kernel
-    each serve one op. Other kernels map to None."""
-    out = []
-    n_scatter = n_reduce = 0
-    for name in names:
-        if "scatter_rows_kernel" in name:
-            out.append(("dispatch", "combine_bwd")[n_scatter % 2])
-            n_scatter += 1
-        elif "reduce_rows_kernel" in name and "true" in name:
-            out.append("combine_weighted")
-        elif "reduce_rows_kernel" in name:
-            out.append(("combine", "dispatch_bwd")[n_reduce % 2])
-            n_reduce += 1
-        elif "weighted_bwd_kernel" in name:
-            out.append("combine_weighted_bwd")
-        else:
-            out.append(None)
-    return out
-
-
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
                   out_dir: str = PROFILE_DIR):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE, both with --calibration-copy-mib) into per-op HBM bytes.
+    WRITE_SIZE, both with --calibration-copy-mib and --schedule-out
+    <dir>/schedule.json) into per-op HBM bytes.
 
     Each counter is scaled by what it reads for the plain copy of known size
-    (PyTorch's elementwise copy kernel, the largest dispatch whose name holds
-    "copy"), so the result is in true bytes. Dispatches of our two payload
-    kernels are attributed to ops by their order inside each step: scatter
-    (dispatch), reduce (combine), scatter (combine_bwd), reduce (dispatch_bwd).
-    """
+    (the runtime's copyBuffer kernel, which PyTorch's device-to-device copy
+    uses), so the result is in true bytes. Payload dispatches are attributed
+    to ops through the recorded launch schedule."""
     import numpy as np
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _read_csv_rows(d, "counter_collection.csv")
                 if r.get("Counter_Name") == counter]
         rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
-        # the calibration copy is a plain device-to-device copy of copy_mib
-        # MiB (PyTorch hands it to the runtime's copyBuffer kernel)
         calib = [r for r in rows if "copybuffer" in r["Kernel_Name"].lower()
                  and float(r["Counter_Value"]) > copy_mib * 1024.0 / 8]
         if not calib:
             raise SystemExit(f"no calibration copy found for {counter} in {d}")
         expected_kib = copy_mib * 1024.0
         factor = float(np.median([float(r["Counter_Value"]) for r in calib])) / expected_kib
-        # the timed steps follow the calibration copy; the one dispatch made
-        # before it (to build the expert outputs) is left out
-        last_copy = max(int(r.get("Dispatch_Id", 0)) for r in calib)
-        seq = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows
-               if int(r.get("Dispatch_Id", 0)) > last_copy]
-        per_op = {op: [] for op in KERNEL_OF_OP}
-        for (name, kib), op in zip(seq, op_sequence([nm for nm, _ in seq])):
-            if op is not None:
-                per_op[op].append(kib / factor * 1024.0)
+        pay = [r for r in rows if _is_payload(r["Kernel_Name"])]
+        ops = attribute([r["Kernel_Name"] for r in pay], _schedule(d))
+        per_op = {}
+        for r, op in zip(pay, ops):
+            per_op.setdefault(op, []).append(float(r["Counter_Value"]) / factor * 1024.0)
         res[counter] = {"factor": factor,
-                        "per_op_bytes": {op: float(np.median(v)) for op, v in per_op.items() if v}}
+                        "per_op_bytes": {op: float(np.median(v)) for op, v in per_op.items()}}
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
            "calibration": {"copy_mib": copy_mib,
                            "fetch_factor": res["FETCH_SIZE"]["factor"],
@@ -184,9 +210,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
     cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc <COUNTER> "
            "-d <dir> -o <name> --output-format csv -- python3 bench.py --workload "
            f"{workload} --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy-mib {copy_mib}"
-           "   (once with FETCH_SIZE, once with WRITE_SIZE); then python bench.py "
-           f"--summarize-pmc <fetch dir> <write dir> --workload {workload} "
-           f"--calibration-copy-mib {copy_mib}")
+           " --schedule-out <dir>/schedule.json   (once with FETCH_SIZE, once with "
+           "WRITE_SIZE); then python bench.py --summarize-pmc <fetch dir> <write dir> "
+           f"--workload {workload} --calibration-copy-mib {copy_mib}")
     for op in KERNEL_OF_OP:
         fb = res["FETCH_SIZE"]["per_op_bytes"].get(op)
         wb = res["WRITE_SIZE"]["per_op_bytes"].get(op)
@@ -202,8 +228,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
             f.write(f"# FETCH_SIZE scale {out['calibration']['fetch_factor']:.4f}, WRITE_SIZE "
                     f"scale {out['calibration']['write_factor']:.4f} (counter / true bytes of "
                     f"a {copy_mib} MiB device copy in the same run)\n")
-            f.write(f"# per launch (median over the timed steps): fetch {fb / 1e6:.1f} MB, "
-                    f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB\n")
+            f.write(f"# per launch (median over the profiled launches): fetch "
+                    f"{fb / 1e6:.1f} MB, write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB\n")
             f.write("JSON: " + json.dumps(summary) + "\n")
         print(f"{path}: fetch {fb / 1e6:.1f} MB write {wb / 1e6:.1f} MB", flush=True)
 
@@ -211,12 +237,31 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
 def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
                     out_dir: str = PROFILE_DIR):
     """profiles/ep_kernels_<workload>_kernel_stats.txt from a rocprofv3
-    --kernel-trace --stats run of this script."""
+    --kernel-trace --stats run of this script with --schedule-out
+    <dir>/schedule.json: rocprofv3's per-kernel statistics, then the same
+    dispatches grouped by op."""
+    import numpy as np
     rows = _read_csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _read_csv_rows(trace_dir, "kernel_trace.csv")
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    pay = [r for r in trace if _is_payload(r["Kernel_Name"])]
+    ops = attribute([r["Kernel_Name"] for r in pay], _schedule(trace_dir))
+    per_op = {}
+    for r, op in zip(pay, ops):
+        per_op.setdefault(op, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    prep = {}
+    for r in trace:
+        for k in ("prepare_hist_kernel", "prepare_slots_kernel"):
+            if k in r["Kernel_Name"]:
+                prep.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     path = os.path.join(out_dir, f"ep_kernels_{workload}_kernel_stats.txt")
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <dir> -o "
            f"trace --output-format csv -- python3 bench.py --workload {workload} --steps "
-           f"{steps} --warmup {warmup} --no-cpu-baseline")
+           f"{steps} --warmup {warmup} --no-cpu-baseline --schedule-out <dir>/schedule.json; "
+           f"then python bench.py --summarize-trace <dir> --workload {workload} --steps "
+           f"{steps} --warmup {warmup}")
     with open(path, "w") as f:
         f.write(f"# rocprofv3 kernel statistics, workload {workload}\n")
         f.write(f"# command: {cmd}\n")
@@ -229,20 +274,25 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
             f.write(f"{short[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
                     f"{float(r['Percentage']):7.2f}\n")
+        f.write("\n# the payload dispatches by op (kernel trace, launch schedule)\n")
+        f.write(f"{'op':24s} {'kernel':22s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
+                f"{'max_us':>9s}\n")
+        for op, v in list(per_op.items()) + list(prep.items()):
+            kern = KERNEL_OF_OP.get(op, op)
+            f.write(f"{op:24s} {kern:22s} {len(v):6d} {np.mean(v):9.2f} {np.min(v):9.2f} "
+                    f"{np.max(v):9.2f}\n")
     print(path, flush=True)
 
 
 def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
     """The oracle as it stands, single-threaded, on the same inputs: whole
     steps repeated until the time budget is spent (at least one)."""
-    import numpy as np
     import oracle
     oracle.build()
     t_d = t_c = 0.0
     n = 0
     start = time.perf_counter()
     while True:
-        t0 = time.perf_counter()
         p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, cap)
         t1 = time.perf_counter()
         oracle.dispatch(p, host["x"], r.topk_weights)
@@ -267,10 +317,12 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-ops", action="store_true",
-                    help="skip timing the weighted combine and its backward")
+                    help="skip timing the ops outside the step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
+    ap.add_argument("--schedule-out", metavar="FILE",
+                    help="write the op of every payload kernel launch, in order, as JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*_pmc.txt from two rocprofv3 counter runs")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -322,10 +374,12 @@ def main():
     g_recv_w = workloads.randn_bf16_torch((cap,), 4).float()
     g_tok = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     g_w = torch.empty(T, K, dtype=torch.float32, device=dev)
+    schedule = []          # op of every payload kernel launch, in order
 
     # The experts' stand-in: expert_out = bf16(recv * recv_topk_weights),
     # computed once outside the timed region (the caller's pre-multiply).
     ep.prepare(L, idx, counts, handle, offsets)
+    schedule.append("dispatch")
     ep.dispatch(L, handle, x, w, recv, recv_w)
     expert_out = (recv.float() * recv_w[:, None]).to(torch.bfloat16)
     torch.cuda.synchronize()
@@ -344,34 +398,31 @@ def main():
         torch.cuda.synchronize()
         del src_c, dst_c
 
-    ops = ["prepare", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
     stream = torch.cuda.current_stream()
+    step_fns = [
+        ("prepare", lambda: ep.prepare(L, idx, counts, handle, offsets)),
+        ("dispatch", lambda: ep.dispatch(L, handle, x, w, recv, recv_w)),
+        ("combine", lambda: ep.combine(L, handle, expert_out, result)),
+        ("combine_bwd", lambda: ep.combine_bwd(L, handle, g_result, g_exp)),
+        ("dispatch_bwd", lambda: ep.dispatch_bwd(L, handle, g_recv, g_recv_w, g_tok, g_w)),
+    ]
 
     def step(ev=None):
+        for j, (op, fn) in enumerate(step_fns):
+            if ev is not None:
+                ev[j].record(stream)
+            if op != "prepare":
+                schedule.append(op)
+            fn()
         if ev is not None:
-            ev[0].record(stream)
-        ep.prepare(L, idx, counts, handle, offsets)
-        if ev is not None:
-            ev[1].record(stream)
-        ep.dispatch(L, handle, x, w, recv, recv_w)
-        if ev is not None:
-            ev[2].record(stream)
-        ep.combine(L, handle, expert_out, result)
-        if ev is not None:
-            ev[3].record(stream)
-        ep.combine_bwd(L, handle, g_result, g_exp)
-        if ev is not None:
-            ev[4].record(stream)
-        ep.dispatch_bwd(L, handle, g_recv, g_recv_w, g_tok, g_w)
-        if ev is not None:
-            ev[5].record(stream)
+            ev[len(step_fns)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     assert ep.read_status(handle) == 0, "unexpected status bits"
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step_fns) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -380,58 +431,83 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    per_op_ms = {op: [] for op in ops}
+    per_op_ms = {op: [] for op in STEP_OPS}
     for ev in events:
-        for j, op in enumerate(ops):
+        for j, op in enumerate(STEP_OPS):
             per_op_ms[op].append(ev[j].elapsed_time(ev[j + 1]))
     avg = {op: float(np.mean(v)) for op, v in per_op_ms.items()}
     med = {op: float(np.median(v)) for op, v in per_op_ms.items()}
 
-    # The fused weighted combine and its backward: not part of the step (the
-    # step's combine is the unweighted one), timed the same way after it.
-    extra_ops = [] if args.no_extra_ops else ["combine_weighted", "combine_weighted_bwd"]
-    if extra_ops:
+    # Ops outside the step, timed one at a time over the same number of
+    # launches after the same warmup.
+    extra = {}
+    if not args.no_extra_ops:
+        lay = {key: ep.Layout(T, K, E, A, H, cap, dtype=key[0], fill_pads=key[1])
+               for key in set(EXTRA_OPS.values())}
         result_w = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         g_rows_w = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
         g_recv_w2 = torch.empty(cap, dtype=torch.float32, device=dev)
-
-        def extra(ev=None):
-            if ev is not None:
-                ev[0].record(stream)
-            ep.combine_weighted(L, handle, recv, recv_w, result_w)
-            if ev is not None:
-                ev[1].record(stream)
-            ep.combine_weighted_bwd(L, handle, g_result, recv, recv_w, g_rows_w, g_recv_w2)
-            if ev is not None:
-                ev[2].record(stream)
-
-        for _ in range(args.warmup):
-            extra()
-        xev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            extra(xev[i])
-        torch.cuda.synchronize()
-        assert ep.read_status(handle) == 0, "unexpected status bits"
-        for j, op in enumerate(extra_ops):
-            v = [ev[j].elapsed_time(ev[j + 1]) for ev in xev]
+        recv_np = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+        recv_w_np = torch.empty(cap, dtype=torch.float32, device=dev)
+        g_exp_np = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+        eo16 = expert_out.to(torch.float16)
+        res16 = torch.empty(T, H, dtype=torch.float16, device=dev)
+        x32 = x.float()
+        recv32 = torch.empty(cap, H, dtype=torch.float32, device=dev)
+        recv_w32 = torch.empty(cap, dtype=torch.float32, device=dev)
+        eo32 = expert_out.float()
+        res32 = torch.empty(T, H, dtype=torch.float32, device=dev)
+        fns = {
+            "combine_weighted": lambda Lx: ep.combine_weighted(Lx, handle, recv, recv_w,
+                                                               result_w),
+            "combine_weighted_bwd": lambda Lx: ep.combine_weighted_bwd(
+                Lx, handle, g_result, recv, recv_w, g_rows_w, g_recv_w2),
+            "dispatch_nopad": lambda Lx: ep.dispatch(Lx, handle, x, w, recv_np, recv_w_np),
+            "combine_bwd_nopad": lambda Lx: ep.combine_bwd(Lx, handle, g_result, g_exp_np),
+            "combine_fp16": lambda Lx: ep.combine(Lx, handle, eo16, res16),
+            "dispatch_fp32": lambda Lx: ep.dispatch(Lx, handle, x32, w, recv32, recv_w32),
+            "combine_fp32": lambda Lx: ep.combine(Lx, handle, eo32, res32),
+        }
+        for op, (dt, fill) in EXTRA_OPS.items():
+            Lx = lay[(dt, fill)]
+            fn = fns[op]
+            for _ in range(args.warmup):
+                schedule.append(op)
+                fn(Lx)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                a.record(stream)
+                schedule.append(op)
+                fn(Lx)
+                b.record(stream)
+            torch.cuda.synchronize()
+            v = [a.elapsed_time(b) for a, b in evs]
             avg[op] = float(np.mean(v))
             med[op] = float(np.median(v))
+            nb = algorithmic_bytes(T, K, E, H, r.topk_idx, counts_np, offsets_np,
+                                   esize=ESIZE[dt], fill_pads=fill)
+            extra[op] = nb[base_op(op)]
+        assert ep.read_status(handle) == 0, "unexpected status bits"
 
-    def gbs(op):
-        return nbytes[op] / (avg[op] * 1e-3) / 1e9
+    if args.schedule_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.schedule_out)), exist_ok=True)
+        with open(args.schedule_out, "w") as f:
+            json.dump({"ops": schedule}, f)
+
+    def gbs(op, nb):
+        return nb / (avg[op] * 1e-3) / 1e9
 
     pair_bytes = nbytes["dispatch"] + nbytes["combine"]
     pair_s = (avg["dispatch"] + avg["combine"]) * 1e-3
     value = pair_bytes / pair_s / 1e9
     dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
                    key=lambda op: avg[op])
-    kernel_of = KERNEL_OF_OP
     src_hash = kernel_source_hash()
     traffic = load_traffic(dominant, cfg.name, src_hash)
-    achieved = gbs(dominant)
-    roofline = {"bound": "hbm", "kernel": f"{kernel_of[dominant]} ({dominant})",
+    achieved = gbs(dominant, nbytes[dominant])
+    roofline = {"bound": "hbm", "kernel": f"{KERNEL_OF_OP[dominant]} ({dominant})",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -476,13 +552,13 @@ def main():
         "tokens_per_s": round(T / pair_s, 1),
         "ops": {op: {"avg_us": round(avg[op] * 1e3, 2), "median_us": round(med[op] * 1e3, 2),
                      "algorithmic_bytes": nbytes[op],
-                     "GBps": round(gbs(op), 1) if op != "prepare" else None}
-                for op in ops},
+                     "GBps": round(gbs(op, nbytes[op]), 1) if op != "prepare" else None}
+                for op in STEP_OPS},
         "ops_outside_step": {op: {"avg_us": round(avg[op] * 1e3, 2),
                                   "median_us": round(med[op] * 1e3, 2),
-                                  "algorithmic_bytes": nbytes[op],
-                                  "GBps": round(gbs(op), 1)}
-                             for op in extra_ops},
+                                  "algorithmic_bytes": nb,
+                                  "GBps": round(gbs(op, nb), 1)}
+                             for op, nb in extra.items()},
         "routing": {"R": nbytes["_R"], "P": nbytes["_P"], "total": nbytes["_total"],
                     "T_act": nbytes["_T_act"]},
         "roofline": roofline,

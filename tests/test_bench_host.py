@@ -1,6 +1,7 @@
 """Host-side logic of the benchmark: algorithmic byte counts on a tiny
 hand-worked routing, and the attribution of profiled kernel dispatches to ops."""
 import numpy as np
+import pytest
 
 import bench
 
@@ -25,15 +26,36 @@ def test_algorithmic_bytes_hand_worked():
                                          + 4 * P)
 
 
-def test_op_sequence_attribution():
-    names = ["epmi::prepare_hist_kernel", "epmi::scatter_rows_kernel<8, 8>",
-             "epmi::reduce_rows_kernel<8, 2, false>", "epmi::scatter_rows_kernel<8, 8>",
-             "epmi::reduce_rows_kernel<8, 2, false>", "at::native::copy",
-             "epmi::scatter_rows_kernel<8, 8>", "epmi::reduce_rows_kernel<8, 2, false>",
-             "epmi::reduce_rows_kernel<8, 2, true>", "epmi::weighted_bwd_kernel<8>"]
-    assert bench.op_sequence(names) == [
-        None, "dispatch", "combine", "combine_bwd", "dispatch_bwd", None, "dispatch",
-        "combine", "combine_weighted", "combine_weighted_bwd"]
+def test_variant_bytes():
+    idx = np.array([[0, 1], [1, -1], [-1, -1]], np.int64)
+    counts = np.array([1, 2], np.int32)
+    offsets = np.array([0, 4, 8], np.int32)
+    R, P, T_act = 3, 5, 2
+    # fp32 rows: B = 32 bytes; no pad fill: pads neither written nor mapped
+    b = bench.algorithmic_bytes(3, 2, 2, 8, idx, counts, offsets, esize=4, fill_pads=False)
+    assert b["dispatch"] == T_act * 32 + R * 32 + 4 * R + 8 * R
+    assert b["combine_bwd"] == T_act * 32 + R * 32 + 4 * R
+    assert b["combine"] == R * 32 + 3 * 32 + 4 * 6
+    assert b["prepare"] == 8 * 6 + 4 * 6 + 4 * (R + P) + 8 * 2
+    assert bench.base_op("dispatch_nopad") == "dispatch"
+    assert bench.base_op("combine_bwd_nopad") == "combine_bwd"
+    assert bench.base_op("combine_fp32") == "combine"
+    assert bench.base_op("combine_weighted_bwd") == "combine_weighted_bwd"
+    for op in bench.EXTRA_OPS:
+        assert bench.base_op(op) in b and op in bench.KERNEL_OF_OP
+
+
+def test_attribution_follows_the_launch_schedule():
+    names = ["epmi::scatter_rows_kernel<8, 8>", "epmi::reduce_rows_kernel<8, 2, false, 0>",
+             "epmi::scatter_rows_kernel<8, 8>", "epmi::reduce_rows_kernel<8, 2, true, 0>",
+             "epmi::weighted_bwd_kernel<8, 0>", "epmi::scatter_rows_kernel<8, 8>"]
+    sched = ["dispatch", "combine", "dispatch_fp32", "combine_weighted",
+             "combine_weighted_bwd", "combine_bwd_nopad"]
+    assert bench.attribute(names, sched) == sched
+    with pytest.raises(SystemExit):
+        bench.attribute(names, sched[:-1])           # a launch missing from the record
+    with pytest.raises(SystemExit):
+        bench.attribute(names, ["combine"] + sched[1:])   # a scatter recorded as combine
 
 
 def test_more_than_one_gpu_is_refused():
