@@ -31,16 +31,21 @@ from . import (Layout, combine as _combine, combine_bwd as _combine_bwd,
 
 
 class EpRouting:
-    """One prepared routing: layout, handle, token counts and segment offsets."""
+    """One prepared routing: handle, token counts and segment offsets. The
+    handle does not depend on the payload type, so one routing serves bf16,
+    fp16 and fp32 payloads; ``fill_pads=False`` leaves pad rows unwritten."""
 
     def __init__(self, topk_idx: torch.Tensor, num_experts: int, alignment: int, hidden: int,
-                 recv_capacity: Optional[int] = None):
+                 recv_capacity: Optional[int] = None, fill_pads: bool = True):
         if topk_idx.dtype != torch.int64:
             raise TypeError("topk_idx must be int64")
         T, K = topk_idx.shape
         if recv_capacity is None:
             recv_capacity = recv_capacity_worst(T, K, num_experts, alignment)
-        self.layout = Layout(T, K, num_experts, alignment, hidden, recv_capacity)
+        self._dims = (T, K, num_experts, alignment, hidden, recv_capacity)
+        self.fill_pads = fill_pads
+        self._layouts = {}
+        self.layout = self.layout_for(torch.bfloat16)
         self.handle = new_handle(self.layout, device=topk_idx.device)
         self.token_counts = torch.empty(num_experts, dtype=torch.int32, device=topk_idx.device)
         self.expert_offsets = torch.empty(num_experts + 1, dtype=torch.int32,
@@ -48,30 +53,36 @@ class EpRouting:
         prepare(self.layout, topk_idx.contiguous(), self.token_counts, self.handle,
                 self.expert_offsets)
 
+    def layout_for(self, dtype: torch.dtype) -> Layout:
+        """The layout of this routing for payloads of ``dtype``."""
+        if dtype not in self._layouts:
+            self._layouts[dtype] = Layout(*self._dims, dtype=dtype, fill_pads=self.fill_pads)
+        return self._layouts[dtype]
+
 
 class _Dispatch(torch.autograd.Function):
     @staticmethod
     def forward(ctx, tokens, topk_weights, routing: EpRouting):
-        L = routing.layout
+        L = routing.layout_for(tokens.dtype)
         recv = torch.empty(L.cap, L.H, dtype=tokens.dtype, device=tokens.device)
         recv_w = torch.empty(L.cap, dtype=torch.float32, device=tokens.device)
         _dispatch(L, routing.handle, tokens.contiguous(), topk_weights.contiguous(), recv,
                   recv_w)
         ctx.routing = routing
+        ctx.dtype = tokens.dtype
         ctx.set_materialize_grads(False)      # an unused output's gradient stays None
         return recv, recv_w
 
     @staticmethod
     def backward(ctx, g_recv, g_recv_w):
         routing = ctx.routing
-        L = routing.layout
+        L = routing.layout_for(ctx.dtype)
         grad_tokens = None
         grad_w = None
         want_tokens, want_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if want_tokens or want_w:
             if g_recv is None:
-                g_recv = torch.zeros(L.cap, L.H, dtype=torch.bfloat16,
-                                     device=routing.handle.device)
+                g_recv = torch.zeros(L.cap, L.H, dtype=ctx.dtype, device=routing.handle.device)
             grad_tokens = torch.empty(L.T, L.H, dtype=g_recv.dtype, device=g_recv.device)
             grad_w = torch.empty(L.T, L.K, dtype=torch.float32, device=g_recv.device)
             _dispatch_bwd(L, routing.handle, g_recv.contiguous(),
@@ -83,7 +94,7 @@ class _Dispatch(torch.autograd.Function):
 class _Combine(torch.autograd.Function):
     @staticmethod
     def forward(ctx, expert_out, routing: EpRouting):
-        L = routing.layout
+        L = routing.layout_for(expert_out.dtype)
         result = torch.empty(L.T, L.H, dtype=expert_out.dtype, device=expert_out.device)
         _combine(L, routing.handle, expert_out.contiguous(), result)
         ctx.routing = routing
@@ -92,7 +103,7 @@ class _Combine(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g_result):
         routing = ctx.routing
-        L = routing.layout
+        L = routing.layout_for(g_result.dtype)
         grad = torch.empty(L.cap, L.H, dtype=g_result.dtype, device=g_result.device)
         _combine_bwd(L, routing.handle, g_result.contiguous(), grad)
         return grad, None
@@ -101,7 +112,7 @@ class _Combine(torch.autograd.Function):
 class _CombineWeighted(torch.autograd.Function):
     @staticmethod
     def forward(ctx, expert_out, recv_topk_weights, routing: EpRouting):
-        L = routing.layout
+        L = routing.layout_for(expert_out.dtype)
         expert_out = expert_out.contiguous()
         recv_topk_weights = recv_topk_weights.contiguous()
         result = torch.empty(L.T, L.H, dtype=expert_out.dtype, device=expert_out.device)
@@ -114,7 +125,7 @@ class _CombineWeighted(torch.autograd.Function):
     def backward(ctx, g_result):
         expert_out, recv_topk_weights = ctx.saved_tensors
         routing = ctx.routing
-        L = routing.layout
+        L = routing.layout_for(expert_out.dtype)
         want_rows, want_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (want_rows or want_w):
             return None, None, None

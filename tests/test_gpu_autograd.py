@@ -142,3 +142,41 @@ def test_fused_weighted_combine_grads():
     o_gt, o_gwt = oracle.dispatch_bwd(p, host_bf16(recv.grad), recv_w.grad.cpu().numpy())
     assert np.array_equal(host_bf16(x.grad), o_gt)
     assert np.array_equal(w.grad.cpu().numpy().view(np.uint32), o_gwt.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", ["fp16", "fp32"])
+def test_payload_types_through_autograd(dt):
+    # the same routing serves every payload type; forward and token/weight
+    # gradients against the oracle's fp16 / fp32 paths
+    cfg, r, idx, x, w = _setup(name="qwen3", T=300, H=256, seed=4)
+    tdt = {"fp16": torch.float16, "fp32": torch.float32}[dt]
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H, fill_pads=False)
+    xt = x.float().to(tdt).clone().requires_grad_(True)
+    wt = w.clone().requires_grad_(True)
+    recv, recv_w = epa.dispatch(xt, wt, routing)
+    recv.retain_grad()
+    y = epa.combine(recv, routing, recv_w)
+    g = workloads.randn_bf16_torch((cfg.T, cfg.H), 80).float().to(tdt)
+    y.backward(g)
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, routing.layout.cap)
+    live = p.live
+
+    def h(t):
+        t = t.detach()
+        return (t.cpu().numpy() if dt == "fp32"
+                else t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+    def bits(a):
+        return a.view(np.uint32) if a.dtype == np.float32 else a
+
+    o_recv, o_recv_w = oracle.dispatch(p, h(xt), r.topk_weights, dtype=dt, fill_pads=False)
+    pad = p.row_src[:live] < 0
+    assert np.array_equal(bits(h(recv)[:live][~pad]), bits(o_recv[:live][~pad]))
+    # pad rows were never written: combine reads only the rows of valid routes
+    rw = recv_w.detach().cpu().numpy()          # weights are fp32 for every payload type
+    assert np.array_equal(bits(h(y)), bits(oracle.combine_weighted(p, h(recv), rw, dtype=dt)))
+    o_gr, _, _ = oracle.combine_weighted_bwd(p, h(g), h(recv), rw, dtype=dt, fill_pads=False)
+    assert np.array_equal(bits(h(recv.grad)[:live][~pad]), bits(o_gr[:live][~pad]))
+    o_gt, _ = oracle.dispatch_bwd(p, h(recv.grad), None, want_grad_w=False, dtype=dt)
+    assert np.array_equal(bits(h(xt.grad)), bits(o_gt))
+    assert wt.grad is not None and wt.grad.shape == (cfg.T, cfg.K)
