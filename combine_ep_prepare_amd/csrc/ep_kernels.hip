@@ -10,7 +10,9 @@
 //                stable (route-ordered) slot map.
 //   dispatch,    scatter_rows_kernel: the linear map D that copies token row
 //   combine_bwd  t into the received row of each of its valid routes and
-//                zero-fills pad rows. Every source row is read once.
+//                zero-fills pad rows. The routes of a group of tokens are
+//                dealt to the wavefronts of a block; a token slice is read
+//                from memory once and re-read from the caches.
 //   combine,     reduce_rows_kernel: the transpose of D. Each token row is the
 //   dispatch_bwd fp32 sum, k ascending, of the received rows of its valid
 //                routes, rounded once to bf16; the dispatch_bwd weight
@@ -397,12 +399,16 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
 // instruction.
 typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 
-// Work-item width in 1 KiB column blocks, launch shape and cache policy.
-// Rows are streamed through once, so both kernels load and store with the
-// non-temporal hint: it keeps one op's dirty lines from being written back
-// during the next op and measured there.
+// Work-item widths in 1 KiB column blocks, launch shapes and cache policy.
+// Output rows are written once, so both kernels store with the non-temporal
+// hint: it keeps one op's dirty lines from being written back during the next
+// op and measured there. The reduce streams its input rows through once and
+// loads them non-temporally too.
 #ifndef EP_SCATTER_CH
-#define EP_SCATTER_CH 8
+#define EP_SCATTER_CH 2
+#endif
+#ifndef EP_SCATTER_BLOCKS_PER_CU
+#define EP_SCATTER_BLOCKS_PER_CU 32
 #endif
 #ifndef EP_REDUCE_CH
 #define EP_REDUCE_CH 2
@@ -413,8 +419,10 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #ifndef EP_SCATTER_NT_STORE
 #define EP_SCATTER_NT_STORE 1
 #endif
+// The scatter's token slices are loaded with the default (temporal) policy:
+// the wavefronts of a block that share a slice must find it in the caches.
 #ifndef EP_SCATTER_NT_LOAD
-#define EP_SCATTER_NT_LOAD 1
+#define EP_SCATTER_NT_LOAD 0
 #endif
 #ifndef EP_REDUCE_NT_STORE
 #define EP_REDUCE_NT_STORE 1
@@ -556,13 +564,22 @@ struct Payload<EP_DTYPE_FP32> {
 // D: dispatch (token rows + weights) and combine_bwd (gradient rows)
 // ---------------------------------------------------------------------------
 
-// Items: (token, column block) for every token, then (pad row, column block)
-// for every live pad row when pads are filled. A token item reads its CH KiB
-// slice of the row once and stores it to the received row of each valid
-// route. With a compile-time top-k the token's slots are wave-uniform
-// scalars. A bit copy: the payload type only sets the row length d.V.
-template <int KT, int CH>
-__global__ void __launch_bounds__(256)
+// A 512-thread block (kScatterWaves wavefronts) takes one unit: a group of
+// G = 64 / K consecutive tokens (at most 64 routes, one per lane) and one
+// column block of CH KiB. The valid routes of the group are ranked with a
+// ballot and dealt round-robin to the wavefronts; each wavefront copies the
+// block's slice of the token row of each of its routes to the route's
+// received row. The token slices of a dense group are read once from memory
+// and then from the caches by the wavefronts that share them, and each
+// wavefront stores to one row at a time: measured on the MI355X, this writes
+// faster than one wavefront storing a token's slice to all of its rows, and
+// a sparse group still gives every wavefront its share of the work.
+// Pad units follow: kScatterWaves 1 KiB pieces of live pad rows, zeroed, when
+// pads are filled. A bit copy: the payload type only sets the row length.
+constexpr int kScatterWaves = 8;
+
+template <int CH>
+__global__ void __launch_bounds__(kScatterWaves * kWave)
 scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                     const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
                     uint32_t* status, const row16_t* __restrict__ src4,
@@ -573,87 +590,58 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
-  const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
+  const int K = d.K;
+  const int G = kWave / K;                               // tokens per group
   const int64_t V = d.V;
   constexpr int64_t CB = (int64_t)kWave * CH;
-  const int64_t ncb = (V + CB - 1) / CB;
-  const int64_t tok_items = d.T * ncb;
-  const int64_t pad_items = d.fill_pads ? (int64_t)hh.pads_live * ncb : 0;
-  const int64_t n_items = tok_items + pad_items;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int64_t ncb = (V + CB - 1) / CB;                 // column blocks per row
+  const int64_t npc = (V + kWave - 1) / kWave;           // 1 KiB pieces per row
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t tok_units = (d.T + G - 1) / G * ncb;
+  const int64_t pad_pieces = d.fill_pads ? (int64_t)hh.pads_live * npc : 0;
+  const int64_t n_units = tok_units + (pad_pieces + kScatterWaves - 1) / kScatterWaves;
   const bool weights = w != nullptr && dst_w != nullptr;
+  const int64_t routes = d.T * (int64_t)K;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));   // lanes < this one
 
-  for (int64_t it = wave_index(); it < n_items; it += nwaves) {
-    if (it < tok_items) {
-      const int64_t t = it / ncb;
-      const int64_t cb = it - t * ncb;
+  for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+    if (u < tok_units) {
+      const int64_t g = u / ncb;
+      const int64_t cb = u - g * ncb;
+      const int64_t first = g * G * (int64_t)K;          // first route of the group
+      const int64_t s = first + lane;
+      const int32_t sl = (lane < G * K && s < routes) ? slot[s] : -1;
+      const bool valid = sl >= 0;
+      const int rank = __builtin_popcountll(wave_ballot(valid) & below);
+      uint64_t mine = wave_ballot(valid && (rank % kScatterWaves) == wv);
       const int64_t v0 = cb * CB + lane;
-      const row16_t* srow = src4 + t * V;
-      if constexpr (KT > 0) {
-        int32_t sl[KT];
-        bool any = false;
-        static_for<KT>([&](auto k) {
-          sl[k] = slot[t * KT + k];
-          any |= sl[k] >= 0;
-        });
-        if (!any) continue;
-        if (cb == 0 && weights) {
-          int32_t mine = -1;
-          static_for<KT>([&](auto k) {
-            if (lane == k) mine = sl[k];
-          });
-          if (mine >= 0) dst_w[mine] = w[t * KT + lane];
-        }
+      while (mine) {
+        const int l = __ffsll((unsigned long long)mine) - 1;
+        mine &= mine - 1;
+        const int32_t r = __builtin_amdgcn_readlane(sl, l);
+        const int64_t t = (first + l) / K;
         row16_t buf[CH];
         static_for<CH>([&](auto j) {
           const int64_t v = v0 + j * kWave;
-          buf[j] = load_row16<kScatterNtLoad>(srow + (v < V ? v : V - 1));
+          buf[j] = load_row16<kScatterNtLoad>(src4 + t * V + (v < V ? v : V - 1));
         });
         consume(buf);
-        static_for<KT>([&](auto k) {
-          if (sl[k] >= 0) {
-            row16_t* drow = dst4 + (int64_t)sl[k] * V;
-            static_for<CH>([&](auto j) {
-              const int64_t v = v0 + j * kWave;
-              if (v < V) store_row16<kScatterNtStore>(drow + v, buf[j]);
-            });
-          }
-        });
-      } else {
-        const int32_t sl = lane < K ? slot[t * K + lane] : -1;
-        uint64_t vm = wave_ballot(sl >= 0);
-        if (vm == 0) continue;
-        if (cb == 0 && weights && sl >= 0) dst_w[sl] = w[t * K + lane];
-        row16_t buf[CH];
         static_for<CH>([&](auto j) {
           const int64_t v = v0 + j * kWave;
-          buf[j] = load_row16<kScatterNtLoad>(srow + (v < V ? v : V - 1));
+          if (v < V) store_row16<kScatterNtStore>(dst4 + (int64_t)r * V + v, buf[j]);
         });
-        consume(buf);
-        while (vm) {
-          const int k = __ffsll((unsigned long long)vm) - 1;
-          vm &= vm - 1;
-          const int32_t r = __builtin_amdgcn_readlane(sl, k);
-          row16_t* drow = dst4 + (int64_t)r * V;
-          static_for<CH>([&](auto j) {
-            const int64_t v = v0 + j * kWave;
-            if (v < V) store_row16<kScatterNtStore>(drow + v, buf[j]);
-          });
-        }
+        if (cb == 0 && weights && lane == 0) dst_w[r] = w[first + l];
       }
     } else {
-      const int64_t pit = it - tok_items;
-      const int64_t p = pit / ncb;
-      const int64_t cb = pit - p * ncb;
+      const int64_t pi = (u - tok_units) * kScatterWaves + wv;
+      if (pi >= pad_pieces) continue;
+      const int64_t p = pi / npc;
+      const int64_t c = pi - p * npc;
       const int32_t r = pad_rows[p];
-      if (cb == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
-      row16_t* drow = dst4 + (int64_t)r * V;
-      const int64_t v0 = cb * CB + lane;
-      static_for<CH>([&](auto j) {
-        const int64_t v = v0 + j * kWave;
-        if (v < V) store_row16<kScatterNtStore>(drow + v, row16_t{0u, 0u, 0u, 0u});
-      });
+      const int64_t v = c * kWave + lane;
+      if (v < V) store_row16<kScatterNtStore>(dst4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
+      if (c == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
     }
   }
 }
@@ -944,6 +932,7 @@ size_t slots_lds_bytes(int E, int nw) {
 }
 
 constexpr int kScatterCH = EP_SCATTER_CH;
+constexpr int kScatterBlocksPerCU = EP_SCATTER_BLOCKS_PER_CU;
 constexpr int kReduceCH = EP_REDUCE_CH;
 constexpr int kBlock = 256;
 constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
@@ -1015,16 +1004,18 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
                                hipStream_t stream) {
   const int64_t CB = (int64_t)kWave * kScatterCH;
   const int64_t ncb = (d.V + CB - 1) / CB;
-  const int64_t max_items = (d.T + (d.fill_pads ? d.cap : 0)) * ncb;
-  if (max_items == 0) return hipSuccess;
-  const int grid = grid_for(max_items, num_cus);
-  return with_topk(d.K, [&](auto kt) {
-    constexpr int KT = decltype(kt)::value;
-    hipLaunchKernelGGL((scatter_rows_kernel<KT, kScatterCH>), dim3(grid), dim3(kBlock), 0,
-                       stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status,
-                       rows_in(src), w, rows_out(dst), dst_w);
-    return hipGetLastError();
-  });
+  const int64_t npc = (d.V + kWave - 1) / kWave;
+  const int64_t G = kWave / d.K;
+  const int64_t max_units = (d.T + G - 1) / G * ncb +
+                            (d.fill_pads ? (d.cap * npc + kScatterWaves - 1) / kScatterWaves : 0);
+  if (max_units == 0) return hipSuccess;
+  int64_t grid = max_units;
+  const int64_t limit = (int64_t)num_cus * kScatterBlocksPerCU;
+  if (grid > limit) grid = limit;
+  hipLaunchKernelGGL((scatter_rows_kernel<kScatterCH>), dim3((int)grid),
+                     dim3(kScatterWaves * kWave), 0, stream, d, hv.header, hv.slot, hv.pad_rows,
+                     &hv.header->status, rows_in(src), w, rows_out(dst), dst_w);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
