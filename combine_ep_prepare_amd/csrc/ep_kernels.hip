@@ -410,6 +410,9 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #ifndef EP_SCATTER_BLOCKS_PER_CU
 #define EP_SCATTER_BLOCKS_PER_CU 32
 #endif
+#ifndef EP_BWD_BLOCKS_PER_CU
+#define EP_BWD_BLOCKS_PER_CU 16
+#endif
 #ifndef EP_REDUCE_CH
 #define EP_REDUCE_CH 2
 #endif
@@ -814,101 +817,103 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // backward of the weighted combine
 // ---------------------------------------------------------------------------
 
-// One block of kBwdThreads per item: tokens first, then live pad rows (when
-// pads are filled). For token t with valid routes k (received rows r_k,
-// weights w_k):
+// For token t with valid routes k (received rows r_k, weights w_k):
 //   grad_rows[r_k] = payload(fp32(w_k * g_t))
 //   grad_w[r_k]    = sum_h g_t[h] * y[r_k][h]
-// Each lane accumulates its share of every dot product with fused
-// multiply-adds in a fixed element order; the block then reduces the lanes
-// with a fixed butterfly and the wavefronts in index order, so the weight
-// gradient is the same bits on every run. Pad rows get zeros.
-constexpr int kBwdThreads = 256;
+// Units are the token groups of the scatter (64 / K tokens, up to 64 routes)
+// with the valid routes dealt round-robin to the 8 wavefronts of a block; a
+// wavefront handles a whole row per route, kBwdUnroll vectors per lane at a
+// time, so the token's gradient row is read from memory once and then from
+// L2 by the wavefronts of its other routes. Each lane accumulates its share
+// of the dot product with fused multiply-adds over its vectors in ascending
+// order, then the wavefront sums the lanes with a fixed butterfly (lane 0's
+// result is stored): the same bits on every run. Pad pieces (1 KiB of pad
+// rows, and their weight gradients) are zeroed when pads are filled.
+constexpr int kBwdWaves = 8;
+#ifndef EP_BWD_UNROLL
+#define EP_BWD_UNROLL 8
+#endif
+constexpr int kBwdUnroll = EP_BWD_UNROLL;
 
-template <int KT, int DT>
-__global__ void __launch_bounds__(kBwdThreads)
+template <int DT, bool WANT_W>
+__global__ void __launch_bounds__(kBwdWaves * kWave)
 weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
                     const int32_t* __restrict__ slot, const int32_t* __restrict__ pad_rows,
                     uint32_t* status, const row16_t* __restrict__ g4,
                     const row16_t* __restrict__ y4, const float* __restrict__ rw,
                     row16_t* __restrict__ o4, float* __restrict__ grad_w) {
   using P = Payload<DT>;
-  // routes are handled G at a time (all of them at once for a compile-time K)
-  constexpr int G = KT > 0 ? KT : 8;
-  __shared__ float s_part[kBwdThreads / kWave][G];
   const HandleHeader hh = *h;
   if (!handle_matches(hh, d)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
-  const int K = KT > 0 ? KT : d.K;
-  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wv = tid / kWave;
+  const int K = d.K;
+  const int G = kWave / K;
   const int64_t V = d.V;
-  const int64_t n_items = d.T + (d.fill_pads ? (int64_t)hh.pads_live : 0);
-  const bool want_w = grad_w != nullptr;
+  const int64_t npc = (V + kWave - 1) / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t n_groups = (d.T + G - 1) / G;
+  const int64_t pad_pieces = d.fill_pads ? (int64_t)hh.pads_live * npc : 0;
+  const int64_t n_units = n_groups + (pad_pieces + kBwdWaves - 1) / kBwdWaves;
+  const int64_t routes = d.T * (int64_t)K;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 
-  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
-    if (it < d.T) {
-      const int64_t t = it;
-      for (int k0 = 0; k0 < K; k0 += G) {
-        int32_t sl[G];
-        float wk[G];
-        bool any = false;
-        static_for<G>([&](auto k) {
-          sl[k] = k0 + k < K ? slot[t * K + k0 + k] : -1;
-          any |= sl[k] >= 0;
-        });
-        if (!any) continue;                        // uniform over the block
-        static_for<G>([&](auto k) { wk[k] = sl[k] >= 0 ? rw[sl[k]] : 0.0f; });
-        float pd[G];
-        static_for<G>([&](auto k) { pd[k] = 0.0f; });
-        for (int64_t v = tid; v < V; v += kBwdThreads) {
-          const row16_t gv = load_row16<kReduceNtLoad>(g4 + t * V + v);
-          row16_t yv[G];
-          if (want_w) {
-            static_for<G>([&](auto k) {
-              if (sl[k] >= 0) yv[k] = load_row16<kReduceNtLoad>(y4 + (int64_t)sl[k] * V + v);
-            });
-          }
-          static_for<G>([&](auto k) {
-            if (sl[k] >= 0) {
+  for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+    if (u < n_groups) {
+      const int64_t first = u * G * (int64_t)K;
+      const int64_t s = first + lane;
+      const int32_t sl = (lane < G * K && s < routes) ? slot[s] : -1;
+      const bool valid = sl >= 0;
+      const int rank = __builtin_popcountll(wave_ballot(valid) & below);
+      uint64_t mine = wave_ballot(valid && (rank % kBwdWaves) == wv);
+      while (mine) {
+        const int l = __ffsll((unsigned long long)mine) - 1;
+        mine &= mine - 1;
+        const int32_t r = __builtin_amdgcn_readlane(sl, l);
+        const int64_t t = (first + l) / K;
+        const float wk = rw[r];
+        const row16_t* grow = g4 + t * V;
+        const row16_t* yrow = y4 + (int64_t)r * V;
+        row16_t* orow = o4 + (int64_t)r * V;
+        float pd = 0.0f;
+        for (int64_t vb = lane; vb < V; vb += (int64_t)kWave * kBwdUnroll) {
+          row16_t gv[kBwdUnroll], yv[kBwdUnroll];
+          static_for<kBwdUnroll>([&](auto j) {
+            const int64_t v = vb + j * kWave;
+            const int64_t vc = v < V ? v : V - 1;
+            gv[j] = load_row16<false>(grow + vc);
+            if constexpr (WANT_W) yv[j] = load_row16<kReduceNtLoad>(yrow + vc);
+          });
+          static_for<kBwdUnroll>([&](auto j) {
+            const int64_t v = vb + j * kWave;
+            if (v < V) {
               float prod[P::N];
               static_for<P::N>([&](auto q) {
                 constexpr int i = q;
-                const float gi = P::template get<i>(gv);
-                prod[i] = wk[k] * gi;
-                if (want_w) pd[k] = __builtin_fmaf(gi, P::template get<i>(yv[k]), pd[k]);
+                const float gi = P::template get<i>(gv[j]);
+                prod[i] = wk * gi;
+                if constexpr (WANT_W) pd = __builtin_fmaf(gi, P::template get<i>(yv[j]), pd);
               });
-              store_row16<kScatterNtStore>(o4 + (int64_t)sl[k] * V + v, P::pack(prod));
+              store_row16<kScatterNtStore>(orow + v, P::pack(prod));
             }
           });
         }
-        if (want_w) {
-          static_for<G>([&](auto k) {
-            float x = pd[k];
-            for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-            if (lane == 0) s_part[wv][k] = x;
-          });
-          __syncthreads();
-          if (tid < G) {
-            float tot = 0.0f;
-            int32_t r = -1;
-            static_for<G>([&](auto k) {
-              if (tid == k) r = sl[k];
-            });
-            for (int q = 0; q < kBwdThreads / kWave; ++q) tot += s_part[q][tid];
-            if (r >= 0) grad_w[r] = tot;
-          }
-          __syncthreads();
+        if constexpr (WANT_W) {
+          for (int off = kWave / 2; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
+          if (lane == 0) grad_w[r] = pd;
         }
       }
     } else {
-      const int32_t r = pad_rows[it - d.T];
-      for (int64_t v = tid; v < V; v += kBwdThreads)
-        store_row16<kScatterNtStore>(o4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
-      if (want_w && tid == 0) grad_w[r] = 0.0f;
+      const int64_t pi = (u - n_groups) * kBwdWaves + wv;
+      if (pi >= pad_pieces) continue;
+      const int64_t p = pi / npc;
+      const int64_t c = pi - p * npc;
+      const int32_t r = pad_rows[p];
+      const int64_t v = c * kWave + lane;
+      if (v < V) store_row16<kScatterNtStore>(o4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
+      if (WANT_W && c == 0 && lane == 0) grad_w[r] = 0.0f;
     }
   }
 }
@@ -1047,20 +1052,28 @@ hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* s
 hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* g,
                                const void* y, const float* rw, void* grad_rows, float* grad_w,
                                int num_cus, hipStream_t stream) {
-  const int64_t max_items = d.T + (d.fill_pads ? d.cap : 0);
-  if (max_items == 0) return hipSuccess;
-  int64_t grid = max_items;
-  const int64_t limit = (int64_t)num_cus * 32;
+  const int64_t npc = (d.V + kWave - 1) / kWave;
+  const int64_t G = kWave / d.K;
+  const int64_t max_units = (d.T + G - 1) / G +
+                            (d.fill_pads ? (d.cap * npc + kBwdWaves - 1) / kBwdWaves : 0);
+  if (max_units == 0) return hipSuccess;
+  int64_t grid = max_units;
+  const int64_t limit = (int64_t)num_cus * EP_BWD_BLOCKS_PER_CU;
   if (grid > limit) grid = limit;
   return with_dtype(d.dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
-    return with_topk(d.K, [&](auto kt) {
-      constexpr int KT = decltype(kt)::value;
-      hipLaunchKernelGGL((weighted_bwd_kernel<KT, DT>), dim3((int)grid), dim3(kBwdThreads), 0,
-                         stream, d, hv.header, hv.slot, hv.pad_rows, &hv.header->status,
-                         rows_in(g), rows_in(y), rw, rows_out(grad_rows), grad_w);
-      return hipGetLastError();
-    });
+    if (grad_w != nullptr) {
+      hipLaunchKernelGGL((weighted_bwd_kernel<DT, true>), dim3((int)grid),
+                         dim3(kBwdWaves * kWave), 0, stream, d, hv.header, hv.slot, hv.pad_rows,
+                         &hv.header->status, rows_in(g), rows_in(y), rw, rows_out(grad_rows),
+                         grad_w);
+    } else {
+      hipLaunchKernelGGL((weighted_bwd_kernel<DT, false>), dim3((int)grid),
+                         dim3(kBwdWaves * kWave), 0, stream, d, hv.header, hv.slot, hv.pad_rows,
+                         &hv.header->status, rows_in(g), nullptr, rw, rows_out(grad_rows),
+                         nullptr);
+    }
+    return hipGetLastError();
   });
 }
 

@@ -89,9 +89,11 @@ def payload(rng, shape, dt, specials=False):
 
 
 def gamma(H, dt):
+    # one wavefront per row: each lane chains n_per_vec * ceil(V/64) fused
+    # multiply-adds, then 6 butterfly adds
     n_per_vec = 4 if dt == "fp32" else 8
     V = H * (4 if dt == "fp32" else 2) // 16
-    n = n_per_vec * math.ceil(V / 256) + 9
+    n = n_per_vec * math.ceil(V / 64) + 6
     u = 2.0 ** -24
     return n * u / (1 - n * u)
 

@@ -3,11 +3,12 @@
 Forward and the row gradient are bit-exact against the oracle. The weight
 gradient is a dot product over H whose order the method does not fix; it is
 compared with the oracle's double-precision dot within the summation error
-bound of the kernel's fixed order: each lane chains 8 * ceil(H/8/256) fused
-multiply-adds, then 6 butterfly adds across the wavefront and 3 adds across
-the 4 wavefronts, so |got - exact| <= gamma_n * sum_h |g_h y_h| with
-n = 8 * ceil(H/2048) + 9 and gamma_n = n u / (1 - n u), u = 2^-24. It must
-also be bit-identical from run to run.
+bound of the kernel's fixed order: one wavefront takes the whole row, each
+lane chains 8 * ceil(V/64) fused multiply-adds over its 16-byte vectors
+(V = H/8 of them per row), then 6 butterfly adds combine the 64 lanes, so
+|got - exact| <= gamma_n * sum_h |g_h y_h| with n = 8 * ceil(V/64) + 6 and
+gamma_n = n u / (1 - n u), u = 2^-24. It must also be bit-identical from run
+to run.
 """
 import math
 import zlib
@@ -33,7 +34,7 @@ def _gpu():
 
 
 def _gamma(H):
-    n = 8 * math.ceil(H / 8 / 256) + 9
+    n = 8 * math.ceil(H / 8 / 64) + 6
     u = 2.0 ** -24
     return n * u / (1 - n * u)
 
