@@ -200,6 +200,9 @@ def _need(t: Optional[torch.Tensor], name: str, dtype, shape=None, allow_none=Fa
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library runs on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
