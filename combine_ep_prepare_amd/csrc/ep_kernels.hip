@@ -414,7 +414,7 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #define EP_BWD_BLOCKS_PER_CU 16
 #endif
 #ifndef EP_REDUCE_CH
-#define EP_REDUCE_CH 2
+#define EP_REDUCE_CH 1
 #endif
 #ifndef EP_BLOCKS_PER_CU
 #define EP_BLOCKS_PER_CU 64
