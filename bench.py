@@ -70,11 +70,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments, trailing blanks and empty lines."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments ignored): profiles taken on
+    other code are not used."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

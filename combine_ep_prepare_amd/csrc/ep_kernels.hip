@@ -1,8 +1,9 @@
 // ep_kernels.hip -- gfx950 (CDNA4) kernels for MoE expert-parallel routing.
 //
-// Three kernel families serve the five ops of "Expert Parallelism: common C
+// Four kernel families serve the five ops of "Expert Parallelism: common C
 // API + NCCL EP backend" (section "Per-step (allocation-free, CUDA-graph
-// capturable)") at one GPU's share:
+// capturable)") at one GPU's share, and the fused weighted combine with its
+// backward:
 //
 //   prepare      prepare_hist_kernel + prepare_slots_kernel: a per-wavefront
 //                expert histogram privatised in LDS, a block-wide wavefront-
@@ -15,15 +16,19 @@
 //                from memory once and re-read from the caches.
 //   combine,     reduce_rows_kernel: the transpose of D. Each token row is the
 //   dispatch_bwd fp32 sum, k ascending, of the received rows of its valid
-//                routes, rounded once to bf16; the dispatch_bwd weight
-//                gradient is gathered in the same pass.
+//                routes, rounded once to the payload type; the dispatch_bwd
+//                weight gradient is gathered in the same pass. With the
+//                received weights it is the fused weighted combine.
+//   weighted     weighted_bwd_kernel: the weighted combine's row gradient
+//   backward     (a scatter of w * g) and weight gradient (a dot product per
+//                route, in a fixed order).
 //
 // None of this is a dense contraction, so no MFMA: every kernel is bound by
 // HBM traffic (or, for prepare, by latency). Rows move as 16-byte vectors,
 // 64 lanes x 16 B = 1 KiB per wavefront instruction, fully coalesced.
-// Work is split into (row, column-block) items handed out to wavefronts in a
-// grid-stride loop whose bound is read on the device, so no host sync is ever
-// needed and every launch is graph-capturable.
+// Work is split into units handed out in a grid-stride loop whose bound is
+// read on the device, so no host sync is ever needed and every launch is
+// graph-capturable.
 
 #include <hip/hip_runtime.h>
 

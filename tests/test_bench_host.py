@@ -65,3 +65,11 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    commented = "/* header\n   text */\nint f(int x) {\n\n  return x + 1;  // plus one\n}\n"
+    changed = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench._code_only(code) == bench._code_only(commented)
+    assert bench._code_only(code) != bench._code_only(changed)
