@@ -447,6 +447,8 @@ def main():
             per_op_ms[op].append(ev[j].elapsed_time(ev[j + 1]))
     avg = {op: float(np.mean(v)) for op, v in per_op_ms.items()}
     med = {op: float(np.median(v)) for op, v in per_op_ms.items()}
+    p10 = {op: float(np.percentile(v, 10)) for op, v in per_op_ms.items()}
+    p90 = {op: float(np.percentile(v, 90)) for op, v in per_op_ms.items()}
 
     # Ops outside the step, timed one at a time over the same number of
     # launches after the same warmup.
@@ -496,6 +498,8 @@ def main():
             v = [a.elapsed_time(b) for a, b in evs]
             avg[op] = float(np.mean(v))
             med[op] = float(np.median(v))
+            p10[op] = float(np.percentile(v, 10))
+            p90[op] = float(np.percentile(v, 90))
             nb = algorithmic_bytes(T, K, E, H, r.topk_idx, counts_np, offsets_np,
                                    esize=ESIZE[dt], fill_pads=fill)
             extra[op] = nb[base_op(op)]
@@ -561,11 +565,14 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / pair_s, 1),
         "ops": {op: {"avg_us": round(avg[op] * 1e3, 2), "median_us": round(med[op] * 1e3, 2),
+                     "p10_us": round(p10[op] * 1e3, 2), "p90_us": round(p90[op] * 1e3, 2),
                      "algorithmic_bytes": nbytes[op],
                      "GBps": round(gbs(op, nbytes[op]), 1) if op != "prepare" else None}
                 for op in STEP_OPS},
         "ops_outside_step": {op: {"avg_us": round(avg[op] * 1e3, 2),
                                   "median_us": round(med[op] * 1e3, 2),
+                                  "p10_us": round(p10[op] * 1e3, 2),
+                                  "p90_us": round(p90[op] * 1e3, 2),
                                   "algorithmic_bytes": nb,
                                   "GBps": round(gbs(op, nb), 1)}
                              for op, nb in extra.items()},
