@@ -193,3 +193,32 @@ def test_binding_rejects_bad_tensors_on_cpu():
         ep.prepare(L, torch.zeros((16, 2), dtype=torch.int32), torch.zeros(4, dtype=torch.int32), h)
     with pytest.raises(ValueError):   # not a GPU tensor
         ep.prepare(L, torch.zeros((16, 2), dtype=torch.int64), torch.zeros(4, dtype=torch.int32), h)
+
+
+def test_weighted_entry_points_error_paths():
+    # ep_combine_weighted(layout, handle, bytes, expert_out, recv_w, result, stream)
+    # ep_combine_weighted_bwd(layout, handle, bytes, grad, expert_out, recv_w,
+    #                         grad_expert_out, grad_recv_w, stream)
+    cw, cwb = ep.lib.ep_combine_weighted, ep.lib.ep_combine_weighted_bwd
+    L = lay()
+    n = ep.handle_mem_size(L)
+    bad = lay(K=0)
+    assert cw(C.byref(bad), P, 1 << 30, P, P2, P2, None) == ep.EP_ERR_SHAPE
+    assert cwb(C.byref(bad), P, 1 << 30, P, P2, P2, P2, P2, None) == ep.EP_ERR_SHAPE
+    assert cw(None, P, n, P, P2, P2, None) == ep.EP_ERR_NULL
+    assert cw(C.byref(L), None, n, P, P2, P2, None) == ep.EP_ERR_NULL
+    assert cw(C.byref(L), P, n, None, P2, P2, None) == ep.EP_ERR_NULL      # rows
+    assert cw(C.byref(L), P, n, P, None, P2, None) == ep.EP_ERR_NULL      # weights
+    assert cw(C.byref(L), P, n, P, P2, None, None) == ep.EP_ERR_NULL      # result
+    assert cw(C.byref(L), P, n - 1, P, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
+    assert cw(C.byref(L), P, n, MIS, P2, P2, None) == ep.EP_ERR_ALIGN
+    assert cw(C.byref(L), P, n, P, P2, MIS, None) == ep.EP_ERR_ALIGN
+    assert cwb(C.byref(L), P, n, None, P2, P2, P2, P2, None) == ep.EP_ERR_NULL   # grad
+    assert cwb(C.byref(L), P, n, P, P2, None, P2, P2, None) == ep.EP_ERR_NULL   # weights
+    assert cwb(C.byref(L), P, n, P, P2, P2, None, P2, None) == ep.EP_ERR_NULL   # grad rows
+    # a weight gradient needs the expert rows
+    assert cwb(C.byref(L), P, n, P, None, P2, P2, P2, None) == ep.EP_ERR_NULL
+    assert cwb(C.byref(L), P, n - 1, P, P2, P2, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
+    assert cwb(C.byref(L), P, n, MIS, P2, P2, P2, P2, None) == ep.EP_ERR_ALIGN
+    assert cwb(C.byref(L), P, n, P, MIS, P2, P2, P2, None) == ep.EP_ERR_ALIGN
+    assert cwb(C.byref(L), P, n, P, P2, P2, MIS, P2, None) == ep.EP_ERR_ALIGN
