@@ -184,7 +184,8 @@ def test_payload_type_parity(dt, name, T, H):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("name,T,H", [("dsv3", 300, 1024), ("qwen3", 500, 512)])
+@pytest.mark.parametrize("name,T,H", [("dsv3", 300, 1024), ("qwen3", 500, 512),
+                                     ("dsv3", 200, 4104)])
 def test_no_pad_fill_parity(dt, name, T, H):
     c = workloads.scaled(workloads.CONFIGS[name], T=T, H=H)
     r = workloads.make_routing(c)
@@ -196,7 +197,8 @@ def test_no_pad_fill_parity(dt, name, T, H):
 @pytest.mark.parametrize("dt", ["fp16", "fp32"])
 @pytest.mark.parametrize("label,T,K,E,A,H,shrink", [
     ("generic_k3", 300, 3, 16, 4, 64, False), ("generic_k12", 150, 12, 40, 8, 136, False),
-    ("overflow", 400, 8, 32, 16, 72, True), ("ragged_cols", 257, 2, 5, 3, 1032, False)])
+    ("overflow", 400, 8, 32, 16, 72, True), ("ragged_cols", 257, 2, 5, 3, 1032, False),
+    ("ragged_long_rows", 157, 6, 9, 5, 2056, False)])
 def test_payload_type_edge_cases(dt, label, T, K, E, A, H, shrink):
     rng = np.random.default_rng(zlib.crc32(f"{label}{dt}".encode()))
     idx = np.argsort(rng.random((T, max(E, K))), axis=1)[:, :K]

@@ -120,6 +120,9 @@ EDGE = [
     ("big_alignment", 100, 2, 4, 1024, 64, "uniform"),
     ("repeated_ids", 500, 6, 5, 8, 64, "repeats"),
     ("mixed_masks", 1200, 8, 32, 128, 64, "half_masked"),
+    # rows of 8 KiB take the interleaved unit order, longer rows the plain one
+    ("h4096_interleaved_edge", 300, 8, 64, 16, 4096, "half_masked"),
+    ("h4104_plain_ragged", 300, 8, 64, 16, 4104, "half_masked"),
 ]
 
 
