@@ -21,7 +21,7 @@ gradient is then zero), the case the pages' review flagged (section
 Rows at or past the live total (``routing.expert_offsets[E]``) of the
 receive buffer are never written, and neither are the same rows of the
 gradient that ``combine`` passes back: both hold unspecified values. Pad rows
-below the total are zero. An expert function that treats rows independently,
+below the total are zero (with ``fill_pads=False`` they are unwritten too). An expert function that treats rows independently,
 or works on expert segments taken from ``expert_offsets``, is unaffected; one
 that mixes rows (a parameter shared across the whole buffer, a reduction over
 it) must slice the buffer to its live rows first, or its parameter gradients
