@@ -77,9 +77,10 @@ Dims dims_of(const ep_layout_t* L, int32_t num_units) {
   return d;
 }
 
-// Common checks of the payload ops; fills dims, view and CU count.
+// Common host-side checks of the payload ops; fills the dims and the handle
+// view. The device check comes after each op's own pointer checks.
 ep_status_t payload_common(const ep_layout_t* L, const void* handle_mem, size_t handle_bytes,
-                           Dims* d, HandleView* hv, int* num_cus) {
+                           Dims* d, HandleView* hv) {
   ep_status_t st = check_layout(L);
   if (st != EP_OK) return st;
   if (!handle_mem) return EP_ERR_NULL;
@@ -89,7 +90,6 @@ ep_status_t payload_common(const ep_layout_t* L, const void* handle_mem, size_t 
   if (!aligned16(handle_mem)) return EP_ERR_ALIGN;
   *d = dims_of(L, hl.num_units);
   *hv = handle_view(const_cast<void*>(handle_mem), hl);
-  (void)num_cus;
   return EP_OK;
 }
 
@@ -157,7 +157,7 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   // A buffer with no element may be NULL: tokens/topk_weights when T == 0,
   // recv_tokens/recv_topk_weights when recv_capacity == 0.
@@ -180,7 +180,7 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   if (d.T > 0 && (!result || (d.cap > 0 && !expert_out))) return EP_ERR_NULL;
   if (!aligned16(expert_out) || !aligned16(result)) return EP_ERR_ALIGN;
@@ -199,7 +199,7 @@ ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   if (d.T > 0 && (!grad_tokens || (d.cap > 0 && !grad))) return EP_ERR_NULL;
   if (!aligned16(grad) || !aligned16(grad_tokens)) return EP_ERR_ALIGN;
@@ -217,7 +217,7 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   if (d.cap > 0 && (!grad_expert_out || (d.T > 0 && !grad))) return EP_ERR_NULL;
   if (!aligned16(grad) || !aligned16(grad_expert_out)) return EP_ERR_ALIGN;
@@ -236,7 +236,7 @@ ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_me
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   if (d.T > 0 && (!result || (d.cap > 0 && (!expert_out || !recv_topk_weights))))
     return EP_ERR_NULL;
@@ -260,7 +260,7 @@ ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handl
   Dims d;
   HandleView hv;
   int num_cus = 0;
-  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv, &num_cus);
+  ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
   if (d.cap > 0) {
     if (!grad_expert_out || !recv_topk_weights) return EP_ERR_NULL;
