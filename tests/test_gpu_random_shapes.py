@@ -60,3 +60,27 @@ def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind):
     worst = T * K + E * (A - 1)
     cap = {"worst": worst, "tight": worst // 2, "zero": 0}[cap_kind]
     run_case(f"random{i}", idx, E, A, H, cap, dt, fill, rng)
+
+
+def _long_row_cases(n=8):
+    # rows of 8 to 19 KiB: the scatter's plain unit order and 16-per-CU grid
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(n):
+        K = int(rng.choice([1, 2, 5, 8, 13, 16]))
+        E = int(rng.integers(1, 65))
+        A = int(rng.choice([1, 4, 16]))
+        H = int(8 * rng.integers(513, 1201))
+        T = int(rng.integers(0, 201))
+        dt = str(rng.choice(["bf16", "fp16", "fp32"]))
+        fill = bool(rng.random() < 0.7)
+        kind = str(rng.choice(["distinct", "repeats", "masked", "bad"]))
+        cap_kind = str(rng.choice(["worst", "worst", "tight"]))
+        out.append((100 + i, T, K, E, A, H, dt, fill, kind, cap_kind))
+    return out
+
+
+@pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _long_row_cases(),
+                         ids=lambda v: str(v) if not isinstance(v, str) else v)
+def test_random_long_rows(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind)
