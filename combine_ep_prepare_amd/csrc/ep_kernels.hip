@@ -625,6 +625,13 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
   const bool weights = w != nullptr && dst_w != nullptr;
   const int64_t routes = d.T * (int64_t)K;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));   // lanes < this one
+  const int tok_of_lane = lane / K;                      // token of lane l within a group
+  // Unit and piece indices fit 32 bits whenever the buffers fit in memory;
+  // the 64-bit divisions stay for a launch where they would not.
+  const bool small = n_units < ((int64_t)1 << 31) && pad_pieces < ((int64_t)1 << 31);
+  auto udiv = [&](int64_t x, int64_t y) -> int64_t {
+    return small ? (int64_t)((uint32_t)x / (uint32_t)y) : x / y;
+  };
 
   for (int64_t i = blockIdx.x; i < n_units; i += gridDim.x) {
     int64_t u = i;
@@ -634,7 +641,7 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       u = c1 > c0 ? c0 : tok_units + (i - c1);
     }
     if (u < tok_units) {
-      const int64_t g = u / ncb;
+      const int64_t g = udiv(u, ncb);
       const int64_t cb = u - g * ncb;
       const int64_t first = g * G * (int64_t)K;          // first route of the group
       const int64_t s = first + lane;
@@ -647,7 +654,7 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
         const int l = __ffsll((unsigned long long)mine) - 1;
         mine &= mine - 1;
         const int32_t r = __builtin_amdgcn_readlane(sl, l);
-        const int64_t t = (first + l) / K;
+        const int64_t t = g * G + __builtin_amdgcn_readlane(tok_of_lane, l);
         row16_t buf[CH];
         static_for<CH>([&](auto j) {
           const int64_t v = v0 + j * kWave;
@@ -663,7 +670,7 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
     } else {
       const int64_t pi = (u - tok_units) * kScatterWaves + wv;
       if (pi >= pad_pieces) continue;
-      const int64_t p = pi / npc;
+      const int64_t p = udiv(pi, npc);
       const int64_t c = pi - p * npc;
       const int32_t r = pad_rows[p];
       const int64_t v = c * kWave + lane;
