@@ -8,7 +8,8 @@
 //   prepare      prepare_hist_kernel + prepare_slots_kernel: a per-wavefront
 //                expert histogram privatised in LDS, a block-wide wavefront-
 //                shuffle exclusive scan of the aligned segment lengths, and a
-//                stable (route-ordered) slot map.
+//                stable (route-ordered) slot map; prepare_fused_kernel does
+//                the same in one block and one launch for small routings.
 //   dispatch,    scatter_rows_kernel: the linear map D that copies token row
 //   combine_bwd  t into the received row of each of its valid routes and
 //                zero-fills pad rows. The routes of a group of tokens are
@@ -385,6 +386,207 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   //    the live ones form a prefix). One wavefront per expert, spread over
   //    every wavefront of the grid; its lanes cover the expert's pad rows.
   for (int e = blockIdx.x * nw + w; e < E; e += gridDim.x * nw) {
+    const int64_t lo = (int64_t)s_offs[e] + s_counts[e];
+    const int64_t hi_full = s_offs[e + 1];
+    const int64_t hi = hi_full < d.cap ? hi_full : d.cap;
+    const int32_t p0 = s_padoff[e];
+    for (int64_t r = lo + lane; r < hi; r += kWave) {
+      hv.row_src[r] = -1;
+      hv.pad_rows[p0 + (r - lo)] = (int32_t)r;
+    }
+  }
+}
+
+// Single-block prepare for small routings, where the two-kernel form is bound
+// by its launches. The kFusedWaves wavefronts of one block each take a
+// contiguous run of at most kPrepRounds 64-route rounds (so wavefront order is
+// route order), load their ids once and count them into a wavefront-private
+// LDS row; the block turns the rows into counts, aligned offsets and
+// per-wavefront cursors; each wavefront then hands out rows from its ids
+// exactly as the two-kernel form does. One launch, and the histograms stay in
+// LDS. Measured on the MI355X it beats the two launches up to a few thousand
+// routes; one CU is too slow beyond.
+constexpr int kFusedWaves = 16;
+
+__global__ void __launch_bounds__(kFusedWaves * kWave)
+prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
+                     int32_t* __restrict__ user_counts, int32_t* __restrict__ user_offsets,
+                     int nbits) {
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t s_wave_tot[2][kFusedWaves];
+  __shared__ int32_t s_pads_live;
+  __shared__ int32_t s_bad;
+  constexpr int nthr = kFusedWaves * kWave;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int E = d.E;
+  const int32_t A = d.A;
+  int32_t* s_cur = lds;                          // [kFusedWaves][E]: counts, then cursors
+  int32_t* s_counts = s_cur + kFusedWaves * E;   // [E]
+  int32_t* s_offs = s_counts + E;                // [E+1]
+  int32_t* s_padoff = s_offs + E + 1;            // [E+1]
+
+  for (int i = tid; i < kFusedWaves * E; i += nthr) s_cur[i] = 0;
+  if (tid == 0) {
+    s_bad = 0;
+    s_pads_live = 0;
+  }
+  __syncthreads();
+
+  // 1. Per-wavefront histograms of this wavefront's rounds; the ids stay in
+  //    registers for step 5.
+  const int64_t routes = d.T * d.K;
+  const int32_t n_rounds = (int32_t)((routes + kWave - 1) / kWave);
+  const int32_t per_wave = (n_rounds + kFusedWaves - 1) / kFusedWaves;   // <= kPrepRounds
+  const int32_t ra = min(n_rounds, w * per_wave);
+  const int32_t nr = min(n_rounds, ra + per_wave) - ra;
+  const int64_t base = (int64_t)ra * kWave;
+  int32_t* hist = s_cur + w * E;
+  int64_t ids[kPrepRounds];
+  static_for<kPrepRounds>([&](auto i) {
+    const int64_t s = base + i * kWave + lane;
+    ids[i] = (i < nr && s < routes) ? topk_idx[s] : -1;
+  });
+  bool bad_any = false;
+  static_for<kPrepRounds>([&](auto i) {
+    if (i < nr) {
+      const int64_t id = ids[i];
+      const bool valid = id >= 0 && id < E;
+      const bool bad = !valid && id != -1;
+      bad_any |= wave_ballot(bad) != 0;
+      const uint32_t key = valid ? (uint32_t)id : 0u;
+      const uint64_t peers = match_peers(key, valid, nbits);
+      if (valid && lane == __ffsll((unsigned long long)peers) - 1)
+        atomicAdd(&hist[key], (int32_t)__popcll(peers));
+    }
+  });
+  if (bad_any && lane == 0) s_bad = 1;
+  __syncthreads();
+
+  // 2. Counts, and each row turned into the routes of earlier wavefronts.
+  for (int e = tid; e < E; e += nthr) {
+    int32_t run = 0;
+    for (int q = 0; q < kFusedWaves; ++q) {
+      const int32_t c = s_cur[q * E + e];
+      s_cur[q * E + e] = run;
+      run += c;
+    }
+    s_counts[e] = run;
+  }
+  __syncthreads();
+
+  // 3. Exclusive scans over experts of the aligned segment lengths and of the
+  //    pad rows (a contiguous chunk per thread, a shuffle scan inside each
+  //    wavefront, then the wavefront totals), and the live pad rows.
+  const int per = (E + nthr - 1) / nthr;
+  const int b0 = tid * per;
+  int32_t loc_a = 0, loc_p = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < E) {
+      const int32_t c = s_counts[e];
+      const int32_t padded = (c + A - 1) / A * A;
+      loc_a += padded;
+      loc_p += padded - c;
+    }
+  }
+  int32_t inc_a = loc_a, inc_p = loc_p;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t ta = __shfl_up(inc_a, off);
+    const int32_t tp = __shfl_up(inc_p, off);
+    if (lane >= off) {
+      inc_a += ta;
+      inc_p += tp;
+    }
+  }
+  if (lane == kWave - 1) {
+    s_wave_tot[0][w] = inc_a;
+    s_wave_tot[1][w] = inc_p;
+  }
+  __syncthreads();
+  int32_t ex_a = inc_a - loc_a, ex_p = inc_p - loc_p;
+  for (int q = 0; q < w; ++q) {
+    ex_a += s_wave_tot[0][q];
+    ex_p += s_wave_tot[1][q];
+  }
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < E) {
+      const int32_t c = s_counts[e];
+      const int32_t padded = (c + A - 1) / A * A;
+      s_offs[e] = ex_a;
+      s_padoff[e] = ex_p;
+      if ((int64_t)ex_a <= d.cap && d.cap < (int64_t)ex_a + padded) {
+        const int64_t first_pad = (int64_t)ex_a + c;
+        s_pads_live = ex_p + (int32_t)(d.cap > first_pad ? d.cap - first_pad : 0);
+      }
+      ex_a += padded;
+      ex_p += padded - c;
+    }
+  }
+  if (tid == nthr - 1) {
+    s_offs[E] = ex_a;
+    s_padoff[E] = ex_p;
+    if ((int64_t)ex_a <= d.cap) s_pads_live = ex_p;
+  }
+  __syncthreads();
+
+  // 4. Publish counts, offsets and the header; cursors = segment start +
+  //    routes of earlier wavefronts.
+  for (int e = tid; e <= E; e += nthr) {
+    hv.offsets[e] = s_offs[e];
+    hv.pad_offsets[e] = s_padoff[e];
+    if (user_offsets) user_offsets[e] = s_offs[e];
+    if (e < E) {
+      hv.counts[e] = s_counts[e];
+      user_counts[e] = s_counts[e];
+    }
+  }
+  if (tid == 0) {
+    HandleHeader* h = hv.header;
+    const int32_t total = s_offs[E];
+    h->status = (s_bad ? EP_STATUS_BAD_EXPERT : 0u) |
+                ((int64_t)total > d.cap ? EP_STATUS_OVERFLOW : 0u);
+    h->num_tokens = d.T;
+    h->topk = d.K;
+    h->num_experts = d.E;
+    h->alignment = d.A;
+    h->num_units = d.num_units;
+    h->recv_capacity = d.cap;
+    h->total = total;
+    h->pads_live = s_pads_live;
+    h->magic = kHandleMagic;
+  }
+  for (int i = tid; i < kFusedWaves * E; i += nthr) s_cur[i] += s_offs[i % E];
+  __syncthreads();
+
+  // 5. Stable slots, round by round in route order: the lowest lane of each
+  //    distinct id claims popc(peers) rows from the wavefront's cursor; every
+  //    peer adds its rank among earlier lanes.
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
+  static_for<kPrepRounds>([&](auto i) {
+    if (i < nr) {
+      const int64_t id = ids[i];
+      const bool valid = id >= 0 && id < E;
+      const uint32_t key = valid ? (uint32_t)id : 0u;
+      const uint64_t peers = match_peers(key, valid, nbits);
+      const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+      int32_t first = 0;
+      if (valid && lane == leader) first = atomicAdd(&hist[key], (int32_t)__popcll(peers));
+      first = __shfl(first, leader);
+      const int64_t s = base + i * kWave + lane;
+      if (s < routes) {
+        const int64_t row = (int64_t)first + __popcll(peers & lanes_below);
+        const bool keep = valid && row < d.cap;
+        hv.slot[s] = keep ? (int32_t)row : -1;
+        if (keep) hv.row_src[row] = (int32_t)s;
+      }
+    }
+  });
+
+  // 6. Pad rows: row_src = -1 and the ascending list of live pad rows.
+  for (int e = w; e < E; e += kFusedWaves) {
     const int64_t lo = (int64_t)s_offs[e] + s_counts[e];
     const int64_t hi_full = s_offs[e + 1];
     const int64_t hi = hi_full < d.cap ? hi_full : d.cap;
@@ -962,6 +1164,13 @@ int key_bits(int E) {
 }
 
 constexpr size_t kLdsBudget = 65536;
+// Routings of at most this many routes take the single-block prepare.
+#ifndef EP_PREP_FUSED_MAX_ROUTES
+#define EP_PREP_FUSED_MAX_ROUTES 4096
+#endif
+constexpr int64_t kPrepFusedMaxRoutes = EP_PREP_FUSED_MAX_ROUTES;
+static_assert(kPrepFusedMaxRoutes <= (int64_t)kFusedWaves * kPrepRounds * kWave,
+              "the one-block prepare holds at most kPrepRounds rounds per wavefront");
 
 size_t slots_lds_bytes(int E, int nw) {
   return sizeof(int32_t) * (size_t)(4 * E + 2 + 2 * kWave * nw + nw * E);
@@ -1018,6 +1227,12 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   (void)num_cus;
   const int nbits = key_bits(d.E);
   const int U = d.num_units;
+  const size_t fused_lds = sizeof(int32_t) * ((size_t)(kFusedWaves + 3) * d.E + 2);
+  if (d.T * (int64_t)d.K <= (int64_t)kPrepFusedMaxRoutes && fused_lds <= kLdsBudget) {
+    hipLaunchKernelGGL(prepare_fused_kernel, dim3(1), dim3(kFusedWaves * kWave), fused_lds,
+                       stream, d, hv, topk_idx, user_counts, user_offsets, nbits);
+    return hipGetLastError();
+  }
   if (U > 0) {
     int nw1 = 8;
     while (nw1 > 1 && sizeof(int32_t) * (size_t)nw1 * d.E > kLdsBudget) nw1 /= 2;

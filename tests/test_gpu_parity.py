@@ -123,6 +123,11 @@ EDGE = [
     # rows of 8 KiB take the interleaved unit order, longer rows the plain one
     ("h4096_interleaved_edge", 300, 8, 64, 16, 4096, "half_masked"),
     ("h4104_plain_ragged", 300, 8, 64, 16, 4104, "half_masked"),
+    # routings of up to 4096 routes are prepared by one block in one launch,
+    # longer ones by the two-kernel form
+    ("prepare_one_block_limit", 512, 8, 64, 16, 64, "half_masked"),
+    ("prepare_two_kernels_from", 513, 8, 64, 16, 64, "half_masked"),
+    ("prepare_one_block_bad_ids", 700, 5, 37, 8, 64, "bad"),
 ]
 
 
@@ -131,6 +136,8 @@ def _edge_ids(rng, T, K, E, recipe):
         return np.full((T, K), -1, np.int64)
     if recipe == "repeats":
         return rng.integers(0, E, size=(T, K)).astype(np.int64)
+    if recipe == "bad":
+        return rng.integers(-3, E + 3, size=(T, K)).astype(np.int64)
     if recipe == "half_masked":
         idx = rng.integers(0, E, size=(T, K))
         return np.where(rng.random((T, K)) < 0.5, -1, idx).astype(np.int64)
