@@ -333,6 +333,8 @@ def main():
                     help="run a plain device copy of this size first (counter calibration)")
     ap.add_argument("--schedule-out", metavar="FILE",
                     help="write the op of every payload kernel launch, in order, as JSON")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in one HIP graph and replayed")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*_pmc.txt from two rocprofv3 counter runs")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -449,6 +451,42 @@ def main():
     med = {op: float(np.median(v)) for op, v in per_op_ms.items()}
     p10 = {op: float(np.percentile(v, 10)) for op, v in per_op_ms.items()}
     p90 = {op: float(np.percentile(v, 90)) for op, v in per_op_ms.items()}
+
+    # The same step captured once in a HIP graph and replayed: the GPU time of
+    # the five ops without the host's launch gaps (what a small, launch-bound
+    # routing costs inside a captured layer). Not under the profiler's launch
+    # schedule: replays are not recorded in it.
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                for _, fn in step_fns:
+                    fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _, fn in step_fns:
+                fn()
+        for _ in range(args.warmup):
+            g.replay()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in gev:
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        gv = [a.elapsed_time(b) for a, b in gev]
+        assert ep.read_status(handle) == 0, "unexpected status bits"
+        graph = {"step_us_median": round(float(np.median(gv)) * 1e3, 2),
+                 "step_us_avg": round(float(np.mean(gv)) * 1e3, 2),
+                 "eager_step_us_avg": round(sum(avg[op] for op in STEP_OPS) * 1e3, 2),
+                 "replays": args.steps}
+        del g
 
     # Ops outside the step, timed one at a time over the same number of
     # launches after the same warmup.
@@ -580,6 +618,7 @@ def main():
                     "T_act": nbytes["_T_act"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        **({"graph": graph} if graph is not None else {}),
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line), flush=True)
