@@ -1,6 +1,7 @@
 """Randomised GPU parity over shapes: top-k from 1 to 64 (every token-group
-size of the scatter), experts 1 to 300, alignments 1 to 64, ragged hidden
-sizes, masked, repeated and out-of-range ids, tight and overflowing
+size of the scatter), experts 1 to 400, alignments 1 to 128, ragged hidden
+sizes (short rows, long rows, and rows around the scatter's 8 KiB switch),
+routings around the one-block prepare's cutover, masked, repeated and out-of-range ids, tight and overflowing
 capacities, every payload type and both pad policies. Each case runs every
 op through the C ABI against the oracle, bit for bit (the weighted backward's
 weight gradient within its summation bound), with canaries in every output.
@@ -83,4 +84,33 @@ def _long_row_cases(n=8):
 @pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _long_row_cases(),
                          ids=lambda v: str(v) if not isinstance(v, str) else v)
 def test_random_long_rows(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind)
+
+
+def _boundary_cases(n=12):
+    # routings around the one-block prepare's 4096-route cutover, and rows
+    # around the scatter's 8 KiB switch between its two unit orders
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(n):
+        K = int(rng.choice([1, 2, 3, 8, 9, 16, 64]))
+        E = int(rng.integers(1, 400))
+        A = int(rng.choice([1, 3, 16, 128]))
+        if i % 2 == 0:
+            T = max(0, (4096 + int(rng.integers(-200, 200))) // K)
+            H = int(8 * rng.integers(1, 40))
+        else:
+            H = int(8 * rng.choice([255, 256, 257, 511, 512, 513, 1023, 1024, 1025]))
+            T = int(rng.integers(0, 200))
+        dt = str(rng.choice(["bf16", "fp16", "fp32"]))
+        fill = bool(rng.random() < 0.6)
+        kind = str(rng.choice(["distinct", "repeats", "masked", "bad"]))
+        cap_kind = str(rng.choice(["worst", "worst", "tight"]))
+        out.append((200 + i, T, K, E, A, H, dt, fill, kind, cap_kind))
+    return out
+
+
+@pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _boundary_cases(),
+                         ids=lambda v: str(v) if not isinstance(v, str) else v)
+def test_random_boundaries(i, T, K, E, A, H, dt, fill, kind, cap_kind):
     test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind)
