@@ -19,7 +19,7 @@ payloads, dispatch and combine on fp32 payloads.
 
     python bench.py [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
 
-Profiling (rocprofv3 on the GPU machine, then summarised here):
+Profiling (rocprofv3 on an MI355X, then summarised here):
     --schedule-out FILE   record, in launch order, the op of every payload
                           kernel launch (prepare excluded), so that profiled
                           dispatches can be attributed to ops
@@ -350,8 +350,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the path; runs on more than one GPU "
-              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the path; the library has no "
+              "multi-GPU path, so only --gpus 1 runs.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
