@@ -632,7 +632,7 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #define EP_REDUCE_CH 1
 #endif
 #ifndef EP_BLOCKS_PER_CU
-#define EP_BLOCKS_PER_CU 64
+#define EP_BLOCKS_PER_CU 128
 #endif
 #ifndef EP_SCATTER_NT_STORE
 #define EP_SCATTER_NT_STORE 1
@@ -676,6 +676,10 @@ constexpr bool kScatterNtStore = EP_SCATTER_NT_STORE;
 constexpr bool kScatterNtLoad = EP_SCATTER_NT_LOAD;
 constexpr bool kReduceNtStore = EP_REDUCE_NT_STORE;
 constexpr bool kReduceNtLoad = EP_REDUCE_NT_LOAD;
+// The reduce's blocks: two wavefronts each. Its wavefronts mostly handle one
+// item and exit, and measured on the MI355X small blocks start faster than
+// blocks of 4 or more wavefronts at the same wavefronts per CU.
+constexpr int kBlock = 128;
 
 // Lanes past the end of a row (a ragged last column block) load the row's
 // last vector instead, so every load is unconditional and never reads out of
@@ -922,7 +926,7 @@ __device__ __forceinline__ void accumulate_wsel(float (&acc)[Payload<DT>::N], ro
 // (up to G of them in flight per lane), then summed in fp32 in ascending k
 // from the first valid one, then rounded once to the payload type.
 template <int KT, int CH, bool WEIGHTED, int DT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kBlock)
 reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                    const int32_t* __restrict__ slot, uint32_t* status,
                    const row16_t* __restrict__ src4, const float* __restrict__ rw,
@@ -1181,7 +1185,6 @@ constexpr int kScatterBlocksPerCU = EP_SCATTER_BLOCKS_PER_CU;
 constexpr int kScatterIlvBlocksPerCU = EP_SCATTER_ILV_BLOCKS_PER_CU;
 constexpr int64_t kScatterIlvMaxRow = EP_SCATTER_ILV_MAX_ROW;
 constexpr int kReduceCH = EP_REDUCE_CH;
-constexpr int kBlock = 256;
 constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
 
 int grid_for(int64_t items, int num_cus) {
