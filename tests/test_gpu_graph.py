@@ -86,7 +86,10 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
     return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
-@pytest.mark.parametrize("name,T,H", [("dsv3", 700, 1024), ("masked_hot", 2048, 512)])
+# dsv3 at T=700 and masked_hot take the two-kernel prepare; tiny and dsv3 at
+# T=400 (at most 4096 routes) the one-block prepare
+@pytest.mark.parametrize("name,T,H", [("dsv3", 700, 1024), ("masked_hot", 2048, 512),
+                                      ("tiny", 256, 512), ("dsv3", 400, 1024)])
 def test_graph_replays_match_eager_and_oracle(name, T, H):
     cfg = workloads.CONFIGS[name]
     cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
