@@ -127,7 +127,10 @@ __device__ __forceinline__ int64_t unit_id(const int64_t (&ids)[kPrepRounds], in
 
 // One wavefront per unit of kUnitRoutes consecutive routes. Histogram of the
 // unit's valid expert ids in a wave-private LDS row; each distinct id of a
-// 64-route round is added once, by its lowest lane, with the peer count.
+// 64-route round is added once, by its lowest lane, with the peer count. The
+// count before the add plus the route's rank among its peers is the route's
+// rank among the unit's routes of its expert: it is left in slot[s], packed
+// with the expert id, for prepare_slots_kernel.
 __global__ void __launch_bounds__(512)
 prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int nbits) {
   extern __shared__ int32_t lds[];
@@ -146,17 +149,37 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
     const int64_t base = (int64_t)u * kUnitRoutes;
     int64_t ids[kPrepRounds];
     load_unit_ids(topk_idx, base, routes, lane, ids);
-#pragma unroll
-    for (int i = 0; i < kPrepRounds; ++i) {
+    // All rounds are matched first, then all claims are issued back to back
+    // (one wavefront's LDS atomics are served in order), so each route's
+    // rank among the unit's routes of its expert comes out in route order.
+    uint64_t peers[kPrepRounds];
+    uint32_t key[kPrepRounds];
+    bool valid[kPrepRounds];
+    static_for<kPrepRounds>([&](auto i) {
       const int64_t id = unit_id(ids, i, base + i * kWave + lane, routes);
-      const bool valid = id >= 0 && id < E;
-      const bool bad = !valid && id != -1;
+      valid[i] = id >= 0 && id < E;
+      const bool bad = !valid[i] && id != -1;
       bad_any |= wave_ballot(bad) != 0;
-      const uint32_t key = valid ? (uint32_t)id : 0u;
-      const uint64_t peers = match_peers(key, valid, nbits);
-      if (valid && lane == __ffsll((unsigned long long)peers) - 1)
-        atomicAdd(&hist[key], (int32_t)__popcll(peers));
-    }
+      key[i] = valid[i] ? (uint32_t)id : 0u;
+      peers[i] = match_peers(key[i], valid[i], nbits);
+    });
+    int32_t first[kPrepRounds];
+    int leader[kPrepRounds];
+    static_for<kPrepRounds>([&](auto i) {
+      leader[i] = valid[i] ? __ffsll((unsigned long long)peers[i]) - 1 : lane;
+      first[i] = 0;
+      if (valid[i] && lane == leader[i])
+        first[i] = atomicAdd(&hist[key[i]], (int32_t)__popcll(peers[i]));
+    });
+    static_for<kPrepRounds>([&](auto i) { first[i] = __shfl(first[i], leader[i]); });
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    static_for<kPrepRounds>([&](auto i) {
+      const int64_t s = base + i * kWave + lane;
+      if (s < routes) {
+        const int32_t rank = first[i] + __popcll(peers[i] & lanes_below);
+        hv.slot[s] = valid[i] ? (rank << kKeyBits) | (int32_t)key[i] : -1;
+      }
+    });
   }
   __syncthreads();
   if (u < d.num_units) {
@@ -167,13 +190,13 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
 }
 
 // Every block derives the same counts and aligned offsets from the unit
-// histograms (block 0 publishes them), then its wavefronts revisit their
-// units and hand out rows: slot = segment start + routes of the same expert
-// in earlier units + rank among earlier lanes and rounds of this unit.
+// histograms (block 0 publishes them), then its wavefronts hand out the rows
+// of their units: slot = segment start + routes of the same expert in earlier
+// units + the route's rank in its unit, which prepare_hist_kernel left in
+// slot[s].
 __global__ void __launch_bounds__(512)
-prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
-                     int32_t* __restrict__ user_counts, int32_t* __restrict__ user_offsets,
-                     int nbits) {
+prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
+                     int32_t* __restrict__ user_offsets) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t s_wave_tot[2][16];
   __shared__ int32_t s_pads_live;
@@ -193,13 +216,17 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   int32_t* s_red = s_padoff + E + 1;    // [2*nthr]
   int32_t* s_cursor = s_red + 2 * nthr; // [nw*E]: own units' counts, then cursors
 
-  // The routing ids of this wavefront's unit are loaded first, so that their
+  // The packed ranks of this wavefront's unit are loaded first, so that their
   // latency overlaps the histogram loads below.
   const int64_t routes = d.T * d.K;
   const int32_t my_unit = u0 + w;
   const int64_t base = (int64_t)my_unit * kUnitRoutes;
-  int64_t ids[kPrepRounds];
-  if (my_unit < U) load_unit_ids(topk_idx, base, routes, lane, ids);
+  int32_t pk[kPrepRounds];                // (rank in unit << kKeyBits) | expert, or -1
+  if (my_unit < U)
+    static_for<kPrepRounds>([&](auto i) {
+      const int64_t s = base + i * kWave + lane;
+      pk[i] = hv.slot[s < routes ? s : routes - 1];
+    });
 
   // 1. Column sums of the unit histograms over all units and over the units
   //    before this block; this block's own unit rows are kept in LDS. Loads
@@ -345,37 +372,18 @@ prepare_slots_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   }
   __syncthreads();
 
-  // 5. Stable slots: the lowest lane of each distinct id claims popc(peers)
-  //    rows from the cursor; every peer adds its rank among earlier lanes.
-  //    All rounds are matched first, then all claims are issued back to
-  //    back (the LDS serves one wavefront's atomics in order, so the rounds
-  //    still claim in route order), then all results are shared.
+  // 5. Stable slots: the unit's start row of the route's expert plus the
+  //    route's rank among the unit's routes of that expert.
   if (my_unit < U) {
-    const uint64_t lanes_below = (1ull << lane) - 1ull;
-    int32_t* cursor = s_cursor + w * E;
-    uint64_t peers[kPrepRounds];
-    uint32_t key[kPrepRounds];
-    bool valid[kPrepRounds];
-    static_for<kPrepRounds>([&](auto i) {
-      const int64_t id = unit_id(ids, i, base + i * kWave + lane, routes);
-      valid[i] = id >= 0 && id < E;
-      key[i] = valid[i] ? (uint32_t)id : 0u;
-      peers[i] = match_peers(key[i], valid[i], nbits);
-    });
-    int32_t first[kPrepRounds];
-    int leader[kPrepRounds];
-    static_for<kPrepRounds>([&](auto i) {
-      leader[i] = valid[i] ? __ffsll((unsigned long long)peers[i]) - 1 : lane;
-      first[i] = 0;
-      if (valid[i] && lane == leader[i])
-        first[i] = atomicAdd(&cursor[key[i]], (int32_t)__popcll(peers[i]));
-    });
-    static_for<kPrepRounds>([&](auto i) { first[i] = __shfl(first[i], leader[i]); });
+    const int32_t* cursor = s_cursor + w * E;
     static_for<kPrepRounds>([&](auto i) {
       const int64_t s = base + i * kWave + lane;
       if (s < routes) {
-        const int64_t row = (int64_t)first[i] + __popcll(peers[i] & lanes_below);
-        const bool keep = valid[i] && row < d.cap;
+        const int32_t p = pk[i];
+        const bool valid = p >= 0;
+        const int32_t e = p & ((1 << kKeyBits) - 1);
+        const int64_t row = valid ? (int64_t)cursor[e] + (p >> kKeyBits) : 0;
+        const bool keep = valid && row < d.cap;
         hv.slot[s] = keep ? (int32_t)row : -1;
         if (keep) hv.row_src[row] = (int32_t)s;
       }
@@ -1250,8 +1258,7 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   int grid2 = (U + nw2 - 1) / nw2;
   if (grid2 < 1) grid2 = 1;
   hipLaunchKernelGGL(prepare_slots_kernel, dim3(grid2), dim3(nw2 * kWave),
-                     slots_lds_bytes(d.E, nw2), stream, d, hv, topk_idx, user_counts,
-                     user_offsets, nbits);
+                     slots_lds_bytes(d.E, nw2), stream, d, hv, user_counts, user_offsets);
   return hipGetLastError();
 }
 
