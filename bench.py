@@ -17,6 +17,14 @@ time, and reported under "ops_outside_step": the fused weighted combine and
 its backward, dispatch and combine_bwd without the pad fill, combine on fp16
 payloads, dispatch and combine on fp32 payloads.
 
+Then the memory-pattern ceilings of the same device (``--no-ceilings`` skips
+them) are timed from ``libep_ceilings.so``, kernels that move bytes in the
+routing ops' access patterns with no routing at all: a dense write front, rows
+of the workload's size written in a scrambled order (dispatch's write
+pattern), a dense read front, a dense copy, and K hashed rows summed per token
+(combine's pattern at full density). They are reported under "ceilings" with
+each headline op's bandwidth as a fraction of its pattern's ceiling.
+
     python bench.py [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
 
 Profiling (rocprofv3 on an MI355X, then summarised here):
@@ -45,6 +53,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "combine_ep_prepare_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_api.hip", "ep_internal.h")]
 
 STEP_OPS = ["prepare", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
+CEILINGS_LIB = os.path.join(ROOT, "combine_ep_prepare_amd", "libep_ceilings.so")
+CEILING_BUFFER_BYTES = 1 << 30     # each pattern moves 1 GiB (or the largest fit)
 
 # op -> the library kernel that runs it
 KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
@@ -319,6 +329,84 @@ def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
     return t_d / n, t_c / n, n, time.perf_counter() - start
 
 
+def _ceilings_lib():
+    import ctypes as C
+    if not os.path.exists(CEILINGS_LIB):
+        raise ImportError(f"{CEILINGS_LIB} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = C.CDLL(CEILINGS_LIB)
+    i64, vp = C.c_int64, C.c_void_p
+    lib.epc_write_linear.argtypes = [vp, i64, vp]
+    lib.epc_write_rows.argtypes = [vp, i64, i64, vp]
+    lib.epc_read_linear.argtypes = [vp, i64, vp, vp]
+    lib.epc_copy_linear.argtypes = [vp, vp, i64, vp]
+    lib.epc_gather_sum.argtypes = [vp, i64, i64, i64, C.c_int, vp, vp]
+    for name in ("epc_write_linear", "epc_write_rows", "epc_read_linear", "epc_copy_linear",
+                 "epc_gather_sum"):
+        getattr(lib, name).restype = C.c_int
+    return lib
+
+
+def ceiling_sizes(T, K, H, esize=2, budget=CEILING_BUFFER_BYTES):
+    """Sizes of the ceiling patterns for a workload: rows of the workload's
+    payload row, as many as fit the budget (a power of two for the scrambled
+    write), and the dense gather of T tokens x K rows when K is 1, 2, 4 or 8
+    and the rows fit."""
+    row = H * esize
+    nrows = 1
+    while nrows * 2 * row <= budget:
+        nrows *= 2
+    gather = None
+    if K in (1, 2, 4, 8) and T * K * row <= budget:
+        gather = {"ntok": T, "k": K, "nrows": T * K, "row_bytes": row,
+                  "bytes": T * K * row + T * row}
+    return {"row_bytes": row, "write_rows": nrows, "write_rows_bytes": nrows * row,
+            "gather": gather}
+
+
+def measure_ceilings(T, K, H, launches, warmup):
+    """GB/s of each memory pattern on the current device and stream."""
+    import torch
+    lib = _ceilings_lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nb = CEILING_BUFFER_BYTES
+    a = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    sz = ceiling_sizes(T, K, H)
+
+    def timed(fn, nbytes):
+        for _ in range(warmup):
+            assert fn() == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(launches):
+            assert fn() == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) * 1e-3 / launches) / 1e9, 1)
+
+    out = {"unit": "GB/s", "row_bytes": sz["row_bytes"], "launches": launches}
+    out["linear_write"] = timed(lambda: lib.epc_write_linear(a.data_ptr(), nb, sp), nb)
+    out["scattered_row_write"] = timed(
+        lambda: lib.epc_write_rows(a.data_ptr(), sz["write_rows"], sz["row_bytes"], sp),
+        sz["write_rows_bytes"])
+    out["linear_read"] = timed(lambda: lib.epc_read_linear(a.data_ptr(), nb, sink.data_ptr(), sp),
+                               nb)
+    out["linear_copy"] = timed(lambda: lib.epc_copy_linear(a.data_ptr(), b.data_ptr(), nb, sp),
+                               2 * nb)
+    g = sz["gather"]
+    if g is not None:
+        out["gather_sum"] = timed(
+            lambda: lib.epc_gather_sum(a.data_ptr(), g["nrows"], g["row_bytes"], g["ntok"],
+                                       g["k"], b.data_ptr(), sp), g["bytes"])
+    del a, b, sink
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +416,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-ops", action="store_true",
                     help="skip timing the ops outside the step")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip timing the memory-pattern ceilings")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
@@ -566,6 +656,15 @@ def main():
                 "algorithmic_bytes_per_launch": nbytes[dominant],
                 "avg_launch_us": round(avg[dominant] * 1e3, 2)}
 
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(T, K, H, args.steps, args.warmup)
+        ceilings["dispatch_frac_of_scattered_row_write"] = round(
+            gbs("dispatch", nbytes["dispatch"]) / ceilings["scattered_row_write"], 4)
+        if "gather_sum" in ceilings:
+            ceilings["combine_frac_of_gather_sum"] = round(
+                gbs("combine", nbytes["combine"]) / ceilings["gather_sum"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload")
@@ -617,6 +716,7 @@ def main():
         "routing": {"R": nbytes["_R"], "P": nbytes["_P"], "total": nbytes["_total"],
                     "T_act": nbytes["_T_act"]},
         "roofline": roofline,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         **({"graph": graph} if graph is not None else {}),
         "kernel_source_hash": src_hash,

@@ -4,6 +4,10 @@ Produces ``combine_ep_prepare_amd/libcombine_ep_prepare_amd.so`` from the
 sources under ``csrc/`` with hipcc. The flags keep IEEE fp32 semantics
 (no fast-math, no contraction, no denormal flush) and disable the packed
 fp32 instructions.
+
+Also produces ``libep_ceilings.so`` from ``csrc/ep_ceilings.hip``: the
+memory-pattern ceiling kernels the benchmark times beside the routing ops.
+It is a separate object; the routing library neither links nor loads it.
 """
 from __future__ import annotations
 
@@ -17,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "ep_api.hip"), os.path.join(CSRC, "ep_kernels.hip")]
 LIB_NAME = "libcombine_ep_prepare_amd.so"
 LIB = os.path.join(HERE, LIB_NAME)
+CEILINGS_SOURCE = os.path.join(CSRC, "ep_ceilings.hip")
+CEILINGS_LIB = os.path.join(HERE, "libep_ceilings.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -34,14 +40,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library needs ROCm's hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def _compile(sources, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp, *SOURCES]
+           "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SOURCES, LIB, verbose)
+    _compile([CEILINGS_SOURCE], CEILINGS_LIB, verbose)
     return LIB
 
 
