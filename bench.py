@@ -290,7 +290,7 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
                 f"{'share%':>7s}\n")
         for r in rows:
             name = r["Name"]
-            short = name.split("(")[0].replace("void ", "")
+            short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             f.write(f"{short[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
                     f"{float(r['Percentage']):7.2f}\n")

@@ -27,7 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace epceil {
 
 typedef uint32_t vec4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
@@ -109,7 +109,9 @@ int finish(int64_t blocks) {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-}  // namespace
+}  // namespace epceil
+
+using namespace epceil;
 
 // Each entry point returns 0 on success, 1 on a launch error, 2 for sizes it
 // does not take (nothing is launched then). Pointers are device pointers,
