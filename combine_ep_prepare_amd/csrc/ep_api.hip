@@ -31,7 +31,8 @@ ep_status_t check_layout(const ep_layout_t* L) {
   if (L->alignment < 1) return EP_ERR_SHAPE;
   if (L->dtype != EP_DTYPE_BF16 && L->dtype != EP_DTYPE_FP16 && L->dtype != EP_DTYPE_FP32)
     return EP_ERR_SHAPE;
-  if ((L->flags & ~(uint32_t)EP_LAYOUT_NO_PAD_FILL) != 0) return EP_ERR_SHAPE;
+  if ((L->flags & ~(uint32_t)(EP_LAYOUT_NO_PAD_FILL | EP_LAYOUT_DENSE_ROUTING)) != 0)
+    return EP_ERR_SHAPE;
   if (L->hidden < 8 || L->hidden % 8 != 0 || L->hidden >= kInt32Limit) return EP_ERR_SHAPE;
   const int64_t routes = L->num_tokens * (int64_t)L->topk;
   const int64_t worst = routes + (int64_t)L->num_experts * ((int64_t)L->alignment - 1);
@@ -74,6 +75,7 @@ Dims dims_of(const ep_layout_t* L, int32_t num_units) {
   d.V = L->hidden * esize / 16;
   d.dtype = L->dtype;
   d.fill_pads = (L->flags & EP_LAYOUT_NO_PAD_FILL) ? 0 : 1;
+  d.dense = (L->flags & EP_LAYOUT_DENSE_ROUTING) ? 1 : 0;
   return d;
 }
 
@@ -168,9 +170,12 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(tokens) || !aligned16(recv_tokens)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  if (launch_scatter_rows(d, hv, tokens, topk_weights, recv_tokens, recv_topk_weights,
-                          num_cus, stream) != hipSuccess)
-    return EP_ERR_HIP;
+  const hipError_t e =
+      d.dense ? launch_run_rows(d, hv, tokens, topk_weights, recv_tokens, recv_topk_weights,
+                                stream)
+              : launch_scatter_rows(d, hv, tokens, topk_weights, recv_tokens,
+                                    recv_topk_weights, num_cus, stream);
+  if (e != hipSuccess) return EP_ERR_HIP;
   return EP_OK;
 }
 
@@ -223,9 +228,11 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(grad) || !aligned16(grad_expert_out)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  if (launch_scatter_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, num_cus, stream) !=
-      hipSuccess)
-    return EP_ERR_HIP;
+  const hipError_t e =
+      d.dense ? launch_run_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, stream)
+              : launch_scatter_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, num_cus,
+                                    stream);
+  if (e != hipSuccess) return EP_ERR_HIP;
   return EP_OK;
 }
 

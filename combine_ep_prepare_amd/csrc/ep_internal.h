@@ -18,6 +18,26 @@ constexpr uint32_t kHandleMagic = 0x45504D49u;  // "EPMI"
 constexpr int kPrepRounds = 8;
 constexpr int kUnitRoutes = kPrepRounds * kWave;
 
+// Run entries: the valid routes of each chunk of run_chunk_tokens(T)
+// consecutive tokens, in ascending received-row order (so the rows an expert
+// receives from one chunk, a contiguous run, are adjacent). Chunk c owns the
+// entries [c*C*K, c*C*K + routes of the chunk); a route that holds no row
+// (masked, a bad id, or dropped past the capacity) leaves an empty entry at
+// the end of its chunk's range.
+struct RunEntry {
+  int32_t row;    // received row, or -1 for an empty entry
+  int32_t route;  // route index s = t*K + k
+};
+constexpr int kRunXcds = 8;          // chunks are dealt round-robin to 8 streams
+constexpr int64_t kRunChunkMax = 256;
+
+// Tokens per chunk: 256, or fewer so that a small batch still spans all eight
+// streams. Depends on T only, so prepare and the payload ops agree.
+inline int64_t run_chunk_tokens(int64_t T) {
+  const int64_t c = (T + kRunXcds - 1) / kRunXcds;
+  return c < 1 ? 1 : (c > kRunChunkMax ? kRunChunkMax : c);
+}
+
 // Header at the start of every handle (256 bytes reserved).
 struct HandleHeader {
   uint32_t status;      // EP_STATUS_* bits of the last prepare
@@ -36,7 +56,7 @@ static_assert(sizeof(HandleHeader) <= 256, "header too large");
 // Byte offsets of the regions of a handle; every region is 256-byte aligned.
 struct HandleLayout {
   size_t header, counts, offsets, pad_offsets, slot, row_src, pad_rows, unit_hist,
-      unit_flags, bytes;
+      unit_flags, runs, bytes;
   int32_t num_units;
 };
 
@@ -60,6 +80,7 @@ inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) 
   h.pad_rows = at;     at += align256(sizeof(int32_t) * (size_t)cap);
   h.unit_hist = at;    at += align256(sizeof(int32_t) * (size_t)h.num_units * (size_t)E);
   h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
+  h.runs = at;         at += align256(sizeof(RunEntry) * (size_t)routes);
   h.bytes = at;
   return h;
 }
@@ -75,6 +96,7 @@ struct HandleView {
   int32_t* pad_rows;
   int32_t* unit_hist;
   int32_t* unit_flags;
+  RunEntry* runs;
 };
 
 inline HandleView handle_view(void* mem, const HandleLayout& h) {
@@ -89,6 +111,7 @@ inline HandleView handle_view(void* mem, const HandleLayout& h) {
   v.pad_rows = reinterpret_cast<int32_t*>(b + h.pad_rows);
   v.unit_hist = reinterpret_cast<int32_t*>(b + h.unit_hist);
   v.unit_flags = reinterpret_cast<int32_t*>(b + h.unit_flags);
+  v.runs = reinterpret_cast<RunEntry*>(b + h.runs);
   return v;
 }
 
@@ -104,6 +127,7 @@ struct Dims {
   int64_t V;          // 16-byte vectors per payload row: H * element size / 16
   int32_t dtype;      // EP_DTYPE_* of the payload rows
   int32_t fill_pads;  // 1: payload ops zero the live pad rows; 0: leave them
+  int32_t dense;      // 1: the caller states every route holds a valid expert id
 };
 
 // Launchers (ep_kernels.hip). Each returns the hipError_t of its launch.
@@ -115,6 +139,10 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
                                const float* w, void* dst, float* dst_w, int num_cus,
                                hipStream_t stream);
 // rw != nullptr selects the weighted sum (weights of the received rows).
+// The same map D over the run entries (dense routings): one launch sized
+// exactly from T and K.
+hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
+                           const float* w, void* dst, float* dst_w, hipStream_t stream);
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
                               const float* rw, const float* g_w, void* dst, float* dst_w,
                               int num_cus, hipStream_t stream);

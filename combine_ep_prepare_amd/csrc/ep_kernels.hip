@@ -607,6 +607,85 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
 }
 
 // ---------------------------------------------------------------------------
+// prepare: run entries
+// ---------------------------------------------------------------------------
+
+// Run entries (after the slot map is final). One block per chunk of C tokens:
+// the chunk's routes to expert e hold a contiguous run of e's rows (rows of a
+// segment follow route order, and a chunk's routes are consecutive), starting
+// at the smallest of them. A route's entry goes to the count of the chunk's
+// routes of lower experts plus its row's offset in its run, so the entries of
+// a chunk are in ascending row order; the chunk's remaining entries (routes
+// without a row) are marked empty.
+constexpr int kRunThreads = 1024;
+
+__global__ void __launch_bounds__(kRunThreads)
+prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int64_t C) {
+  extern __shared__ int32_t s_run[];                // base[E] (counts first), first[E]
+  __shared__ int32_t s_wave_tot[kRunThreads / kWave];
+  __shared__ int32_t s_total;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & (kWave - 1), w = tid / kWave;
+  const int E = d.E;
+  int32_t* s_base = s_run;
+  int32_t* s_first = s_run + E;
+  const int64_t CK = C * d.K;
+  const int64_t routes = d.T * (int64_t)d.K;
+  const int64_t s0 = (int64_t)blockIdx.x * CK;
+  const int64_t s1 = s0 + CK < routes ? s0 + CK : routes;
+  const int n = (int)(s1 - s0);
+  for (int e = tid; e < E; e += nthr) {
+    s_base[e] = 0;
+    s_first[e] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += nthr) {
+    const int32_t sl = hv.slot[s0 + i];
+    if (sl >= 0) {
+      const int e = (int)topk_idx[s0 + i];
+      atomicAdd(&s_base[e], 1);
+      atomicMin(&s_first[e], sl);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the counts over experts, in place: a contiguous block
+  // of experts per thread, a shuffle scan per wavefront, then wave totals
+  const int per = (E + nthr - 1) / nthr;
+  const int b0 = tid * per;
+  int32_t loc = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < E) loc += s_base[b0 + i];
+  int32_t inc = loc;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == kWave - 1) s_wave_tot[w] = inc;
+  __syncthreads();
+  int32_t ex = inc - loc;
+  for (int q = 0; q < w; ++q) ex += s_wave_tot[q];
+  for (int i = 0; i < per; ++i) {
+    if (b0 + i < E) {
+      const int32_t c = s_base[b0 + i];
+      s_base[b0 + i] = ex;
+      ex += c;
+    }
+  }
+  if (tid == nthr - 1) s_total = ex;
+  __syncthreads();
+  const int total = s_total;
+  for (int i = tid; i < n; i += nthr) {
+    const int32_t sl = hv.slot[s0 + i];
+    if (sl >= 0) {
+      const int e = (int)topk_idx[s0 + i];
+      const int pos = s_base[e] + (sl - s_first[e]);
+      hv.runs[s0 + pos] = RunEntry{sl, (int32_t)(s0 + i)};
+    }
+  }
+  for (int i = total + tid; i < n; i += nthr) hv.runs[s0 + i] = RunEntry{-1, -1};
+}
+
+// ---------------------------------------------------------------------------
 // row vectors and tunables
 // ---------------------------------------------------------------------------
 
@@ -891,6 +970,93 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       if (v < V) store_row16<kScatterNtStore>(dst4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
       if (c == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
     }
+  }
+}
+
+// D over the run entries, for dense routings. The grid's first tok_blocks
+// blocks copy token rows: block i takes stream i mod 8 (the chunks i mod 8,
+// i mod 8 + 8, ... of the run entries, one after another) and in it the 1 KiB
+// pieces 8k .. 8k+7, k = i div 8, one per wavefront; piece q of a stream is
+// column piece q mod npc of the stream's entry q div npc. The hardware deals
+// blocks round-robin over the eight XCDs, so one stream's blocks share one
+// L2: a chunk's token rows are read from memory once and then from that L2,
+// and consecutive blocks of a stream write consecutive pieces of the chunk's
+// runs (the rows an expert receives from the chunk, adjacent in memory). The
+// other blocks zero the live pad rows, kRunPadPieces pieces per wavefront
+// interleaved over the block, in address order. Every block is launched once
+// and exits, so blocks are issued in order and the write front stays dense.
+#ifndef EP_RUN_PAD_PIECES
+#define EP_RUN_PAD_PIECES 4
+#endif
+constexpr int kRunWaves = 8;
+constexpr int kRunPadPieces = EP_RUN_PAD_PIECES;
+
+__global__ void __launch_bounds__(kRunWaves * kWave)
+run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __restrict__ runs,
+                const int32_t* __restrict__ pad_rows, uint32_t* status,
+                const row16_t* __restrict__ src4, const float* __restrict__ w,
+                row16_t* __restrict__ dst4, float* __restrict__ dst_w, int64_t C,
+                uint32_t tok_blocks) {
+  const int lane = lane_id();
+  const int64_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t V = d.V;
+  const int64_t npc = (V + kWave - 1) / kWave;
+  if (blockIdx.x < tok_blocks) {
+    const int64_t x = blockIdx.x % kRunXcds;
+    const int64_t q = (int64_t)(blockIdx.x / kRunXcds) * kRunWaves + wv;
+    const int64_t CK = C * d.K;
+    const int64_t routes = d.T * (int64_t)d.K;
+    const int64_t nch = (d.T + C - 1) / C;
+    // entries of stream x: its chunks' ranges, the last chunk of all short
+    int64_t len = 0;
+    if (x < nch) {
+      len = ((nch - 1 - x) / kRunXcds + 1) * CK;
+      if ((nch - 1) % kRunXcds == x) len -= nch * CK - routes;
+    }
+    // the entry is loaded together with the header (always in bounds: the
+    // entry index is below T*K whatever the header holds)
+    RunEntry ent{-1, -1};
+    int64_t col = 0;
+    if (q < len * npc) {
+      const int64_t qe = q / npc;
+      col = q - qe * npc;
+      const int64_t j = qe / CK;
+      ent = runs[(x + j * kRunXcds) * CK + (qe - j * CK)];
+    }
+    const HandleHeader hh = *h;
+    if (!handle_matches(hh, d)) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+      return;
+    }
+    if (ent.row < 0) return;
+    const int64_t t = ent.route / d.K;
+    const int64_t v = col * kWave + lane;
+    const row16_t val = load_row16<kScatterNtLoad>(src4 + t * V + (v < V ? v : V - 1));
+    if (v < V) store_row16<kScatterNtStore>(dst4 + (int64_t)ent.row * V + v, val);
+    if (col == 0 && w != nullptr && dst_w != nullptr && lane == 0) dst_w[ent.row] = w[ent.route];
+  } else {
+    const HandleHeader hh = *h;
+    if (!handle_matches(hh, d)) {
+      if (threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+      return;
+    }
+    const int64_t live = (int64_t)hh.pads_live * npc;
+    const int64_t p0 = (int64_t)(blockIdx.x - tok_blocks) * (kRunWaves * kRunPadPieces) + wv;
+    int32_t r[kRunPadPieces];
+    static_for<kRunPadPieces>([&](auto j) {
+      const int64_t p = p0 + j * kRunWaves;
+      r[j] = p < live ? pad_rows[p / npc] : -1;
+    });
+    static_for<kRunPadPieces>([&](auto j) {
+      const int64_t p = p0 + j * kRunWaves;
+      if (r[j] >= 0) {
+        const int64_t c = p - (p / npc) * npc;
+        const int64_t v = c * kWave + lane;
+        if (v < V)
+          store_row16<kScatterNtStore>(dst4 + (int64_t)r[j] * V + v, row16_t{0u, 0u, 0u, 0u});
+        if (c == 0 && dst_w != nullptr && lane == 0) dst_w[r[j]] = 0.0f;
+      }
+    });
   }
 }
 
@@ -1232,6 +1398,20 @@ row16_t* rows_out(void* p) { return static_cast<row16_t*>(p); }
 
 }  // namespace
 
+namespace {
+
+hipError_t launch_prepare_runs(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
+                               hipStream_t stream) {
+  if (d.T == 0) return hipSuccess;
+  const int64_t C = run_chunk_tokens(d.T);
+  const int64_t chunks = (d.T + C - 1) / C;
+  hipLaunchKernelGGL(prepare_runs_kernel, dim3((unsigned)chunks), dim3(kRunThreads),
+                     2 * sizeof(int32_t) * (size_t)d.E, stream, d, hv, topk_idx, C);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
                           int32_t* user_counts, int32_t* user_offsets, int num_cus,
                           hipStream_t stream) {
@@ -1242,7 +1422,9 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   if (d.T * (int64_t)d.K <= (int64_t)kPrepFusedMaxRoutes && fused_lds <= kLdsBudget) {
     hipLaunchKernelGGL(prepare_fused_kernel, dim3(1), dim3(kFusedWaves * kWave), fused_lds,
                        stream, d, hv, topk_idx, user_counts, user_offsets, nbits);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_prepare_runs(d, hv, topk_idx, stream);
   }
   if (U > 0) {
     int nw1 = 8;
@@ -1259,7 +1441,9 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   if (grid2 < 1) grid2 = 1;
   hipLaunchKernelGGL(prepare_slots_kernel, dim3(grid2), dim3(nw2 * kWave),
                      slots_lds_bytes(d.E, nw2), stream, d, hv, user_counts, user_offsets);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_prepare_runs(d, hv, topk_idx, stream);
 }
 
 hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,
@@ -1281,6 +1465,37 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
                      dim3(kScatterWaves * kWave), 0, stream, d, hv.header, hv.slot, hv.pad_rows,
                      &hv.header->status, rows_in(src), w, rows_out(dst), dst_w,
                      (int)interleave);
+  return hipGetLastError();
+}
+
+hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
+                           const float* w, void* dst, float* dst_w, hipStream_t stream) {
+  const int64_t npc = (d.V + kWave - 1) / kWave;
+  int64_t C = 0, tok_blocks = 0;
+  if (d.T > 0) {
+    C = run_chunk_tokens(d.T);
+    const int64_t nch = (d.T + C - 1) / C;
+    // stream 0 holds the most chunks; a shorter stream's extra blocks exit
+    const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
+    tok_blocks = kRunXcds * ((entries * npc + kRunWaves - 1) / kRunWaves);
+  }
+  int64_t pad_rows_max = (int64_t)d.E * (d.A - 1);
+  if (pad_rows_max > d.cap) pad_rows_max = d.cap;
+  const int64_t per_block = (int64_t)kRunWaves * kRunPadPieces;
+  const int64_t pad_blocks = d.fill_pads ? (pad_rows_max * npc + per_block - 1) / per_block : 0;
+  const int64_t grid = tok_blocks + pad_blocks;
+  if (grid == 0) return hipSuccess;
+  if (grid >= ((int64_t)1 << 31)) {
+    // a size no buffer in memory reaches; the scatter takes any size
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    return launch_scatter_rows(d, hv, src, w, dst, dst_w, cus, stream);
+  }
+  hipLaunchKernelGGL(run_rows_kernel, dim3((unsigned)grid), dim3(kRunWaves * kWave), 0, stream, d,
+                     hv.header, hv.runs, hv.pad_rows, &hv.header->status, rows_in(src), w,
+                     rows_out(dst), dst_w, C, (uint32_t)tok_blocks);
   return hipGetLastError();
 }
 

@@ -102,8 +102,20 @@ enum {
  * thread); this flag makes the pad writes a choice. It does not change the
  * routing maps: one prepared handle serves both policies. */
 enum {
-  EP_LAYOUT_NO_PAD_FILL = 1u
+  EP_LAYOUT_NO_PAD_FILL = 1u,
+  EP_LAYOUT_DENSE_ROUTING = 2u
 };
+
+/* EP_LAYOUT_DENSE_ROUTING: the caller states that every entry of topk_idx is
+ * a valid expert id (no -1 masks), as when all of a layer's experts are local.
+ * It is a speed hint for ep_dispatch and ep_combine_bwd only and never changes
+ * a result: with it they copy the rows in received-row order, chunk by chunk
+ * of the tokens, in one launch sized from T and K (the valid-route count of a
+ * dense routing), which writes each expert's rows from a chunk as one
+ * contiguous run. Without it (or for a routing that breaks the statement,
+ * which is then still handled correctly but more slowly) they walk the tokens
+ * and scatter each route's row. The routing maps the copy needs are built by
+ * every ep_prepare, whatever its flags. */
 
 /*
  * Per-layer sizes (the role of the layer configuration in the common C API,

@@ -57,9 +57,9 @@ class GpuRun:
     """One handle: prepare, then any of the payload ops."""
 
     def __init__(self, topk_idx: np.ndarray, E: int, A: int, H: int, cap: int,
-                 stream=None):
+                 stream=None, dense: bool = False):
         T, K = topk_idx.shape
-        self.layout = ep.Layout(T, K, E, A, H, cap)
+        self.layout = ep.Layout(T, K, E, A, H, cap, dense=dense)
         self.T, self.K, self.E, self.A, self.H, self.cap = T, K, E, A, H, cap
         self.stream = stream
         self.handle = ep.new_handle(self.layout)

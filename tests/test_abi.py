@@ -94,8 +94,9 @@ def test_bad_layouts_rejected(kw, code):
 
 
 @pytest.mark.parametrize("dtype,flags,ok", [
-    (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True),
-    (3, 0, False), (0xFFFF, 0, False), (0, 2, False), (0, 0x8001, False),
+    (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True), (0, 2, True),
+    (1, 3, True), (3, 0, False), (0xFFFF, 0, False), (0, 4, False), (0, 6, False),
+    (0, 0x8001, False),
 ])
 def test_payload_type_and_flags_validated(dtype, flags, ok):
     L = lay()
@@ -103,7 +104,8 @@ def test_payload_type_and_flags_validated(dtype, flags, ok):
     L.flags = flags
     n = ep.handle_mem_size(L)
     if ok:
-        # neither the payload type nor the pad policy changes the handle
+        # neither the payload type, the pad policy nor the dense-routing hint
+        # changes the handle
         assert n == ep.handle_mem_size(lay())
     else:
         assert n == 0

@@ -98,11 +98,11 @@ def gamma(H, dt):
     return n * u / (1 - n * u)
 
 
-def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False):
+def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense=False):
     T, K = idx.shape
-    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} T={T} K={K} E={E} A={A} H={H} "
-        f"cap={cap}")
-    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads)
+    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} dense={dense} T={T} K={K} E={E} "
+        f"A={A} H={H} cap={cap}")
+    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads, dense=dense)
     handle = ep.new_handle(L)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ep.prepare(L, torch.from_numpy(idx).cuda(), counts, handle)
