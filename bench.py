@@ -65,14 +65,31 @@ KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_
                 "combine_bwd_nopad": "scatter_rows_kernel",
                 "combine_fp16": "reduce_rows_kernel",
                 "dispatch_fp32": "scatter_rows_kernel",
-                "combine_fp32": "reduce_rows_kernel"}
-PAYLOAD_KERNELS = ("scatter_rows_kernel", "reduce_rows_kernel", "weighted_bwd_kernel")
+                "combine_fp32": "reduce_rows_kernel",
+                "dispatch_scatter": "scatter_rows_kernel"}
+PAYLOAD_KERNELS = ("scatter_rows_kernel", "reduce_rows_kernel", "weighted_bwd_kernel",
+                   "run_rows_kernel")
+# ops that copy over the run entries when the routing is dense (no masked
+# route, EP_LAYOUT_DENSE_ROUTING); "dispatch_scatter" is dispatch without the
+# flag, timed beside it
+DENSE_OPS = ("dispatch", "combine_bwd", "dispatch_nopad", "combine_bwd_nopad", "dispatch_fp32")
+PREPARE_KERNELS = ("prepare_hist_kernel", "prepare_slots_kernel", "prepare_fused_kernel",
+                   "prepare_runs_kernel")
 
-# ops timed after the step: op -> (payload type, pads filled)
-EXTRA_OPS = {"combine_weighted": ("bf16", True), "combine_weighted_bwd": ("bf16", True),
-             "dispatch_nopad": ("bf16", False), "combine_bwd_nopad": ("bf16", False),
-             "combine_fp16": ("fp16", True), "dispatch_fp32": ("fp32", True),
-             "combine_fp32": ("fp32", True)}
+
+def kernel_of(op: str, dense: bool) -> str:
+    """The library kernel that runs ``op`` (dispatch and combine_bwd take the
+    run-entry copy on a dense routing)."""
+    if dense and op in DENSE_OPS:
+        return "run_rows_kernel"
+    return KERNEL_OF_OP[op]
+
+# ops timed after the step: op -> (payload type, pads filled, dense path allowed)
+EXTRA_OPS = {"combine_weighted": ("bf16", True, True),
+             "combine_weighted_bwd": ("bf16", True, True),
+             "dispatch_nopad": ("bf16", False, True), "combine_bwd_nopad": ("bf16", False, True),
+             "combine_fp16": ("fp16", True, True), "dispatch_fp32": ("fp32", True, True),
+             "combine_fp32": ("fp32", True, True), "dispatch_scatter": ("bf16", True, False)}
 ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
 
 
@@ -135,13 +152,13 @@ def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np, esize=2, fill
 
 def base_op(op: str) -> str:
     """dispatch_fp32 -> dispatch, combine_bwd_nopad -> combine_bwd, ..."""
-    for suffix in ("_nopad", "_fp16", "_fp32"):
+    for suffix in ("_nopad", "_fp16", "_fp32", "_scatter"):
         if op.endswith(suffix):
             return op[:-len(suffix)]
     return op
 
 
-def attribute(kernel_names, schedule):
+def attribute(kernel_names, schedule, dense=False):
     """Pair the library's payload-kernel dispatches (demangled names in
     dispatch order, all other kernels already left out) with the ops recorded
     in launch order. Raises if the two do not line up."""
@@ -149,7 +166,7 @@ def attribute(kernel_names, schedule):
         raise SystemExit(f"{len(kernel_names)} payload dispatches profiled but "
                          f"{len(schedule)} launches recorded")
     for i, (name, op) in enumerate(zip(kernel_names, schedule)):
-        if KERNEL_OF_OP[op] not in name:
+        if kernel_of(op, dense) not in name:
             raise SystemExit(f"dispatch {i}: {name} does not run {op}")
     return list(schedule)
 
@@ -165,22 +182,24 @@ def _read_csv_rows(directory: str, suffix: str):
 
 
 def _schedule(directory: str):
+    """(ops in launch order, whether the run took the dense-routing path)."""
     with open(os.path.join(directory, "schedule.json")) as f:
-        return json.load(f)["ops"]
+        d = json.load(f)
+    return d["ops"], bool(d.get("dense", False))
 
 
 def _is_payload(name: str) -> bool:
     return any(k in name for k in PAYLOAD_KERNELS)
 
 
-def _pmc_path(op: str, workload: str) -> str:
-    return os.path.join(PROFILE_DIR, f"{KERNEL_OF_OP[op]}_{op}_{workload}_pmc.txt")
+def _pmc_path(op: str, workload: str, dense: bool = False) -> str:
+    return os.path.join(PROFILE_DIR, f"{kernel_of(op, dense)}_{op}_{workload}_pmc.txt")
 
 
-def load_traffic(op: str, workload: str, src_hash: str):
+def load_traffic(op: str, workload: str, src_hash: str, dense: bool = False):
     """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
     used only when it was taken on the current kernel sources."""
-    path = _pmc_path(op, workload)
+    path = _pmc_path(op, workload, dense)
     if not os.path.exists(path):
         return None
     try:
@@ -217,7 +236,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         expected_kib = copy_mib * 1024.0
         factor = float(np.median([float(r["Counter_Value"]) for r in calib])) / expected_kib
         pay = [r for r in rows if _is_payload(r["Kernel_Name"])]
-        ops = attribute([r["Kernel_Name"] for r in pay], _schedule(d))
+        sched, dense = _schedule(d)
+        ops = attribute([r["Kernel_Name"] for r in pay], sched, dense)
+        res["dense"] = dense
         per_op = {}
         for r, op in zip(pay, ops):
             per_op.setdefault(op, []).append(float(r["Counter_Value"]) / factor * 1024.0)
@@ -239,11 +260,13 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         if fb is None or wb is None:
             continue
         summary = dict(out)
-        summary.update({"op": op, "kernel": KERNEL_OF_OP[op], "fetch_bytes_per_launch": fb,
-                        "write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb})
-        path = _pmc_path(op, workload)
+        kern = kernel_of(op, res["dense"])
+        summary.update({"op": op, "kernel": kern, "dense_routing": res["dense"],
+                        "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                        "hbm_bytes_per_launch": fb + wb})
+        path = _pmc_path(op, workload, res["dense"])
         with open(path, "w") as f:
-            f.write(f"# HBM traffic of {KERNEL_OF_OP[op]} ({op}), workload {workload}\n")
+            f.write(f"# HBM traffic of {kern} ({op}), workload {workload}\n")
             f.write(f"# command: {cmd}\n")
             f.write(f"# FETCH_SIZE scale {out['calibration']['fetch_factor']:.4f}, WRITE_SIZE "
                     f"scale {out['calibration']['write_factor']:.4f} (counter / true bytes of "
@@ -265,14 +288,15 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
     trace = _read_csv_rows(trace_dir, "kernel_trace.csv")
     trace.sort(key=lambda r: int(r["Dispatch_Id"]))
     pay = [r for r in trace if _is_payload(r["Kernel_Name"])]
-    ops = attribute([r["Kernel_Name"] for r in pay], _schedule(trace_dir))
+    sched, dense = _schedule(trace_dir)
+    ops = attribute([r["Kernel_Name"] for r in pay], sched, dense)
     per_op = {}
     for r, op in zip(pay, ops):
         per_op.setdefault(op, []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     prep = {}
     for r in trace:
-        for k in ("prepare_hist_kernel", "prepare_slots_kernel"):
+        for k in PREPARE_KERNELS:
             if k in r["Kernel_Name"]:
                 prep.setdefault(k, []).append(
                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -298,7 +322,7 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
         f.write(f"{'op':24s} {'kernel':22s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
                 f"{'max_us':>9s}\n")
         for op, v in list(per_op.items()) + list(prep.items()):
-            kern = KERNEL_OF_OP.get(op, op)
+            kern = kernel_of(op, dense) if op in KERNEL_OF_OP else op
             f.write(f"{op:24s} {kern:22s} {len(v):6d} {np.mean(v):9.2f} {np.min(v):9.2f} "
                     f"{np.max(v):9.2f}\n")
     print(path, flush=True)
@@ -459,7 +483,10 @@ def main():
     log(f"workload {cfg.name}: T={T} H={H} E={E} K={K} A={A}")
     r = workloads.make_routing(cfg)
     cap = ep.recv_capacity_worst(T, K, E, A)
-    L = ep.Layout(T, K, E, A, H, cap)
+    # a routing with no masked route takes the dense-routing copy (the flag a
+    # caller sets when all of a layer's experts are local)
+    dense = bool((r.topk_idx >= 0).all())
+    L = ep.Layout(T, K, E, A, H, cap, dense=dense)
     dev = torch.device("cuda")
     handle = ep.new_handle(L)
     idx = torch.from_numpy(r.topk_idx).to(dev)
@@ -582,7 +609,8 @@ def main():
     # launches after the same warmup.
     extra = {}
     if not args.no_extra_ops:
-        lay = {key: ep.Layout(T, K, E, A, H, cap, dtype=key[0], fill_pads=key[1])
+        lay = {key: ep.Layout(T, K, E, A, H, cap, dtype=key[0], fill_pads=key[1],
+                              dense=dense and key[2])
                for key in set(EXTRA_OPS.values())}
         result_w = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         g_rows_w = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
@@ -607,9 +635,13 @@ def main():
             "combine_fp16": lambda Lx: ep.combine(Lx, handle, eo16, res16),
             "dispatch_fp32": lambda Lx: ep.dispatch(Lx, handle, x32, w, recv32, recv_w32),
             "combine_fp32": lambda Lx: ep.combine(Lx, handle, eo32, res32),
+            "dispatch_scatter": lambda Lx: ep.dispatch(Lx, handle, x, w, recv_np, recv_w_np),
         }
-        for op, (dt, fill) in EXTRA_OPS.items():
-            Lx = lay[(dt, fill)]
+        for op, key in EXTRA_OPS.items():
+            if op == "dispatch_scatter" and not dense:
+                continue                      # the same launch as dispatch itself
+            dt, fill = key[0], key[1]
+            Lx = lay[key]
             fn = fns[op]
             for _ in range(args.warmup):
                 schedule.append(op)
@@ -636,7 +668,7 @@ def main():
     if args.schedule_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.schedule_out)), exist_ok=True)
         with open(args.schedule_out, "w") as f:
-            json.dump({"ops": schedule}, f)
+            json.dump({"ops": schedule, "dense": dense}, f)
 
     def gbs(op, nb):
         return nb / (avg[op] * 1e-3) / 1e9
@@ -647,9 +679,9 @@ def main():
     dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
                    key=lambda op: avg[op])
     src_hash = kernel_source_hash()
-    traffic = load_traffic(dominant, cfg.name, src_hash)
+    traffic = load_traffic(dominant, cfg.name, src_hash, dense)
     achieved = gbs(dominant, nbytes[dominant])
-    roofline = {"bound": "hbm", "kernel": f"{KERNEL_OF_OP[dominant]} ({dominant})",
+    roofline = {"bound": "hbm", "kernel": f"{kernel_of(dominant, dense)} ({dominant})",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -698,7 +730,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} topk={K} alignment={A} "
                                f"routing={cfg.routing} cap={cap}",
-                   "global_batch": T, "parallelism": "none (one GPU's share)"},
+                   "global_batch": T, "parallelism": "none (one GPU's share)",
+                   "dense_routing": dense},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / pair_s, 1),
         "ops": {op: {"avg_us": round(avg[op] * 1e3, 2), "median_us": round(med[op] * 1e3, 2),

@@ -58,6 +58,22 @@ def test_attribution_follows_the_launch_schedule():
         bench.attribute(names, ["combine"] + sched[1:])   # a scatter recorded as combine
 
 
+def test_attribution_of_the_dense_routing_path():
+    # dense routings run dispatch and combine_bwd over the run entries; the
+    # scatter stays for the op timed without the flag
+    names = ["epmi::run_rows_kernel", "epmi::reduce_rows_kernel<8, 1, false, 0>",
+             "epmi::run_rows_kernel", "epmi::scatter_rows_kernel<2>"]
+    sched = ["dispatch", "combine", "combine_bwd", "dispatch_scatter"]
+    assert bench.attribute(names, sched, dense=True) == sched
+    with pytest.raises(SystemExit):
+        bench.attribute(names, sched, dense=False)
+    assert bench.kernel_of("dispatch", True) == "run_rows_kernel"
+    assert bench.kernel_of("dispatch", False) == "scatter_rows_kernel"
+    assert bench.kernel_of("combine", True) == "reduce_rows_kernel"
+    assert bench.kernel_of("dispatch_scatter", True) == "scatter_rows_kernel"
+    assert bench.base_op("dispatch_scatter") == "dispatch"
+
+
 def test_more_than_one_gpu_is_refused():
     import subprocess
     import sys
