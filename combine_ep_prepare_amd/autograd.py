@@ -42,10 +42,14 @@ from . import (Layout, combine as _combine, combine_bwd as _combine_bwd,
 class EpRouting:
     """One prepared routing: handle, token counts and segment offsets. The
     handle does not depend on the payload type, so one routing serves bf16,
-    fp16 and fp32 payloads; ``fill_pads=False`` leaves pad rows unwritten."""
+    fp16 and fp32 payloads; ``fill_pads=False`` leaves pad rows unwritten;
+    ``dense=True`` states that ``topk_idx`` holds no masked route (-1), which
+    lets dispatch and its backward copy rows in received-row order (faster;
+    the results are the same either way)."""
 
     def __init__(self, topk_idx: torch.Tensor, num_experts: int, alignment: int, hidden: int,
-                 recv_capacity: Optional[int] = None, fill_pads: bool = True):
+                 recv_capacity: Optional[int] = None, fill_pads: bool = True,
+                 dense: bool = False):
         if topk_idx.dtype != torch.int64:
             raise TypeError("topk_idx must be int64")
         T, K = topk_idx.shape
@@ -53,6 +57,7 @@ class EpRouting:
             recv_capacity = recv_capacity_worst(T, K, num_experts, alignment)
         self._dims = (T, K, num_experts, alignment, hidden, recv_capacity)
         self.fill_pads = fill_pads
+        self.dense = dense
         self._layouts = {}
         self.layout = self.layout_for(torch.bfloat16)
         self.handle = new_handle(self.layout, device=topk_idx.device)
@@ -65,7 +70,8 @@ class EpRouting:
     def layout_for(self, dtype: torch.dtype) -> Layout:
         """The layout of this routing for payloads of ``dtype``."""
         if dtype not in self._layouts:
-            self._layouts[dtype] = Layout(*self._dims, dtype=dtype, fill_pads=self.fill_pads)
+            self._layouts[dtype] = Layout(*self._dims, dtype=dtype, fill_pads=self.fill_pads,
+                                          dense=self.dense)
         return self._layouts[dtype]
 
 

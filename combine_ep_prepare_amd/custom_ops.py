@@ -20,7 +20,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 from torch import Tensor
 
-from . import (DTYPE_BF16, LAYOUT_NO_PAD_FILL, TORCH_DTYPE, Layout, combine as _combine,
+from . import (DTYPE_BF16, LAYOUT_DENSE_ROUTING, LAYOUT_NO_PAD_FILL, TORCH_DTYPE, Layout,
+               combine as _combine,
                combine_bwd as _combine_bwd, combine_weighted as _combine_weighted,
                combine_weighted_bwd as _combine_weighted_bwd, dispatch as _dispatch,
                dispatch_bwd as _dispatch_bwd, prepare as _prepare)
@@ -36,7 +37,8 @@ def layout_list(layout: Layout) -> List[int]:
 
 def _layout(ll: Sequence[int]) -> Layout:
     T, K, E, A, H, cap, dt, flags = ll
-    return Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=not (flags & LAYOUT_NO_PAD_FILL))
+    return Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=not (flags & LAYOUT_NO_PAD_FILL),
+                  dense=bool(flags & LAYOUT_DENSE_ROUTING))
 
 
 def _pdtype(ll: Sequence[int]) -> torch.dtype:

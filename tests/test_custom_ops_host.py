@@ -54,3 +54,12 @@ def test_layout_list_round_trip():
     assert ll == [5, 2, 3, 4, 64, 100, ep.DTYPE_FP32, ep.LAYOUT_NO_PAD_FILL]
     L2 = cops._layout(ll)
     assert cops.layout_list(L2) == ll
+
+
+def test_layout_flags_round_trip():
+    # the pad policy and the dense-routing hint both survive the op schema
+    for fill, dense in ((True, False), (False, False), (True, True), (False, True)):
+        L = ep.Layout(16, 2, 4, 8, 64, 100, dtype="fp16", fill_pads=fill, dense=dense)
+        back = cops._layout(cops.layout_list(L))
+        assert back.flags == L.flags and back.dtype == L.dtype
+        assert cops.layout_list(back) == cops.layout_list(L)

@@ -61,9 +61,10 @@ def test_identity_round_trip_and_none_weight_grad():
     assert w.grad is not None and torch.count_nonzero(w.grad) == 0
 
 
-def test_weighted_round_trip_grads_match_oracle():
+@pytest.mark.parametrize("dense", [False, True])
+def test_weighted_round_trip_grads_match_oracle(dense):
     cfg, r, idx, x, w = _setup(name="qwen3", T=500, H=256, seed=1)
-    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H)
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H, dense=dense)
     x = x.clone().requires_grad_(True)
     w = w.clone().requires_grad_(True)
     recv, recv_w = epa.dispatch(x, w, routing)

@@ -88,12 +88,16 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 # dsv3 at T=700 and masked_hot take the two-kernel prepare; tiny and dsv3 at
 # T=400 (at most 4096 routes) the one-block prepare
-@pytest.mark.parametrize("name,T,H", [("dsv3", 700, 1024), ("masked_hot", 2048, 512),
-                                      ("tiny", 256, 512), ("dsv3", 400, 1024)])
-def test_graph_replays_match_eager_and_oracle(name, T, H):
+# (dense: dispatch and combine_bwd through the run entries; on masked_hot the
+# flag's statement does not hold and the results must not change)
+@pytest.mark.parametrize("name,T,H,dense", [
+    ("dsv3", 700, 1024, False), ("masked_hot", 2048, 512, False), ("tiny", 256, 512, False),
+    ("dsv3", 400, 1024, False), ("dsv3", 700, 1024, True), ("tiny", 256, 512, True),
+    ("masked_hot", 2048, 512, True)])
+def test_graph_replays_match_eager_and_oracle(name, T, H, dense):
     cfg = workloads.CONFIGS[name]
     cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
-    L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap)
+    L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap, dense=dense)
     g_step, e_step = Step(L), Step(L)
     _fill(g_step, cfg, 0)
     # warm up on a side stream, then capture
