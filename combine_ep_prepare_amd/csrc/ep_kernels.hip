@@ -973,29 +973,25 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
   }
 }
 
-// D over the run entries, for dense routings. The grid's first tok_blocks
-// blocks copy token rows: block i takes stream i mod 8 (the chunks i mod 8,
-// i mod 8 + 8, ... of the run entries, one after another) and in it 8P
-// consecutive 1 KiB pieces, P per wavefront; piece q of a stream is column
-// piece q mod npc of the stream's entry q div npc. The hardware deals blocks
-// round-robin over the eight XCDs, so one stream's blocks share one L2: a
-// chunk's token rows are read from memory once and then from that L2, and
-// consecutive blocks of a stream write consecutive pieces of the chunk's runs
-// (the rows an expert receives from the chunk, adjacent in memory). The other
-// blocks zero the live pad rows, each XCD one contiguous share of them in
-// address order. Every block runs once and exits, so blocks are issued in
-// order and each XCD's write front stays one dense band; measured on the
+// D over the run entries, for dense routings. Block i takes stream i mod 8
+// (the chunks i mod 8, i mod 8 + 8, ... of the run entries, one after
+// another) and in it 8P consecutive 1 KiB pieces, P per wavefront; piece q of
+// a stream is column piece q mod npc of the stream's entry q div npc. The
+// hardware deals blocks round-robin over the eight XCDs, so one stream's
+// blocks share one L2: a chunk's token rows are read from memory once and
+// then from that L2, and consecutive blocks of a stream write consecutive
+// pieces of the chunk's runs (the rows an expert receives from the chunk,
+// adjacent in memory). Each block also zeroes its slice of its XCD's share of
+// the pad rows. Every block runs once and exits, so blocks are issued in
+// order and each XCD's write fronts stay dense bands; measured on the
 // MI355X, contiguous runs of 128 KiB and more written this way reach
 // 6.5 TB/s against 5.1 TB/s for rows in scattered order.
-#ifndef EP_RUN_PAD_PIECES
-#define EP_RUN_PAD_PIECES 8
-#endif
 #ifndef EP_RUN_TOK_PIECES
 #define EP_RUN_TOK_PIECES 4
 #endif
 
+
 constexpr int kRunWaves = 8;
-constexpr int kRunPadPieces = EP_RUN_PAD_PIECES;
 constexpr int kRunTokPieces = EP_RUN_TOK_PIECES;
 
 // Sizes of a run-entry copy, computed on the host; every index of the launch
@@ -1006,7 +1002,7 @@ struct RunGeom {
   uint32_t CK;          // routes (entries) per chunk
   uint32_t nch;         // chunks
   uint32_t last_short;  // entries the last chunk lacks: nch*CK - T*K
-  uint32_t tok_blocks;  // blocks of the token part
+  uint32_t tok_blocks;  // blocks of the launch
 };
 
 __global__ void __launch_bounds__(kRunWaves * kWave)
@@ -1017,90 +1013,84 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t V = d.V;
-  // Token blocks first, then pad blocks.
-  const bool tok = blockIdx.x < g.tok_blocks;
   const uint32_t tb = blockIdx.x;
-  const uint32_t pb = blockIdx.x - g.tok_blocks;
-  if (tok) {
-    // Block k of stream x holds pieces k*8P .. k*8P + 8P-1 of the stream,
-    // wavefront wv the pieces k*8P + 8j + wv (j < P): at each step the block
-    // writes 8 consecutive pieces. Entries and rows are loaded without
-    // conditions (a piece past the stream reads entry 0 and is dropped), so
-    // all loads of a step are in flight together.
-    const uint32_t x = tb % kRunXcds;
-    const uint32_t q0 = (tb / kRunXcds) * (kRunWaves * kRunTokPieces) + wv;
-    uint32_t len = 0;
-    if (x < g.nch) {
-      len = ((g.nch - 1 - x) / kRunXcds + 1) * g.CK;
-      if ((g.nch - 1) % kRunXcds == x) len -= g.last_short;
-    }
-    const uint32_t pieces = len * g.npc;
-    RunEntry ent[kRunTokPieces];
-    uint32_t col[kRunTokPieces];
+  // Block k of stream x holds pieces k*8P .. k*8P + 8P-1 of the stream,
+  // wavefront wv the pieces k*8P + 8j + wv (j < P): at each step the block
+  // writes 8 consecutive pieces. Entries and rows are loaded without
+  // conditions (a piece past the stream reads entry 0 and is dropped), so
+  // all loads of a step are in flight together.
+  const uint32_t x = tb % kRunXcds;
+  const uint32_t q0 = (tb / kRunXcds) * (kRunWaves * kRunTokPieces) + wv;
+  uint32_t len = 0;
+  if (x < g.nch) {
+    len = ((g.nch - 1 - x) / kRunXcds + 1) * g.CK;
+    if ((g.nch - 1) % kRunXcds == x) len -= g.last_short;
+  }
+  const uint32_t pieces = len * g.npc;
+  RunEntry ent[kRunTokPieces];
+  uint32_t col[kRunTokPieces];
+  static_for<kRunTokPieces>([&](auto j) {
+    const uint32_t q = q0 + j * kRunWaves;
+    const bool in = q < pieces;
+    const uint32_t qq = in ? q : 0;
+    const uint32_t qe = qq / g.npc;
+    col[j] = qq - qe * g.npc;
+    const uint32_t c = qe / g.CK;
+    ent[j] = runs[in ? (x + c * kRunXcds) * g.CK + (qe - c * g.CK) : 0u];
+    if (!in) ent[j].row = -1;
+  });
+  const HandleHeader hh = *h;
+  if (!handle_matches(hh, d)) {
+    if (tb == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+    return;
+  }
+  row16_t val[kRunTokPieces];
+  static_for<kRunTokPieces>([&](auto j) {
+    const uint32_t t = ent[j].row >= 0 ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
+    const int64_t v = (int64_t)(col[j] * kWave + lane);
+    val[j] = load_row16<kScatterNtLoad>(src4 + (int64_t)t * V + (v < V ? v : V - 1));
+  });
+  consume(val);
+  static_for<kRunTokPieces>([&](auto j) {
+    const int64_t v = (int64_t)(col[j] * kWave + lane);
+    if (ent[j].row >= 0 && v < V)
+      store_row16<kScatterNtStore>(dst4 + (int64_t)ent[j].row * V + v, val[j]);
+  });
+  if (w != nullptr && dst_w != nullptr && lane == 0) {
     static_for<kRunTokPieces>([&](auto j) {
-      const uint32_t q = q0 + j * kRunWaves;
-      const bool in = q < pieces;
-      const uint32_t qq = in ? q : 0;
-      const uint32_t qe = qq / g.npc;
-      col[j] = qq - qe * g.npc;
-      const uint32_t c = qe / g.CK;
-      ent[j] = runs[in ? (x + c * kRunXcds) * g.CK + (qe - c * g.CK) : 0u];
-      if (!in) ent[j].row = -1;
+      if (ent[j].row >= 0 && col[j] == 0) dst_w[ent[j].row] = w[ent[j].route];
     });
-    const HandleHeader hh = *h;
-    if (!handle_matches(hh, d)) {
-      if (tb == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
-      return;
-    }
-    row16_t val[kRunTokPieces];
-    static_for<kRunTokPieces>([&](auto j) {
-      const uint32_t t = ent[j].row >= 0 ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
-      const int64_t v = (int64_t)(col[j] * kWave + lane);
-      val[j] = load_row16<kScatterNtLoad>(src4 + (int64_t)t * V + (v < V ? v : V - 1));
-    });
-    consume(val);
-    static_for<kRunTokPieces>([&](auto j) {
-      const int64_t v = (int64_t)(col[j] * kWave + lane);
-      if (ent[j].row >= 0 && v < V)
-        store_row16<kScatterNtStore>(dst4 + (int64_t)ent[j].row * V + v, val[j]);
-    });
-    if (w != nullptr && dst_w != nullptr && lane == 0) {
-      static_for<kRunTokPieces>([&](auto j) {
-        if (ent[j].row >= 0 && col[j] == 0) dst_w[ent[j].row] = w[ent[j].route];
-      });
-    }
-  } else {
-    // The live pad pieces are split into kRunXcds contiguous shares, share x
-    // zeroed in order by the pad blocks of XCD x (pad block pb is the
-    // pb / kRunXcds-th of XCD pb % kRunXcds), so each XCD's write front is one
-    // dense band. The header is needed first (the share size).
-    const HandleHeader hh = *h;
-    if (!handle_matches(hh, d)) {
-      if (threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
-      return;
-    }
+  }
+  if (d.fill_pads) {
+    // Pads: the live pad pieces are split into kRunXcds contiguous shares and
+    // share x is split over stream x's blocks in order, so the pads of each
+    // XCD are zeroed as one dense band alongside its token runs (two pieces
+    // per wavefront and step). A routing has pad rows only if some route is
+    // valid, so T > 0 and these blocks exist whenever pads do.
     const uint32_t all = (uint32_t)hh.pads_live * g.npc;
     const uint32_t share = (all + kRunXcds - 1) / kRunXcds;
-    const uint32_t xs = pb % kRunXcds;
-    const uint32_t lo = xs * share;
-    const uint32_t hi = lo + share < all ? lo + share : all;
-    const uint32_t p0 = lo + (pb / kRunXcds) * (kRunWaves * kRunPadPieces) + wv;
-    const uint32_t live = hi;
-    int32_t r[kRunPadPieces];
-    static_for<kRunPadPieces>([&](auto j) {
-      const uint32_t pr = (p0 + j * kRunWaves) / g.npc;
-      r[j] = pad_rows[(int64_t)pr < d.cap ? pr : 0u];
-    });
-    static_for<kRunPadPieces>([&](auto j) {
-      const uint32_t p = p0 + j * kRunWaves;
-      if (p < live) {
-        const uint32_t c = p - (p / g.npc) * g.npc;
-        const int64_t v = (int64_t)(c * kWave + lane);
-        if (v < V)
-          store_row16<kScatterNtStore>(dst4 + (int64_t)r[j] * V + v, row16_t{0u, 0u, 0u, 0u});
-        if (c == 0 && dst_w != nullptr && lane == 0) dst_w[r[j]] = 0.0f;
+    const uint32_t bpx = g.tok_blocks / kRunXcds;
+    const uint32_t qn = (share + bpx - 1) / bpx;
+    const uint32_t k = tb / kRunXcds;
+    const uint32_t send = (x + 1) * share < all ? (x + 1) * share : all;
+    const uint32_t lo = x * share + k * qn;
+    const uint32_t hi = lo + qn < send ? lo + qn : send;
+    for (uint32_t p0 = lo + wv; p0 < hi; p0 += 2 * kRunWaves) {
+      const uint32_t p1 = p0 + kRunWaves;
+      const int32_t r0 = pad_rows[p0 / g.npc];
+      const int32_t r1 = pad_rows[(p1 < hi ? p1 : p0) / g.npc];
+      const uint32_t c0 = p0 - (p0 / g.npc) * g.npc;
+      const uint32_t c1 = p1 - (p1 / g.npc) * g.npc;
+      const int64_t v0 = (int64_t)(c0 * kWave + lane), v1 = (int64_t)(c1 * kWave + lane);
+      if (v0 < V)
+        store_row16<kScatterNtStore>(dst4 + (int64_t)r0 * V + v0, row16_t{0u, 0u, 0u, 0u});
+      if (c0 == 0 && dst_w != nullptr && lane == 0) dst_w[r0] = 0.0f;
+      if (p1 < hi) {
+        if (v1 < V)
+          store_row16<kScatterNtStore>(dst4 + (int64_t)r1 * V + v1, row16_t{0u, 0u, 0u, 0u});
+        if (c1 == 0 && dst_w != nullptr && lane == 0) dst_w[r1] = 0.0f;
       }
-    });
+    }
   }
 }
 
@@ -1514,29 +1504,22 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
 
 hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
                            const float* w, void* dst, float* dst_w, hipStream_t stream) {
+  if (d.T == 0) return hipSuccess;          // no route, so no row and no pad row
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t routes = d.T * (int64_t)d.K;
-  int64_t C = 1, nch = 0, tok_blocks = 0;
-  if (d.T > 0) {
-    C = run_chunk_tokens(d.T);
-    nch = (d.T + C - 1) / C;
-    // stream 0 holds the most chunks; a shorter stream's extra blocks exit
-    const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
-    const int64_t per_block = (int64_t)kRunWaves * kRunTokPieces;
-    tok_blocks = kRunXcds * ((entries * npc + per_block - 1) / per_block);
-  }
+  const int64_t C = run_chunk_tokens(d.T);
+  const int64_t nch = (d.T + C - 1) / C;
+  // stream 0 holds the most chunks; a shorter stream's extra blocks copy no
+  // token piece (they still zero their slice of the pads)
+  const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
+  const int64_t per_block = (int64_t)kRunWaves * kRunTokPieces;
+  const int64_t grid = kRunXcds * ((entries * npc + per_block - 1) / per_block);
   int64_t pad_rows_max = (int64_t)d.E * (d.A - 1);
   if (pad_rows_max > d.cap) pad_rows_max = d.cap;
-  const int64_t per_block = (int64_t)kRunWaves * kRunPadPieces;
-  int64_t pad_blocks = d.fill_pads ? (pad_rows_max * npc + per_block - 1) / per_block : 0;
-  pad_blocks = (pad_blocks + kRunXcds - 1) / kRunXcds * kRunXcds;    // as many per XCD
-  const int64_t grid = tok_blocks + pad_blocks;
-  if (grid == 0) return hipSuccess;
   // 32-bit indices: pieces of a stream and of the pads, entries, blocks
   const int64_t lim = (int64_t)1 << 31;
-  if (grid >= lim || tok_blocks * kRunWaves * kRunTokPieces >= lim ||
-      pad_blocks * per_block >= lim ||
-      routes * npc >= lim || nch * C * d.K >= lim) {
+  if (grid * per_block >= lim || routes * npc >= lim || nch * C * d.K >= lim ||
+      pad_rows_max * npc >= lim) {
     // a size no buffer in memory reaches; the scatter takes any size
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -1549,7 +1532,7 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   g.CK = (uint32_t)(C * d.K);
   g.nch = (uint32_t)nch;
   g.last_short = (uint32_t)(nch * C * d.K - routes);
-  g.tok_blocks = (uint32_t)tok_blocks;
+  g.tok_blocks = (uint32_t)grid;
   hipLaunchKernelGGL(run_rows_kernel, dim3((unsigned)grid), dim3(kRunWaves * kWave), 0, stream, d,
                      hv.header, hv.runs, hv.pad_rows, &hv.header->status, rows_in(src), w,
                      rows_out(dst), dst_w, g);
