@@ -125,6 +125,7 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
   out->offsets = hl.offsets;
   out->slot = hl.slot;
   out->row_src = hl.row_src;
+  out->runs = hl.runs;
   out->bytes = hl.bytes;
   return EP_OK;
 }

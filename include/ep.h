@@ -165,6 +165,12 @@ size_t ep_handle_mem_size(const ep_layout_t* layout);
  *   row_src  [recv_capacity]  route held by received row r, -1 for a pad row;
  *            entries at or past min(total, recv_capacity) are unspecified
  *   bytes    == ep_handle_mem_size(layout)
+ *   runs     [T*K] pairs (row, route): the run entries. The tokens are cut
+ *            into chunks of C = min(256, ceil(T/8)) consecutive tokens, and
+ *            chunk c owns entries [c*C*K, min((c+1)*C*K, T*K)): its routes
+ *            that hold a row, in ascending row order, then (-1, -1) for
+ *            its other routes. dispatch and combine_bwd read them under
+ *            EP_LAYOUT_DENSE_ROUTING.
  * Every offset is a multiple of 256. Host only. */
 typedef struct ep_handle_regions {
   size_t status;
@@ -173,6 +179,7 @@ typedef struct ep_handle_regions {
   size_t slot;
   size_t row_src;
   size_t bytes;
+  size_t runs;
 } ep_handle_regions_t;
 
 ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* out);

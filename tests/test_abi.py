@@ -62,6 +62,8 @@ def test_handle_size_and_regions():
     assert r.offsets + 4 * 257 <= r.slot
     assert r.slot + 4 * 4096 * 8 <= r.row_src
     assert r.row_src + 4 * L.cap <= n
+    assert r.runs % 256 == 0 and r.row_src + 4 * L.cap <= r.runs
+    assert r.runs + 8 * 4096 * 8 == n             # the run entries close the handle
     # the handle grows with the capacity and does not depend on H
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=512)) == n
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=7168, cap=L.cap * 2)) > n
