@@ -990,7 +990,6 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 #define EP_RUN_TOK_PIECES 4
 #endif
 
-
 constexpr int kRunWaves = 8;
 constexpr int kRunTokPieces = EP_RUN_TOK_PIECES;
 
