@@ -5,7 +5,8 @@ routings around the one-block prepare's cutover, masked, repeated and out-of-ran
 capacities, every payload type and both pad policies. Each case runs every
 op through the C ABI against the oracle, bit for bit (the weighted backward's
 weight gradient within its summation bound), with canaries in every output.
-The cases are drawn from a fixed seed, so the set is the same on every run.
+The cases are drawn from a fixed seed, so the set is the same on every run,
+and each runs twice: without and with the dense-routing hint.
 """
 import zlib
 
@@ -45,7 +46,7 @@ def _cases(n=24):
 
 @pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _cases(),
                          ids=lambda v: str(v) if not isinstance(v, str) else v)
-def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, dense=False):
     rng = np.random.default_rng(zlib.crc32(f"random-shape-{i}".encode()))
     if kind == "distinct":
         idx = np.argsort(rng.random((T, max(E, K))), axis=1)[:, :K] if T else \
@@ -60,7 +61,7 @@ def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind):
     idx = np.asarray(idx, np.int64).reshape(T, K)
     worst = T * K + E * (A - 1)
     cap = {"worst": worst, "tight": worst // 2, "zero": 0}[cap_kind]
-    run_case(f"random{i}", idx, E, A, H, cap, dt, fill, rng)
+    run_case(f"random{i}", idx, E, A, H, cap, dt, fill, rng, dense=dense)
 
 
 def _long_row_cases(n=8):
@@ -114,3 +115,12 @@ def _boundary_cases(n=12):
                          ids=lambda v: str(v) if not isinstance(v, str) else v)
 def test_random_boundaries(i, T, K, E, A, H, dt, fill, kind, cap_kind):
     test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind)
+
+
+@pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind",
+                         _cases() + _long_row_cases() + _boundary_cases(),
+                         ids=lambda v: str(v) if not isinstance(v, str) else v)
+def test_random_dense_routing(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+    """Every random case again with EP_LAYOUT_DENSE_ROUTING: the run-entry
+    copy, exact whether or not the routing masks routes."""
+    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, dense=True)
