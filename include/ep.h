@@ -194,8 +194,9 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
  *                                                expert_offsets[E] = total
  *   handle_mem      handle_bytes of device memory, fully (re)written here
  * After this call the handle holds, for the later ops, the received row of
- * every route (-1 if masked or dropped) and the source route of every live
- * received row (-1 for pads). Its status word is reset, then raises
+ * every route (-1 if masked or dropped), the source route of every live
+ * received row (-1 for pads) and the run entries (see ep_handle_regions),
+ * whatever the layout's flags. Its status word is reset, then raises
  * BAD_EXPERT / OVERFLOW as described above.
  */
 ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
