@@ -763,11 +763,16 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #ifndef EP_SCATTER_CH
 #define EP_SCATTER_CH 2
 #endif
+// The scatter's grid in the plain order (rows over 8 KiB), in blocks per CU.
+// The scatter serves routings with masked routes (dense ones take the
+// run-entry copy), and those copy fastest on this grid: measured on the
+// MI355X against 16 per CU, masked routing 5% and a hot-expert routing 8%
+// faster (a dense routing without the hint 8% slower).
 #ifndef EP_SCATTER_BLOCKS_PER_CU
-#define EP_SCATTER_BLOCKS_PER_CU 16
+#define EP_SCATTER_BLOCKS_PER_CU 64
 #endif
 // Rows of at most this many bytes take the interleaved unit order (token and
-// pad units spread evenly over the grid) and the wider grid below.
+// pad units spread evenly over the grid) and their own grid below.
 #ifndef EP_SCATTER_ILV_MAX_ROW
 #define EP_SCATTER_ILV_MAX_ROW 8192
 #endif
