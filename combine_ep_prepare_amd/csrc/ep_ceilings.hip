@@ -7,9 +7,10 @@
 // against what the memory system gives for the same access pattern, not
 // only against the 8 TB/s HBM peak.
 //
-// Every kernel moves 16-byte vectors with non-temporal loads and stores (the
-// policy of the routing kernels), one wavefront per piece and no grid-stride
-// loop, so that blocks are issued in address order:
+// Every kernel moves 16-byte vectors with non-temporal loads and with the
+// routing kernels' streaming stores (non-temporal, system scope: they write
+// through the L2), one wavefront per piece and no grid-stride loop, so that
+// blocks are issued in address order:
 //   write_linear   a dense write front: wavefront i zeroes bytes [1024 i, 1024 i + 1024)
 //   write_rows     the dispatch pattern: rows of `row_bytes` in a scrambled
 //                  order (row r -> r * 2654435761 mod nrows, nrows a power of
@@ -34,6 +35,14 @@ constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr uint32_t kScramble = 2654435761u;
 
+// The routing kernels' streaming store (cache-policy bits sc0 sc1 nt), with
+// the one wait state a 128-bit store needs before its data registers may be
+// overwritten.
+__device__ __forceinline__ void store_stream(vec4* p, vec4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 0" ::"v"(p), "v"(v)
+               : "memory");
+}
+
 __device__ __forceinline__ int64_t piece_index() {
   return (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
 }
@@ -42,7 +51,7 @@ __global__ void __launch_bounds__(kWavesPerBlock * kWave)
 write_linear_kernel(vec4* __restrict__ dst, int64_t pieces) {
   const int64_t p = piece_index();
   if (p >= pieces) return;
-  __builtin_nontemporal_store(vec4{0u, 0u, 0u, 0u}, dst + p * kWave + (threadIdx.x & (kWave - 1)));
+  store_stream(dst + p * kWave + (threadIdx.x & (kWave - 1)), vec4{0u, 0u, 0u, 0u});
 }
 
 __global__ void __launch_bounds__(kWavesPerBlock * kWave)
@@ -54,8 +63,8 @@ write_rows_kernel(vec4* __restrict__ dst, int64_t nrows, int64_t row_vecs, int64
   const int64_t rr = (int64_t)(((uint64_t)r * kScramble) & (uint64_t)(nrows - 1));
   const int64_t v = c * 2 * kWave + (threadIdx.x & (kWave - 1));
   vec4* row = dst + rr * row_vecs;
-  if (v < row_vecs) __builtin_nontemporal_store(vec4{0u, 0u, 0u, 0u}, row + v);
-  if (v + kWave < row_vecs) __builtin_nontemporal_store(vec4{0u, 0u, 0u, 0u}, row + v + kWave);
+  if (v < row_vecs) store_stream(row + v, vec4{0u, 0u, 0u, 0u});
+  if (v + kWave < row_vecs) store_stream(row + v + kWave, vec4{0u, 0u, 0u, 0u});
 }
 
 __global__ void __launch_bounds__(kWavesPerBlock * kWave)
@@ -71,7 +80,7 @@ copy_linear_kernel(const vec4* __restrict__ src, vec4* __restrict__ dst, int64_t
   const int64_t p = piece_index();
   if (p >= pieces) return;
   const int64_t i = p * kWave + (threadIdx.x & (kWave - 1));
-  __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  store_stream(dst + i, __builtin_nontemporal_load(src + i));
 }
 
 template <int K>
@@ -96,7 +105,7 @@ gather_sum_kernel(const vec4* __restrict__ rows, int64_t nrows, int64_t row_vecs
   vec4 acc = b[0];
 #pragma unroll
   for (int j = 1; j < K; ++j) acc += b[j];
-  if (live) __builtin_nontemporal_store(acc, out + t * row_vecs + v);
+  if (live) store_stream(out + t * row_vecs + v, acc);
 }
 
 int64_t blocks_for(int64_t pieces) { return (pieces + kWavesPerBlock - 1) / kWavesPerBlock; }
