@@ -820,9 +820,10 @@ __device__ __forceinline__ row16_t load_row16(const row16_t* p) {
 // Streaming stores write through the XCD's L2: non-temporal at system scope
 // (cache-policy bits sc0 sc1 nt of the CDNA3/CDNA4 vector memory
 // instructions). A plain non-temporal store (nt alone) leaves its lines
-// dirty in the L2 until they are evicted; measured on the MI355X, the dsv3
-// dispatch by run entries takes 118 µs with the write-through form against
-// 125 µs, with no change on the other ops. The compiler emits no such store
+// dirty in the L2 until they are evicted, where they push out rows that are
+// still to be read; measured on the MI355X, the dsv3 dispatch by run entries
+// takes 118 µs with the write-through form against 125 µs (its token rows
+// are then read from HBM once), and no op is slower. The compiler emits no such store
 // from C++, so it is written out; the s_nop gives the one wait state that a
 // 128-bit store needs before a VALU instruction may overwrite its data
 // registers, which the compiler does not insert after an asm statement.
