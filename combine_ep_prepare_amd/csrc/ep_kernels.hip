@@ -1068,12 +1068,25 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // order and each XCD's write fronts stay dense bands; measured on the
 // MI355X, contiguous runs of 128 KiB and more written this way reach
 // 6.5 TB/s against 5.1 TB/s for rows in scattered order.
-#ifndef EP_RUN_TOK_PIECES
-#define EP_RUN_TOK_PIECES 4
+//
+// P, the pieces per wavefront, depends on the row length and on the pad
+// fill. Measured on the MI355X with A/B runs on one device (dispatch /
+// combine_bwd µs), on two devices: rows of 14 KiB (dsv3) with the pad fill take
+// 119.6-124 / 124-129 at P = 4 and 118.5-119 / 114-115.6 at P = 3 (P = 2 and 5
+// are slower than both), 28 KiB rows (dsv3 in fp32) 231.5 against 226;
+// without the pad fill the same rows are 4 µs faster at P = 4; rows of 4 and
+// 8 KiB (qwen3, mixtral) are fastest at P = 4 and lose 3-7% at P = 3.
+#ifndef EP_RUN_PIECES_LONG
+#define EP_RUN_PIECES_LONG 3
+#endif
+#ifndef EP_RUN_PIECES_SHORT
+#define EP_RUN_PIECES_SHORT 4
 #endif
 
 constexpr int kRunWaves = 8;
-constexpr int kRunTokPieces = EP_RUN_TOK_PIECES;
+constexpr int kRunPiecesLong = EP_RUN_PIECES_LONG;    // rows of kRunLongRow pieces or more, pads filled
+constexpr int kRunPiecesShort = EP_RUN_PIECES_SHORT;  // the rest
+constexpr int64_t kRunLongRow = 12;                   // 1 KiB pieces
 
 // Sizes of a run-entry copy, computed on the host; every index of the launch
 // is below 2^32 (the launcher checks), so all index arithmetic is 32-bit and
@@ -1086,6 +1099,7 @@ struct RunGeom {
   uint32_t tok_blocks;  // blocks of the launch
 };
 
+template <int kRunTokPieces>
 __global__ void __launch_bounds__(kRunWaves * kWave)
 run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __restrict__ runs,
                 const int32_t* __restrict__ pad_rows, uint32_t* status,
@@ -1610,7 +1624,8 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   // stream 0 holds the most chunks; a shorter stream's extra blocks copy no
   // token piece (they still zero their slice of the pads)
   const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
-  const int64_t per_block = (int64_t)kRunWaves * kRunTokPieces;
+  const int P = npc >= kRunLongRow && d.fill_pads ? kRunPiecesLong : kRunPiecesShort;
+  const int64_t per_block = (int64_t)kRunWaves * P;
   const int64_t grid = kRunXcds * ((entries * npc + per_block - 1) / per_block);
   int64_t pad_rows_max = (int64_t)d.E * (d.A - 1);
   if (pad_rows_max > d.cap) pad_rows_max = d.cap;
@@ -1631,9 +1646,14 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   g.nch = (uint32_t)nch;
   g.last_short = (uint32_t)(nch * C * d.K - routes);
   g.tok_blocks = (uint32_t)grid;
-  hipLaunchKernelGGL(run_rows_kernel, dim3((unsigned)grid), dim3(kRunWaves * kWave), 0, stream, d,
-                     hv.header, hv.runs, hv.pad_rows, &hv.header->status, rows_in(src), w,
-                     rows_out(dst), dst_w, g);
+  if (P == kRunPiecesLong)
+    hipLaunchKernelGGL(run_rows_kernel<kRunPiecesLong>, dim3((unsigned)grid),
+                       dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                       &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
+  else
+    hipLaunchKernelGGL(run_rows_kernel<kRunPiecesShort>, dim3((unsigned)grid),
+                       dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                       &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
   return hipGetLastError();
 }
 

@@ -136,3 +136,16 @@ def test_dense_payload_types_and_pad_policy(dt, fill_pads, name, T, H):
     run_case(name + "-dense", r.topk_idx, c.E, c.A, H, cap, dt, fill_pads,
              np.random.default_rng(zlib.crc32(f"{name}{dt}{fill_pads}dense".encode())),
              dense=True)
+
+
+@pytest.mark.parametrize("fill_pads", [True, False])
+@pytest.mark.parametrize("T,H", [(1, 6144), (9, 6152), (300, 6144), (2049, 6152)])
+def test_dense_long_rows(T, H, fill_pads):
+    """Rows of 12 KiB and more, where the copy takes three pieces per wavefront
+    when it also fills the pads (four otherwise): 6144 is exactly 12 pieces,
+    6152 has a ragged 13th; token counts around the chunk boundaries."""
+    rng = np.random.default_rng(zlib.crc32(f"long{T}-{H}-{fill_pads}".encode()))
+    K, E, A = 8, 64, 16
+    idx = _edge_ids(rng, T, K, E, "uniform")
+    cap = T * K + E * (A - 1)
+    run_case(f"long-T{T}-H{H}", idx, E, A, H, cap, "bf16", fill_pads, rng, dense=True)
