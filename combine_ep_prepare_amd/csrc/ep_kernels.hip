@@ -1076,8 +1076,11 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // combine_bwd µs), on two devices: rows of 14 KiB (dsv3) with the pad fill take
 // 119.6-124 / 124-129 at P = 4 and 118.5-119 / 114-115.6 at P = 3 (P = 2 and 5
 // are slower than both), 28 KiB rows (dsv3 in fp32) 231.5 against 226;
-// without the pad fill the same rows are 4 µs faster at P = 4; rows of 4 and
-// 8 KiB (qwen3, mixtral) are fastest at P = 4 and lose 3-7% at P = 3.
+// without the pad fill the same rows are 4 µs faster at P = 4; rows of 8 KiB
+// (mixtral) are fastest at P = 4 and lose 3-7% at P = 3 or 6; rows of 4 KiB
+// (qwen3) take 58.4 / 54.7 at P = 6 against 60.1 / 56.3 at P = 4, while a
+// launch-bound routing of 1 KiB rows in 16 blocks (T = 256) loses 0.8 µs at
+// P = 6, so six pieces need a grid that fills the device.
 #ifndef EP_RUN_PIECES_LONG
 #define EP_RUN_PIECES_LONG 3
 #endif
@@ -1088,7 +1091,10 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 constexpr int kRunWaves = 8;
 constexpr int kRunPiecesLong = EP_RUN_PIECES_LONG;    // rows of kRunLongRow pieces or more, pads filled
 constexpr int kRunPiecesShort = EP_RUN_PIECES_SHORT;  // the rest
+constexpr int kRunPiecesNarrow = 6;                   // rows of kRunNarrowRow pieces or fewer, pads filled
 constexpr int64_t kRunLongRow = 12;                   // 1 KiB pieces
+constexpr int64_t kRunNarrowRow = 4;
+constexpr int64_t kRunNarrowMinBlocks = 2048;
 
 // Sizes of a run-entry copy, computed on the host; every index of the launch
 // is below 2^32 (the launcher checks), so all index arithmetic is 32-bit and
@@ -1626,7 +1632,13 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   // stream 0 holds the most chunks; a shorter stream's extra blocks copy no
   // token piece (they still zero their slice of the pads)
   const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
-  const int P = npc >= kRunLongRow && d.fill_pads ? kRunPiecesLong : kRunPiecesShort;
+  int P = !d.fill_pads ? kRunPiecesShort
+          : npc >= kRunLongRow ? kRunPiecesLong
+          : npc <= kRunNarrowRow ? kRunPiecesNarrow : kRunPiecesShort;
+  // narrow rows take six pieces only while the grid still fills the device
+  if (P == kRunPiecesNarrow &&
+      (entries * npc + kRunWaves * P - 1) / (kRunWaves * P) * kRunXcds < kRunNarrowMinBlocks)
+    P = kRunPiecesShort;
   const int64_t per_block = (int64_t)kRunWaves * P;
   const int64_t grid = kRunXcds * ((entries * npc + per_block - 1) / per_block);
   int64_t pad_rows_max = (int64_t)d.E * (d.A - 1);
@@ -1650,6 +1662,10 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   g.tok_blocks = (uint32_t)grid;
   if (P == kRunPiecesLong)
     hipLaunchKernelGGL(run_rows_kernel<kRunPiecesLong>, dim3((unsigned)grid),
+                       dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                       &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
+  else if (P == kRunPiecesNarrow)
+    hipLaunchKernelGGL(run_rows_kernel<kRunPiecesNarrow>, dim3((unsigned)grid),
                        dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                        &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
   else
