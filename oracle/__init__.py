@@ -22,9 +22,11 @@ _LIB = os.path.join(_HERE, "libep_oracle.so")
 STATUS_BAD_EXPERT = 1
 STATUS_OVERFLOW = 2
 
-# Plain scalar C: no fast-math, no contraction, IEEE binary32 via SSE.
+# Plain scalar C: no fast-math, no contraction, IEEE binary32 via SSE. OpenMP
+# shares the loops over received rows and over tokens among threads (see
+# set_threads); every result bit is the same on any thread count.
 CFLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-          "-fno-fast-math", "-msse2", "-mfpmath=sse", "-Wall", "-Werror"]
+          "-fno-fast-math", "-msse2", "-mfpmath=sse", "-fopenmp", "-Wall", "-Werror"]
 
 
 def build() -> str:
@@ -47,11 +49,11 @@ def _load():
         i64, i32, u32p, vp = C.c_int64, C.c_int32, C.POINTER(C.c_uint32), C.c_void_p
         lib.ep_oracle_prepare.argtypes = [i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, u32p]
         lib.ep_oracle_prepare.restype = C.c_int
-        lib.ep_oracle_dispatch.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64, i64, vp, vp,
-                                           vp, vp, vp]
+        lib.ep_oracle_dispatch.argtypes = [i64, i32, i64, C.c_int, C.c_int, C.c_int, i64,
+                                           i64, vp, vp, vp, vp, vp]
         lib.ep_oracle_dispatch.restype = C.c_int
-        lib.ep_oracle_combine_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64, i64, vp,
-                                              vp, vp]
+        lib.ep_oracle_combine_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int, C.c_int, i64,
+                                              i64, vp, vp, vp]
         lib.ep_oracle_combine_bwd.restype = C.c_int
         lib.ep_oracle_combine.argtypes = [i64, i32, i64, C.c_int, vp, vp, vp]
         lib.ep_oracle_combine.restype = C.c_int
@@ -59,8 +61,9 @@ def _load():
         lib.ep_oracle_dispatch_bwd.restype = C.c_int
         lib.ep_oracle_combine_weighted.argtypes = [i64, i32, i64, C.c_int, vp, vp, vp, vp]
         lib.ep_oracle_combine_weighted.restype = C.c_int
-        lib.ep_oracle_combine_weighted_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int, i64,
-                                                       i64, vp, vp, vp, vp, vp, vp, vp]
+        lib.ep_oracle_combine_weighted_bwd.argtypes = [i64, i32, i64, C.c_int, C.c_int,
+                                                       C.c_int, i64, i64, vp, vp, vp, vp, vp,
+                                                       vp, vp]
         lib.ep_oracle_combine_weighted_bwd.restype = C.c_int
         lib.ep_oracle_f16_to_f32.argtypes = [C.c_uint16]
         lib.ep_oracle_f16_to_f32.restype = C.c_float
@@ -72,6 +75,8 @@ def _load():
         lib.ep_oracle_bf16_to_f32.restype = C.c_float
         lib.ep_oracle_recv_capacity_worst.argtypes = [i64, i32, i32, i32]
         lib.ep_oracle_recv_capacity_worst.restype = i64
+        lib.ep_oracle_set_threads.argtypes = [C.c_int]
+        lib.ep_oracle_set_threads.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -105,6 +110,12 @@ class Prepared:
     @property
     def live(self) -> int:
         return min(self.total, self.cap)
+
+
+def set_threads(n: int = 0) -> int:
+    """Threads the oracle's row and token loops use from now on (n >= 1), or
+    none changed (n = 0); returns the count in force."""
+    return int(_load().ep_oracle_set_threads(int(n)))
 
 
 def recv_capacity_worst(T, K, E, A) -> int:
@@ -153,10 +164,10 @@ def prepare(topk_idx: np.ndarray, E: int, A: int, cap: int, fill: int = -7) -> P
 
 def dispatch(prep: Prepared, x: np.ndarray, w: np.ndarray | None,
              recv_init: np.ndarray | None = None, recv_w_init: np.ndarray | None = None,
-             dtype: str = "bf16", fill_pads: bool = True):
+             dtype: str = "bf16", fill_pads: bool = True, zero_tail: bool = False):
     """Returns (recv [cap,H], recv_w f32 [cap] or None). Rows past the live
-    total (and pad rows when fill_pads is False) keep the values of the
-    ``*_init`` arrays (zeros if not given)."""
+    total (unless zero_tail) and pad rows when fill_pads is False keep the
+    values of the ``*_init`` arrays (zeros if not given)."""
     x = _rows(x, dtype)
     T, H = x.shape
     st = DTYPES[dtype][1]
@@ -167,23 +178,23 @@ def dispatch(prep: Prepared, x: np.ndarray, w: np.ndarray | None,
         w = np.ascontiguousarray(w, dtype=np.float32)
         recv_w = (np.zeros(prep.cap, np.float32) if recv_w_init is None
                   else np.array(recv_w_init, dtype=np.float32, copy=True))
-    rc = _load().ep_oracle_dispatch(T, prep.K, H, DTYPES[dtype][0], int(fill_pads), prep.cap,
-                                    prep.total, _p(prep.row_src), _p(x), _p(w), _p(recv),
-                                    _p(recv_w))
+    rc = _load().ep_oracle_dispatch(T, prep.K, H, DTYPES[dtype][0], int(fill_pads),
+                                    int(zero_tail), prep.cap, prep.total, _p(prep.row_src),
+                                    _p(x), _p(w), _p(recv), _p(recv_w))
     _check(rc, "dispatch")
     return recv, recv_w
 
 
 def combine_bwd(prep: Prepared, g_result: np.ndarray, init: np.ndarray | None = None,
-                dtype: str = "bf16", fill_pads: bool = True):
+                dtype: str = "bf16", fill_pads: bool = True, zero_tail: bool = False):
     g_result = _rows(g_result, dtype)
     T, H = g_result.shape
     st = DTYPES[dtype][1]
     out = (np.zeros((prep.cap, H), st) if init is None
            else np.array(init, dtype=st, copy=True))
     rc = _load().ep_oracle_combine_bwd(T, prep.K, H, DTYPES[dtype][0], int(fill_pads),
-                                       prep.cap, prep.total, _p(prep.row_src), _p(g_result),
-                                       _p(out))
+                                       int(zero_tail), prep.cap, prep.total, _p(prep.row_src),
+                                       _p(g_result), _p(out))
     _check(rc, "combine_bwd")
     return out
 
@@ -231,10 +242,10 @@ def combine_weighted(prep: Prepared, rows: np.ndarray, w: np.ndarray, T: int | N
 
 def combine_weighted_bwd(prep: Prepared, g: np.ndarray, rows: np.ndarray | None,
                          w: np.ndarray, init: np.ndarray | None = None, dtype: str = "bf16",
-                         fill_pads: bool = True):
-    """(grad_rows [cap,H] with rows past the live total, and pad rows when
-    fill_pads is False, left at ``init``; grad_w float64 [cap] or None; sum of
-    |terms| float64 [cap] or None)."""
+                         fill_pads: bool = True, zero_tail: bool = False):
+    """(grad_rows [cap,H] with rows past the live total (unless zero_tail),
+    and pad rows when fill_pads is False, left at ``init``; grad_w float64
+    [cap] or None; sum of |terms| float64 [cap] or None)."""
     g = _rows(g, dtype)
     T, H = g.shape
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -247,7 +258,8 @@ def combine_weighted_bwd(prep: Prepared, g: np.ndarray, rows: np.ndarray | None,
         gw = np.zeros(prep.cap, np.float64)
         aw = np.zeros(prep.cap, np.float64)
     rc = _load().ep_oracle_combine_weighted_bwd(T, prep.K, H, DTYPES[dtype][0], int(fill_pads),
-                                                prep.cap, prep.total, _p(prep.row_src), _p(g),
-                                                _p(rows), _p(w), _p(grad_rows), _p(gw), _p(aw))
+                                                int(zero_tail), prep.cap, prep.total,
+                                                _p(prep.row_src), _p(g), _p(rows), _p(w),
+                                                _p(grad_rows), _p(gw), _p(aw))
     _check(rc, "combine_weighted_bwd")
     return grad_rows, gw, aw

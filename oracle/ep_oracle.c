@@ -7,8 +7,12 @@
  * and the benchmark's CPU-baseline leg may load it; the library itself never
  * calls it, and it shares no code, header or table with the library.
  *
- * Everything here is single-threaded scalar C, one loop per step of the
- * definition. Integer work is exact; the only floating point is an ordered
+ * Everything here is scalar C, one loop per step of the definition. When
+ * built with OpenMP, the loops over received rows and over tokens (each
+ * iteration writes outputs no other iteration touches, and every output's
+ * arithmetic stays inside one iteration) are shared among threads; prepare,
+ * a sequential counting sort, always runs on one thread. The thread count
+ * changes no result bit. Integer work is exact; the only floating point is an ordered
  * binary32 sum followed by one round-to-nearest-even to the payload type
  * (bf16, fp16 or fp32), and, for the weighted combine, products and fused
  * multiply-adds in binary32.
@@ -63,6 +67,13 @@
 #include <string.h>
 #include <xmmintrin.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#define ORACLE_PARALLEL_FOR _Pragma("omp parallel for schedule(static)")
+#else
+#define ORACLE_PARALLEL_FOR
+#endif
+
 #define ORACLE_STATUS_BAD_EXPERT 1u
 #define ORACLE_STATUS_OVERFLOW 2u
 
@@ -79,6 +90,18 @@ static int fpenv_is_ieee(void) {
   if (csr & (1u << 15)) return 0; /* FTZ */
   if (csr & (1u << 6)) return 0;  /* DAZ */
   return fegetround() == FE_TONEAREST;
+}
+
+/* Threads the row and token loops may use (the OpenMP default is every
+ * core); returns the count now in force, always 1 without OpenMP. */
+int ep_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }
 
 /* bf16 -> fp32: a bf16 value is the upper half of the binary32 pattern. */
@@ -278,20 +301,29 @@ int ep_oracle_prepare(int64_t T, int32_t K, int32_t E, int32_t A, int64_t cap,
  * dispatch (token part and weight part): received row r holds the token row
  * of the route it came from (a bit copy of its elements), or zeros for a pad
  * row (left as they are if fill_pads is 0). Rows at or past min(total, cap)
- * are not touched.
+ * are not touched, unless zero_tail is 1: then they are zeros too (the tail
+ * policy, under which the whole receive buffer is defined).
  *
  *   x        payload [T*H]  token rows
  *   w        f32  [T*K]     routing weights (may be NULL: then no weight output)
  *   recv     payload [cap*H]
  *   recv_w   f32  [cap]
  */
-int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads, int64_t cap,
-                       int64_t total, const int32_t* row_src, const void* x, const float* w,
-                       void* recv, float* recv_w) {
+int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads,
+                       int zero_tail, int64_t cap, int64_t total, const int32_t* row_src,
+                       const void* x, const float* w, void* recv, float* recv_w) {
   if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0 || !dtype_ok(dtype))
     return ORACLE_ERR_ARGS;
   const size_t eb = elem_bytes(dtype);
   const int64_t live = total < cap ? total : cap;
+  if (zero_tail) {
+    ORACLE_PARALLEL_FOR
+    for (int64_t r = live; r < cap; ++r) {
+      for (int64_t h = 0; h < H; ++h) store_zero(recv, r * H + h, dtype);
+      if (w && recv_w) recv_w[r] = 0.0f;
+    }
+  }
+  ORACLE_PARALLEL_FOR
   for (int64_t r = 0; r < live; ++r) {
     int32_t s = row_src[r];
     if (s >= 0) {
@@ -311,10 +343,10 @@ int ep_oracle_dispatch(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads
 /* combine_bwd is the same row map as dispatch's token part, applied to the
  * gradient of the combined output. */
 int ep_oracle_combine_bwd(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads,
-                          int64_t cap, int64_t total, const int32_t* row_src,
+                          int zero_tail, int64_t cap, int64_t total, const int32_t* row_src,
                           const void* g_result, void* g_expert_out) {
-  return ep_oracle_dispatch(T, K, H, dtype, fill_pads, cap, total, row_src, g_result, NULL,
-                            g_expert_out, NULL);
+  return ep_oracle_dispatch(T, K, H, dtype, fill_pads, zero_tail, cap, total, row_src,
+                            g_result, NULL, g_expert_out, NULL);
 }
 
 /*
@@ -328,6 +360,7 @@ int ep_oracle_combine(int64_t T, int32_t K, int64_t H, int dtype, const int32_t*
                       const void* rows, void* out) {
   if (T < 0 || K < 1 || H < 1 || !dtype_ok(dtype)) return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
+  ORACLE_PARALLEL_FOR
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t h = 0; h < H; ++h) {
       float acc = 0.0f;
@@ -365,6 +398,7 @@ int ep_oracle_dispatch_bwd(int64_t T, int32_t K, int64_t H, int dtype, const int
   int rc = ep_oracle_combine(T, K, H, dtype, slot, g_recv, grad_tokens);
   if (rc != ORACLE_OK) return rc;
   if (!grad_w) return ORACLE_OK;
+  ORACLE_PARALLEL_FOR
   for (int64_t s = 0; s < T * (int64_t)K; ++s) {
     int32_t r = slot[s];
     grad_w[s] = (r >= 0 && g_recv_w) ? g_recv_w[r] : 0.0f;
@@ -387,6 +421,7 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, int dtype, const
                                const void* rows, const float* w, void* out) {
   if (T < 0 || K < 1 || H < 1 || !dtype_ok(dtype)) return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
+  ORACLE_PARALLEL_FOR
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t h = 0; h < H; ++h) {
       float acc = 0.0f;
@@ -417,7 +452,9 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, int dtype, const
  * route s of token t = s / K:
  *   grad_rows[r, h] = payload(fp32(w[r] * g[t, h]))       (pads: +0)
  *   grad_w[r]       = sum over h of g[t, h] * rows[r, h]   (pads: +0)
- * Pads are left as they are when fill_pads is 0. The weight gradient is a
+ * Pads are left as they are when fill_pads is 0; rows at or past
+ * min(total, cap) are zeros when zero_tail is 1, else untouched. The weight
+ * gradient is a
  * dot product whose summation order the method does not fix; the oracle
  * returns it from a double-precision sum of the exact products (grad_w64)
  * together with the sum of their magnitudes (abs_dot64), and the tests
@@ -425,13 +462,23 @@ int ep_oracle_combine_weighted(int64_t T, int32_t K, int64_t H, int dtype, const
  * may be NULL (then rows is not read).
  */
 int ep_oracle_combine_weighted_bwd(int64_t T, int32_t K, int64_t H, int dtype, int fill_pads,
-                                   int64_t cap, int64_t total, const int32_t* row_src,
-                                   const void* g, const void* rows, const float* w,
-                                   void* grad_rows, double* grad_w64, double* abs_dot64) {
+                                   int zero_tail, int64_t cap, int64_t total,
+                                   const int32_t* row_src, const void* g, const void* rows,
+                                   const float* w, void* grad_rows, double* grad_w64,
+                                   double* abs_dot64) {
   if (T < 0 || K < 1 || H < 1 || cap < 0 || total < 0 || !dtype_ok(dtype))
     return ORACLE_ERR_ARGS;
   if (!fpenv_is_ieee()) return ORACLE_ERR_FPENV;
   const int64_t live = total < cap ? total : cap;
+  if (zero_tail) {
+    ORACLE_PARALLEL_FOR
+    for (int64_t r = live; r < cap; ++r) {
+      for (int64_t h = 0; h < H; ++h) store_zero(grad_rows, r * H + h, dtype);
+      if (grad_w64) grad_w64[r] = 0.0;
+      if (abs_dot64) abs_dot64[r] = 0.0;
+    }
+  }
+  ORACLE_PARALLEL_FOR
   for (int64_t r = 0; r < live; ++r) {
     int32_t s = row_src[r];
     if (s < 0) {

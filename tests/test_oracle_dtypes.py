@@ -296,3 +296,39 @@ def test_no_pad_fill_changes_only_pad_rows(dtype):
                                               fill_pads=False)
     check(gr, gr2)
     assert np.array_equal(gw[~pad], gw2[~pad])
+
+
+def test_thread_count_changes_no_bit():
+    # the OpenMP build shares the row and token loops among threads; one
+    # thread and every core must give the same bits for every op
+    import zlib
+    cfg = workloads.scaled(workloads.CONFIGS["qwen3"], T=700, H=256)
+    r = workloads.make_routing(cfg)
+    idx = r.topk_idx.copy()
+    idx[::3, 1] = -1
+    cap = oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A)
+    p = oracle.prepare(idx, cfg.E, cfg.A, cap)
+    rng = np.random.default_rng(zlib.crc32(b"threads"))
+    x = workloads.randn_bf16(rng, (cfg.T, cfg.H))
+    Y = workloads.randn_bf16(rng, (cap, cfg.H))
+    g = workloads.randn_bf16(rng, (cfg.T, cfg.H))
+    wr = rng.standard_normal(cap).astype(np.float32)
+    Gw = rng.standard_normal(cap).astype(np.float32)
+
+    def everything():
+        recv, recv_w = oracle.dispatch(p, x, r.topk_weights, zero_tail=True)
+        return [recv, recv_w.view(np.uint32), oracle.combine(p, Y),
+                oracle.combine_bwd(p, g), *oracle.dispatch_bwd(p, Y, Gw),
+                oracle.combine_weighted(p, Y, wr),
+                *oracle.combine_weighted_bwd(p, g, Y, wr)[:2]]
+
+    before = oracle.set_threads(0)
+    try:
+        assert oracle.set_threads(1) == 1
+        one = everything()
+        assert oracle.set_threads(max(2, os.cpu_count() or 2)) >= 2
+        many = everything()
+    finally:
+        oracle.set_threads(before)
+    for a, b in zip(one, many):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))

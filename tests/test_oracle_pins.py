@@ -508,3 +508,84 @@ def test_weighted_adjoints_exact_small_ints():
         s = p.row_src[rr]
         want = 0 if s < 0 else int(np.dot(gi[s // cfg.K], Yi[rr]))
         assert gw[rr] == want
+
+
+# --------------------------------------------------------------------------
+# the tail policy and the capacity bound
+# --------------------------------------------------------------------------
+
+def test_zero_tail_makes_adjoints_hold_over_the_whole_buffer():
+    # Combine never reads a row past the live total, so the gradient of such a
+    # row is zero: with the tail policy, <combine(Y), g> = <Y, combine_bwd(g)>
+    # over every row of the [cap,H] buffer even when that buffer started as
+    # garbage; without it the stale rows break the identity (the check has
+    # teeth). The same holds for dispatch and for the weighted pair.
+    cfg = workloads.scaled(workloads.CONFIGS["qwen3"], T=150, H=16)
+    r = workloads.make_routing(cfg)
+    idx = r.topk_idx.copy()
+    idx[::4, 2] = -1
+    cap = oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A)
+    p = oracle.prepare(idx, cfg.E, cfg.A, cap)
+    assert p.live < cap
+    rng = np.random.default_rng(21)
+    Y = workloads.small_int_bf16(rng, (cap, cfg.H), 8)
+    g = workloads.small_int_bf16(rng, (cfg.T, cfg.H), 8)
+    garbage = workloads.small_int_bf16(rng, (cap, cfg.H), 8)
+    lhs = pins.dot_f64(_f32_of(oracle.combine(p, Y)), _f32_of(g))
+    gy = oracle.combine_bwd(p, g, init=garbage, zero_tail=True)
+    assert (gy[p.live:] == 0).all()
+    assert pins.dot_f64(_f32_of(Y), _f32_of(gy)) == lhs
+    stale = oracle.combine_bwd(p, g, init=garbage, zero_tail=False)
+    assert pins.dot_f64(_f32_of(Y), _f32_of(stale)) != lhs
+    # dispatch: <D x, G> over the whole buffer equals <x, D^T G>
+    x = workloads.small_int_bf16(rng, (cfg.T, cfg.H), 8)
+    w = rng.integers(-4, 5, size=(cfg.T, cfg.K)).astype(np.float32)
+    G = workloads.small_int_bf16(rng, (cap, cfg.H), 8)
+    Gw = rng.integers(-4, 5, size=cap).astype(np.float32)
+    recv, recv_w = oracle.dispatch(p, x, w, recv_init=garbage,
+                                   recv_w_init=np.full(cap, 3.0, np.float32), zero_tail=True)
+    assert (recv[p.live:] == 0).all() and (recv_w[p.live:] == 0).all()
+    gt, gw = oracle.dispatch_bwd(p, G, Gw)
+    assert (pins.dot_f64(_f32_of(recv), _f32_of(G)) + pins.dot_f64(recv_w, Gw) ==
+            pins.dot_f64(_f32_of(x), _f32_of(gt)) + pins.dot_f64(w, gw))
+    # weighted pair: <combine_w(Y), g> = <Y, dY> = <w, dw> over every row
+    wr = rng.integers(-4, 5, size=cap).astype(np.float32)
+    lhs_w = pins.dot_f64(_f32_of(oracle.combine_weighted(p, Y, wr)), _f32_of(g))
+    gr, gw64, _ = oracle.combine_weighted_bwd(p, g, Y, wr, init=garbage, zero_tail=True)
+    assert (gr[p.live:] == 0).all() and (gw64[p.live:] == 0).all()
+    assert pins.dot_f64(_f32_of(Y), _f32_of(gr)) == lhs_w
+    assert float(np.dot(wr.astype(np.float64), gw64)) == lhs_w
+
+
+@pytest.mark.parametrize("T,K,E,A,want", [
+    (4096, 8, 256, 128, 4096 * 8 + 256 * 127),
+    (10, 8, 4, 1, 40),        # K > E: a token reaches at most E distinct experts
+    (3, 5, 2, 3, 3 * 2 + 2 * 2),
+    (7, 1, 1, 1, 7),          # A = 1: no pad row ever
+    (0, 8, 32, 128, 32 * 127),
+])
+def test_capacity_bound_hand_values(T, K, E, A, want):
+    assert oracle.recv_capacity_worst(T, K, E, A) == want
+
+
+@pytest.mark.parametrize("T,K,E,A", [(4, 8, 4, 3), (7, 2, 5, 4), (5, 3, 3, 1), (1, 6, 6, 2)])
+def test_capacity_bound_is_attained(T, K, E, A):
+    # A routing that reaches the bound exactly: every token routes to min(K,E)
+    # distinct experts (the rest masked), spread so that each expert's count
+    # leaves it A-1 pad rows whenever T*min(K,E) allows. The bound is tight
+    # from both sides: at the bound nothing overflows, and one row less
+    # overflows whenever the routing fills it.
+    m = min(K, E)
+    idx = np.full((T, K), -1, np.int64)
+    for t in range(T):
+        for j in range(m):
+            idx[t, j] = (t + j) % E
+    cap = oracle.recv_capacity_worst(T, K, E, A)
+    p = oracle.prepare(idx, E, A, cap)
+    assert p.status == 0
+    counts = np.bincount(idx[idx >= 0], minlength=E)
+    total = int(((counts + A - 1) // A * A).sum())
+    assert p.total == total <= cap
+    if all(c % A == 1 % A for c in counts) and A > 1:
+        assert total == cap
+        assert oracle.prepare(idx, E, A, cap - 1).status & oracle.STATUS_OVERFLOW
