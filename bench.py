@@ -77,9 +77,13 @@ PREPARE_KERNELS = ("prepare_hist_kernel", "prepare_slots_kernel", "prepare_fused
                    "prepare_runs_kernel")
 
 
+COLD = "@cold"      # suffix of the launches timed after a cache flush
+
+
 def kernel_of(op: str, dense: bool) -> str:
     """The library kernel that runs ``op`` (dispatch and combine_bwd take the
-    run-entry copy on a dense routing)."""
+    run-entry copy on a dense routing); a cold launch runs the op's kernel."""
+    op = op[:-len(COLD)] if op.endswith(COLD) else op
     if dense and op in DENSE_OPS:
         return "run_rows_kernel"
     return KERNEL_OF_OP[op]
@@ -254,7 +258,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
            " --schedule-out <dir>/schedule.json   (once with FETCH_SIZE, once with "
            "WRITE_SIZE); then python bench.py --summarize-pmc <fetch dir> <write dir> "
            f"--workload {workload} --calibration-copy-mib {copy_mib}")
-    for op in KERNEL_OF_OP:
+    for op in KERNEL_OF_OP:                    # warm launches only
         fb = res["FETCH_SIZE"]["per_op_bytes"].get(op)
         wb = res["WRITE_SIZE"]["per_op_bytes"].get(op)
         if fb is None or wb is None:
@@ -322,17 +326,19 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
         f.write(f"{'op':24s} {'kernel':22s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
                 f"{'max_us':>9s}\n")
         for op, v in list(per_op.items()) + list(prep.items()):
-            kern = kernel_of(op, dense) if op in KERNEL_OF_OP else op
+            kern = kernel_of(op, dense) if op.replace(COLD, "") in KERNEL_OF_OP else op
             f.write(f"{op:24s} {kern:22s} {len(v):6d} {np.mean(v):9.2f} {np.min(v):9.2f} "
                     f"{np.max(v):9.2f}\n")
     print(path, flush=True)
 
 
-def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
-    """The oracle as it stands, single-threaded, on the same inputs: whole
-    steps repeated until the time budget is spent (at least one)."""
+def cpu_baseline(cfg, r, host, cap, budget_s=12.0, threads=1):
+    """The oracle as it stands on the same inputs, its row and token loops on
+    ``threads`` threads (0: the OpenMP default, every core it is given):
+    whole steps repeated until the time budget is spent (at least one).
+    Returns (dispatch s, combine s, steps, seconds spent, threads used)."""
     import oracle
-    oracle.build()
+    used = oracle.set_threads(threads)
     t_d = t_c = 0.0
     n = 0
     start = time.perf_counter()
@@ -350,7 +356,7 @@ def cpu_baseline(cfg, r, host, cap, budget_s=12.0):
         n += 1
         if time.perf_counter() - start > budget_s:
             break
-    return t_d / n, t_c / n, n, time.perf_counter() - start
+    return t_d / n, t_c / n, n, time.perf_counter() - start, used
 
 
 def _ceilings_lib():
@@ -365,8 +371,9 @@ def _ceilings_lib():
     lib.epc_read_linear.argtypes = [vp, i64, vp, vp]
     lib.epc_copy_linear.argtypes = [vp, vp, i64, vp]
     lib.epc_gather_sum.argtypes = [vp, i64, i64, i64, C.c_int, vp, vp]
+    lib.epc_flush.argtypes = [vp, vp, i64, vp, vp]
     for name in ("epc_write_linear", "epc_write_rows", "epc_read_linear", "epc_copy_linear",
-                 "epc_gather_sum"):
+                 "epc_gather_sum", "epc_flush"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -442,7 +449,15 @@ def main():
                     help="skip timing the ops outside the step")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip timing the memory-pattern ceilings")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of CPU oracle work per thread setting (all cores, one)")
+    ap.add_argument("--cold-steps", type=int, default=None,
+                    help="steps timed with the caches flushed before every op "
+                         "(default: --steps; 0 skips them)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written, then MiB of another buffer read, before each cold op")
+    ap.add_argument("--headline", choices=("warm", "cold"), default="warm",
+                    help="which timing protocol `value` reports")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     ap.add_argument("--schedule-out", metavar="FILE",
@@ -569,6 +584,44 @@ def main():
     p10 = {op: float(np.percentile(v, 10)) for op, v in per_op_ms.items()}
     p90 = {op: float(np.percentile(v, 90)) for op, v in per_op_ms.items()}
 
+    # Cold: the same five ops, each preceded on the same stream (no host gap)
+    # by a flush that writes one buffer and then reads another, each larger
+    # than the 256 MB Infinity Cache, with plain cache-allocating accesses. The
+    # op then finds none of its inputs in the L2s or the Infinity Cache, and
+    # no dirty line of the op before it is left to write back meanwhile.
+    cold_steps = args.steps if args.cold_steps is None else args.cold_steps
+    cold_avg = cold_med = None
+    if cold_steps > 0:
+        clib = _ceilings_lib()
+        fbytes = args.flush_mib << 20
+        fl_a = torch.empty(fbytes, dtype=torch.uint8, device=dev)
+        fl_b = torch.zeros(fbytes, dtype=torch.uint8, device=dev)
+        fl_sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
+        sp = stream.cuda_stream
+
+        def flush():
+            assert clib.epc_flush(fl_a.data_ptr(), fl_b.data_ptr(), fbytes,
+                                  fl_sink.data_ptr(), sp) == 0
+
+        cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in step_fns] for _ in range(cold_steps)]
+        torch.cuda.synchronize()
+        for i in range(cold_steps):
+            for j, (op, fn) in enumerate(step_fns):
+                flush()
+                cev[i][j][0].record(stream)
+                if op != "prepare":
+                    schedule.append(op + COLD)
+                fn()
+                cev[i][j][1].record(stream)
+        torch.cuda.synchronize()
+        assert ep.read_status(handle) == 0, "unexpected status bits"
+        cold_ms = {op: [cev[i][j][0].elapsed_time(cev[i][j][1]) for i in range(cold_steps)]
+                   for j, (op, _) in enumerate(step_fns)}
+        cold_avg = {op: float(np.mean(v)) for op, v in cold_ms.items()}
+        cold_med = {op: float(np.median(v)) for op, v in cold_ms.items()}
+        del fl_a, fl_b, fl_sink
+
     # The same step captured once in a HIP graph and replayed: the GPU time of
     # the five ops without the host's launch gaps (what a small, launch-bound
     # routing costs inside a captured layer). Not under the profiler's launch
@@ -674,7 +727,30 @@ def main():
         return nb / (avg[op] * 1e-3) / 1e9
 
     pair_bytes = nbytes["dispatch"] + nbytes["combine"]
-    pair_s = (avg["dispatch"] + avg["combine"]) * 1e-3
+    warm_pair_s = (avg["dispatch"] + avg["combine"]) * 1e-3
+    warm = {"pair_GBps": round(pair_bytes / warm_pair_s / 1e9, 1),
+            "pct_of_peak": round(100 * pair_bytes / warm_pair_s / 1e9 / HBM_PEAK_GBS, 2),
+            "dispatch_us": round(avg["dispatch"] * 1e3, 2),
+            "combine_us": round(avg["combine"] * 1e3, 2),
+            "protocol": "ops back to back inside whole steps"}
+    cold = None
+    if cold_avg is not None:
+        cold_pair_s = (cold_avg["dispatch"] + cold_avg["combine"]) * 1e-3
+        cold = {"pair_GBps": round(pair_bytes / cold_pair_s / 1e9, 1),
+                "pct_of_peak": round(100 * pair_bytes / cold_pair_s / 1e9 / HBM_PEAK_GBS, 2),
+                "dispatch_us": round(cold_avg["dispatch"] * 1e3, 2),
+                "combine_us": round(cold_avg["combine"] * 1e3, 2),
+                "protocol": f"each op after a flush ({args.flush_mib} MiB written, then "
+                            f"{args.flush_mib} MiB of another buffer read, same stream)",
+                "steps": cold_steps,
+                "ops": {op: {"avg_us": round(cold_avg[op] * 1e3, 2),
+                             "median_us": round(cold_med[op] * 1e3, 2),
+                             "GBps": (round(nbytes[op] / (cold_avg[op] * 1e-3) / 1e9, 1)
+                                      if op != "prepare" else None)}
+                        for op in STEP_OPS}}
+    if args.headline == "cold" and cold is None:
+        raise SystemExit("--headline cold needs --cold-steps > 0")
+    pair_s = cold_pair_s if args.headline == "cold" else warm_pair_s
     value = pair_bytes / pair_s / 1e9
     dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
                    key=lambda op: avg[op])
@@ -707,12 +783,22 @@ def main():
             "g_recv": g_recv.view(torch.int16).cpu().numpy().view(np.uint16),
             "g_recv_w": g_recv_w.cpu().numpy(),
         }
-        td, tc, n, spent = cpu_baseline(cfg, r, host, cap, args.cpu_budget)
+        import oracle
+        oracle.build()
+        default_threads = oracle.set_threads(0)
+        td, tc, n, spent, used = cpu_baseline(cfg, r, host, cap, args.cpu_budget, 0)
+        td1, tc1, n1, spent1, _ = cpu_baseline(cfg, r, host, cap, args.cpu_budget, 1)
+        oracle.set_threads(default_threads)
         cpu = {"value": round(pair_bytes / (td + tc) / 1e9, 3), "unit": "GB/s",
-               "cores": 1, "kind": "oracle",
+               "cores": used, "kind": "oracle",
                "sample": f"{n} whole step(s) of the {cfg.name} workload (all five ops, "
-                         f"same inputs) by the single-threaded C oracle, {spent:.1f} s; "
-                         f"dispatch {td * 1e3:.1f} ms, combine {tc * 1e3:.1f} ms per step",
+                         f"same inputs) by the C oracle with its row and token loops on "
+                         f"{used} OpenMP threads, {spent:.1f} s; dispatch {td * 1e3:.1f} ms, "
+                         f"combine {tc * 1e3:.1f} ms per step",
+               "single_thread": {"value": round(pair_bytes / (td1 + tc1) / 1e9, 3),
+                                 "unit": "GB/s", "cores": 1,
+                                 "sample": f"{n1} whole step(s), {spent1:.1f} s; dispatch "
+                                           f"{td1 * 1e3:.1f} ms, combine {tc1 * 1e3:.1f} ms"},
                "host_cpu_count": os.cpu_count()}
 
     line = {
@@ -734,6 +820,9 @@ def main():
                    "dense_routing": dense},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / pair_s, 1),
+        "value_is": args.headline,
+        "warm": warm,
+        "cold": cold,
         "ops": {op: {"avg_us": round(avg[op] * 1e3, 2), "median_us": round(med[op] * 1e3, 2),
                      "p10_us": round(p10[op] * 1e3, 2), "p90_us": round(p90[op] * 1e3, 2),
                      "algorithmic_bytes": nbytes[op],

@@ -18,14 +18,16 @@ arrives here as None and is passed to the library as NULL (the weight
 gradient is then zero), the case the pages' review flagged (section
 "Greptile Summary").
 
-Rows at or past the live total (``routing.expert_offsets[E]``) of the
-receive buffer are never written, and neither are the same rows of the
-gradient that ``combine`` passes back: both hold unspecified values. Pad rows
-below the total are zero (with ``fill_pads=False`` they are unwritten too). An expert function that treats rows independently,
-or works on expert segments taken from ``expert_offsets``, is unaffected; one
-that mixes rows (a parameter shared across the whole buffer, a reduction over
-it) must slice the buffer to its live rows first, or its parameter gradients
-pick up those values.
+Every expert-major buffer these ops allocate is defined in full: rows at or
+past the live total (``routing.expert_offsets[E]``) of the receive buffer,
+of its weights and of the gradients passed back by ``combine`` are zeros
+(the library's tail policy, LAYOUT_ZERO_TAIL; combine never reads those rows,
+so zero is their exact gradient), and so are pad rows below the total. An
+expert function applied to the whole buffer (a parameter shared by every
+row, a reduction over it) therefore gets exact parameter gradients. With
+``EpRouting(..., zero_tail=False)`` the tail is left unwritten (one zero
+write per tail row saved) and such a function must slice the buffer to its
+live rows first; with ``fill_pads=False`` pad rows are unwritten too.
 """
 from __future__ import annotations
 
@@ -45,11 +47,12 @@ class EpRouting:
     fp16 and fp32 payloads; ``fill_pads=False`` leaves pad rows unwritten;
     ``dense=True`` states that ``topk_idx`` holds no masked route (-1), which
     lets dispatch and its backward copy rows in received-row order (faster;
-    the results are the same either way)."""
+    the results are the same either way); ``zero_tail=False`` leaves the rows
+    past the live total unwritten."""
 
     def __init__(self, topk_idx: torch.Tensor, num_experts: int, alignment: int, hidden: int,
                  recv_capacity: Optional[int] = None, fill_pads: bool = True,
-                 dense: bool = False):
+                 dense: bool = False, zero_tail: bool = True):
         if topk_idx.dtype != torch.int64:
             raise TypeError("topk_idx must be int64")
         T, K = topk_idx.shape
@@ -58,6 +61,7 @@ class EpRouting:
         self._dims = (T, K, num_experts, alignment, hidden, recv_capacity)
         self.fill_pads = fill_pads
         self.dense = dense
+        self.zero_tail = zero_tail
         self._layouts = {}
         self.layout = self.layout_for(torch.bfloat16)
         self.handle = new_handle(self.layout, device=topk_idx.device)
@@ -71,7 +75,7 @@ class EpRouting:
         """The layout of this routing for payloads of ``dtype``."""
         if dtype not in self._layouts:
             self._layouts[dtype] = Layout(*self._dims, dtype=dtype, fill_pads=self.fill_pads,
-                                          dense=self.dense)
+                                          dense=self.dense, zero_tail=self.zero_tail)
         return self._layouts[dtype]
 
 
@@ -155,7 +159,7 @@ class _CombineWeighted(torch.autograd.Function):
 
 def dispatch(tokens: torch.Tensor, topk_weights: torch.Tensor, routing: EpRouting):
     """(recv_tokens [cap,H], recv_topk_weights [cap]); rows past the live total
-    are unspecified."""
+    are zeros (unless the routing was made with ``zero_tail=False``)."""
     return _Dispatch.apply(tokens, topk_weights, routing)
 
 

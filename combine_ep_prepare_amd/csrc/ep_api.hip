@@ -31,7 +31,8 @@ ep_status_t check_layout(const ep_layout_t* L) {
   if (L->alignment < 1) return EP_ERR_SHAPE;
   if (L->dtype != EP_DTYPE_BF16 && L->dtype != EP_DTYPE_FP16 && L->dtype != EP_DTYPE_FP32)
     return EP_ERR_SHAPE;
-  if ((L->flags & ~(uint32_t)(EP_LAYOUT_NO_PAD_FILL | EP_LAYOUT_DENSE_ROUTING)) != 0)
+  if ((L->flags &
+       ~(uint32_t)(EP_LAYOUT_NO_PAD_FILL | EP_LAYOUT_DENSE_ROUTING | EP_LAYOUT_ZERO_TAIL)) != 0)
     return EP_ERR_SHAPE;
   if (L->hidden < 8 || L->hidden % 8 != 0 || L->hidden >= kInt32Limit) return EP_ERR_SHAPE;
   const int64_t routes = L->num_tokens * (int64_t)L->topk;
@@ -76,6 +77,7 @@ Dims dims_of(const ep_layout_t* L, int32_t num_units) {
   d.dtype = L->dtype;
   d.fill_pads = (L->flags & EP_LAYOUT_NO_PAD_FILL) ? 0 : 1;
   d.dense = (L->flags & EP_LAYOUT_DENSE_ROUTING) ? 1 : 0;
+  d.zero_tail = (L->flags & EP_LAYOUT_ZERO_TAIL) ? 1 : 0;
   return d;
 }
 
@@ -165,7 +167,7 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
   // A buffer with no element may be NULL: tokens/topk_weights when T == 0,
   // recv_tokens/recv_topk_weights when recv_capacity == 0.
   const bool rows = d.cap > 0, toks = d.T > 0;
-  if ((rows && !recv_tokens) || (rows && toks && !tokens)) return EP_ERR_NULL;
+  if ((rows && !recv_tokens) || (toks && !tokens)) return EP_ERR_NULL;
   if (rows && toks && (topk_weights == nullptr) != (recv_topk_weights == nullptr))
     return EP_ERR_NULL;
   if (!aligned16(tokens) || !aligned16(recv_tokens)) return EP_ERR_ALIGN;
@@ -188,7 +190,7 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
   int num_cus = 0;
   ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
-  if (d.T > 0 && (!result || (d.cap > 0 && !expert_out))) return EP_ERR_NULL;
+  if ((d.T > 0 && !result) || (d.cap > 0 && !expert_out)) return EP_ERR_NULL;
   if (!aligned16(expert_out) || !aligned16(result)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
@@ -207,7 +209,7 @@ ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
   int num_cus = 0;
   ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
-  if (d.T > 0 && (!grad_tokens || (d.cap > 0 && !grad))) return EP_ERR_NULL;
+  if ((d.T > 0 && !grad_tokens) || (d.cap > 0 && !grad)) return EP_ERR_NULL;
   if (!aligned16(grad) || !aligned16(grad_tokens)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
@@ -225,7 +227,7 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
   int num_cus = 0;
   ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
-  if (d.cap > 0 && (!grad_expert_out || (d.T > 0 && !grad))) return EP_ERR_NULL;
+  if ((d.cap > 0 && !grad_expert_out) || (d.T > 0 && !grad)) return EP_ERR_NULL;
   if (!aligned16(grad) || !aligned16(grad_expert_out)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
@@ -246,7 +248,7 @@ ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_me
   int num_cus = 0;
   ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
-  if (d.T > 0 && (!result || (d.cap > 0 && (!expert_out || !recv_topk_weights))))
+  if ((d.T > 0 && !result) || (d.cap > 0 && (!expert_out || !recv_topk_weights)))
     return EP_ERR_NULL;
   if (!aligned16(expert_out) || !aligned16(result)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
@@ -270,9 +272,9 @@ ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handl
   int num_cus = 0;
   ep_status_t st = payload_common(layout, handle_mem, handle_bytes, &d, &hv);
   if (st != EP_OK) return st;
+  if (d.T > 0 && !grad) return EP_ERR_NULL;
   if (d.cap > 0) {
     if (!grad_expert_out || !recv_topk_weights) return EP_ERR_NULL;
-    if (d.T > 0 && !grad) return EP_ERR_NULL;
     if (grad_recv_topk_weights && !expert_out) return EP_ERR_NULL;
   }
   if (!aligned16(grad) || !aligned16(expert_out) || !aligned16(grad_expert_out))

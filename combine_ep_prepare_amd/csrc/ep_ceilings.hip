@@ -20,6 +20,10 @@
 //                  sink that is written only under a condition that does not
 //                  hold for the zero-filled input)
 //   copy_linear    dense read and write fronts, 1 KiB per wavefront
+//   flush          not a pattern: plain (cache-allocating) stores over one
+//                  buffer, then plain loads over a second one, so that the
+//                  L2s and the Infinity Cache end up holding clean lines of
+//                  the second buffer and nothing a following kernel uses
 //   gather_sum     the combine pattern: for each of `ntok` tokens and each
 //                  1 KiB column block, k rows picked by a multiplicative
 //                  hash of (token, k) are read and summed as 32-bit integers,
@@ -81,6 +85,21 @@ copy_linear_kernel(const vec4* __restrict__ src, vec4* __restrict__ dst, int64_t
   if (p >= pieces) return;
   const int64_t i = p * kWave + (threadIdx.x & (kWave - 1));
   store_stream(dst + i, __builtin_nontemporal_load(src + i));
+}
+
+__global__ void __launch_bounds__(kWavesPerBlock * kWave)
+write_plain_kernel(vec4* __restrict__ dst, int64_t pieces) {
+  const int64_t p = piece_index();
+  if (p >= pieces) return;
+  dst[p * kWave + (threadIdx.x & (kWave - 1))] = vec4{(uint32_t)p, 0u, 0u, 0u};
+}
+
+__global__ void __launch_bounds__(kWavesPerBlock * kWave)
+read_plain_kernel(const vec4* __restrict__ src, int64_t pieces, vec4* __restrict__ sink) {
+  const int64_t p = piece_index();
+  if (p >= pieces) return;
+  const vec4 v = src[p * kWave + (threadIdx.x & (kWave - 1))];
+  if ((v.x ^ v.y ^ v.z ^ v.w) == 0x9E3779B9u) sink[threadIdx.x & (kWave - 1)] = v;
 }
 
 template <int K>
@@ -169,6 +188,23 @@ int epc_copy_linear(const void* src, void* dst, int64_t bytes, hipStream_t strea
   if (blocks == 0) return 0;
   hipLaunchKernelGGL(copy_linear_kernel, dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
                      stream, static_cast<const vec4*>(src), static_cast<vec4*>(dst), pieces);
+  return finish(blocks);
+}
+
+// Evicts the caches: plain stores over `a`, then plain loads over `b` (both
+// `bytes` long, a multiple of 1024; sink: 1 KiB). Two launches on `stream`.
+int epc_flush(void* a, const void* b, int64_t bytes, void* sink, hipStream_t stream) {
+  const int64_t pieces = bytes / 1024;
+  const int64_t blocks = blocks_for(pieces);
+  if (a == nullptr || b == nullptr || sink == nullptr || bytes % 1024 != 0 ||
+      blocks > kMaxBlocks)
+    return 2;
+  if (blocks == 0) return 0;
+  hipLaunchKernelGGL(write_plain_kernel, dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
+                     stream, static_cast<vec4*>(a), pieces);
+  if (hipGetLastError() != hipSuccess) return 1;
+  hipLaunchKernelGGL(read_plain_kernel, dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
+                     stream, static_cast<const vec4*>(b), pieces, static_cast<vec4*>(sink));
   return finish(blocks);
 }
 

@@ -85,6 +85,28 @@ __device__ __forceinline__ bool handle_matches(const HandleHeader& hh, const Dim
          (hh.total >= 0) & (hh.pads_live >= 0);
 }
 
+// Rows a payload op writes as zeros, in this order: the live pad rows
+// (pad_rows[0, npads), ascending) when pads are filled, then the rows past the
+// live total (live .. cap-1) when the tail is zeroed.
+struct ZeroRows {
+  int64_t npads;  // pad rows among them
+  int64_t n;      // all of them
+  int64_t live;   // min(total, cap): the first tail row
+};
+
+__device__ __forceinline__ ZeroRows zero_rows_of(const HandleHeader& hh, const Dims& d) {
+  ZeroRows z;
+  z.live = (int64_t)hh.total < d.cap ? (int64_t)hh.total : d.cap;
+  z.npads = d.fill_pads ? (int64_t)hh.pads_live : 0;
+  z.n = z.npads + (d.zero_tail ? d.cap - z.live : 0);
+  return z;
+}
+
+__device__ __forceinline__ int64_t zero_row(const ZeroRows& z,
+                                            const int32_t* __restrict__ pad_rows, int64_t i) {
+  return i < z.npads ? (int64_t)pad_rows[i] : z.live + (i - z.npads);
+}
+
 // fp32 -> bf16 bits, round to nearest even; any NaN -> 0x7FC0. Adding
 // 0x7FFF plus the lowest kept bit carries into the kept half exactly when the
 // discarded half is above one half ulp, or equal to it with an odd kept half.
@@ -997,7 +1019,8 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
   const int64_t npc = (V + kWave - 1) / kWave;           // 1 KiB pieces per row
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t tok_units = (d.T + G - 1) / G * ncb;
-  const int64_t pad_pieces = d.fill_pads ? (int64_t)hh.pads_live * npc : 0;
+  const ZeroRows zr = zero_rows_of(hh, d);
+  const int64_t pad_pieces = zr.n * npc;
   const int64_t n_units = tok_units + (pad_pieces + kScatterWaves - 1) / kScatterWaves;
   const bool weights = w != nullptr && dst_w != nullptr;
   const int64_t routes = d.T * (int64_t)K;
@@ -1049,9 +1072,9 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       if (pi >= pad_pieces) continue;
       const int64_t p = udiv(pi, npc);
       const int64_t c = pi - p * npc;
-      const int32_t r = pad_rows[p];
+      const int64_t r = zero_row(zr, pad_rows, p);
       const int64_t v = c * kWave + lane;
-      if (v < V) store_row16<kScatterNtStore>(dst4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
+      if (v < V) store_row16<kScatterNtStore>(dst4 + r * V + v, row16_t{0u, 0u, 0u, 0u});
       if (c == 0 && dst_w != nullptr && lane == 0) dst_w[r] = 0.0f;
     }
   }
@@ -1164,13 +1187,14 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
       if (ent[j].row >= 0 && col[j] == 0) dst_w[ent[j].row] = w[ent[j].route];
     });
   }
-  if (d.fill_pads) {
-    // Pads: the live pad pieces are split into kRunXcds contiguous shares and
-    // share x is split over stream x's blocks in order, so the pads of each
-    // XCD are zeroed as one dense band alongside its token runs (two pieces
-    // per wavefront and step). A routing has pad rows only if some route is
-    // valid, so T > 0 and these blocks exist whenever pads do.
-    const uint32_t all = (uint32_t)hh.pads_live * g.npc;
+  if (d.fill_pads || d.zero_tail) {
+    // Zero rows (the live pads, and the tail under the tail policy): their
+    // pieces are split into kRunXcds contiguous shares and share x is split
+    // over stream x's blocks in order, so the zeros of each XCD are written
+    // as one dense band alongside its token runs (two pieces per wavefront
+    // and step). The launch has blocks whenever T > 0.
+    const ZeroRows zr = zero_rows_of(hh, d);
+    const uint32_t all = (uint32_t)zr.n * g.npc;
     const uint32_t share = (all + kRunXcds - 1) / kRunXcds;
     const uint32_t bpx = g.tok_blocks / kRunXcds;
     const uint32_t qn = (share + bpx - 1) / bpx;
@@ -1180,17 +1204,16 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
     const uint32_t hi = lo + qn < send ? lo + qn : send;
     for (uint32_t p0 = lo + wv; p0 < hi; p0 += 2 * kRunWaves) {
       const uint32_t p1 = p0 + kRunWaves;
-      const int32_t r0 = pad_rows[p0 / g.npc];
-      const int32_t r1 = pad_rows[(p1 < hi ? p1 : p0) / g.npc];
+      const int64_t r0 = zero_row(zr, pad_rows, p0 / g.npc);
+      const int64_t r1 = zero_row(zr, pad_rows, (p1 < hi ? p1 : p0) / g.npc);
       const uint32_t c0 = p0 - (p0 / g.npc) * g.npc;
       const uint32_t c1 = p1 - (p1 / g.npc) * g.npc;
       const int64_t v0 = (int64_t)(c0 * kWave + lane), v1 = (int64_t)(c1 * kWave + lane);
-      if (v0 < V)
-        store_row16<kScatterNtStore>(dst4 + (int64_t)r0 * V + v0, row16_t{0u, 0u, 0u, 0u});
+      if (v0 < V) store_row16<kScatterNtStore>(dst4 + r0 * V + v0, row16_t{0u, 0u, 0u, 0u});
       if (c0 == 0 && dst_w != nullptr && lane == 0) dst_w[r0] = 0.0f;
       if (p1 < hi) {
         if (v1 < V)
-          store_row16<kScatterNtStore>(dst4 + (int64_t)r1 * V + v1, row16_t{0u, 0u, 0u, 0u});
+          store_row16<kScatterNtStore>(dst4 + r1 * V + v1, row16_t{0u, 0u, 0u, 0u});
         if (c1 == 0 && dst_w != nullptr && lane == 0) dst_w[r1] = 0.0f;
       }
     }
@@ -1403,7 +1426,8 @@ weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
   const int64_t npc = (V + kWave - 1) / kWave;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t n_groups = (d.T + G - 1) / G;
-  const int64_t pad_pieces = d.fill_pads ? (int64_t)hh.pads_live * npc : 0;
+  const ZeroRows zr = zero_rows_of(hh, d);
+  const int64_t pad_pieces = zr.n * npc;
   const int64_t n_units = n_groups + (pad_pieces + kBwdWaves - 1) / kBwdWaves;
   const int64_t routes = d.T * (int64_t)K;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
@@ -1458,9 +1482,9 @@ weighted_bwd_kernel(Dims d, const HandleHeader* __restrict__ h,
       if (pi >= pad_pieces) continue;
       const int64_t p = pi / npc;
       const int64_t c = pi - p * npc;
-      const int32_t r = pad_rows[p];
+      const int64_t r = zero_row(zr, pad_rows, p);
       const int64_t v = c * kWave + lane;
-      if (v < V) store_row16<kScatterNtStore>(o4 + (int64_t)r * V + v, row16_t{0u, 0u, 0u, 0u});
+      if (v < V) store_row16<kScatterNtStore>(o4 + r * V + v, row16_t{0u, 0u, 0u, 0u});
       if (WANT_W && c == 0 && lane == 0) grad_w[r] = 0.0f;
     }
   }
@@ -1607,8 +1631,9 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
   const int64_t ncb = (d.V + CB - 1) / CB;
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t G = kWave / d.K;
-  const int64_t max_units = (d.T + G - 1) / G * ncb +
-                            (d.fill_pads ? (d.cap * npc + kScatterWaves - 1) / kScatterWaves : 0);
+  const int64_t max_units =
+      (d.T + G - 1) / G * ncb +
+      (d.fill_pads || d.zero_tail ? (d.cap * npc + kScatterWaves - 1) / kScatterWaves : 0);
   if (max_units == 0) return hipSuccess;
   const bool interleave = d.V * (int64_t)sizeof(row16_t) <= kScatterIlvMaxRow;
   int64_t grid = max_units;
@@ -1624,7 +1649,17 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
 
 hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
                            const float* w, void* dst, float* dst_w, hipStream_t stream) {
-  if (d.T == 0) return hipSuccess;          // no route, so no row and no pad row
+  // no token: no route, so no row and no pad row (a zeroed tail needs a grid
+  // the run entries do not size; the scatter takes it); no capacity: nothing
+  // to write
+  if (d.T == 0 || d.cap == 0) {
+    if (d.cap == 0 || !d.zero_tail) return hipSuccess;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    return launch_scatter_rows(d, hv, src, w, dst, dst_w, cus, stream);
+  }
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t routes = d.T * (int64_t)d.K;
   const int64_t C = run_chunk_tokens(d.T);
@@ -1641,7 +1676,7 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
     P = kRunPiecesShort;
   const int64_t per_block = (int64_t)kRunWaves * P;
   const int64_t grid = kRunXcds * ((entries * npc + per_block - 1) / per_block);
-  int64_t pad_rows_max = (int64_t)d.E * (d.A - 1);
+  int64_t pad_rows_max = d.zero_tail ? d.cap : (int64_t)d.E * (d.A - 1);
   if (pad_rows_max > d.cap) pad_rows_max = d.cap;
   // 32-bit indices: pieces of a stream and of the pads, entries, blocks
   const int64_t lim = (int64_t)1 << 31;
@@ -1706,8 +1741,9 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
                                int num_cus, hipStream_t stream) {
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t G = kWave / d.K;
-  const int64_t max_units = (d.T + G - 1) / G +
-                            (d.fill_pads ? (d.cap * npc + kBwdWaves - 1) / kBwdWaves : 0);
+  const int64_t max_units =
+      (d.T + G - 1) / G +
+      (d.fill_pads || d.zero_tail ? (d.cap * npc + kBwdWaves - 1) / kBwdWaves : 0);
   if (max_units == 0) return hipSuccess;
   int64_t grid = max_units;
   const int64_t limit = (int64_t)num_cus * EP_BWD_BLOCKS_PER_CU;

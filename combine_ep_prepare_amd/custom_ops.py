@@ -20,7 +20,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 from torch import Tensor
 
-from . import (DTYPE_BF16, LAYOUT_DENSE_ROUTING, LAYOUT_NO_PAD_FILL, TORCH_DTYPE, Layout,
+from . import (DTYPE_BF16, LAYOUT_DENSE_ROUTING, LAYOUT_NO_PAD_FILL, LAYOUT_ZERO_TAIL,
+               TORCH_DTYPE, Layout,
                combine as _combine,
                combine_bwd as _combine_bwd, combine_weighted as _combine_weighted,
                combine_weighted_bwd as _combine_weighted_bwd, dispatch as _dispatch,
@@ -35,10 +36,14 @@ def layout_list(layout: Layout) -> List[int]:
             int(layout.dtype), int(layout.flags)]
 
 
-def _layout(ll: Sequence[int]) -> Layout:
+def _layout(ll: Sequence[int], zero_tail: bool = False) -> Layout:
+    """The layout of a list; ``zero_tail`` adds LAYOUT_ZERO_TAIL, which every
+    op below that allocates an expert-major output sets, so that its rows past
+    the live total are zeros rather than uninitialised memory."""
     T, K, E, A, H, cap, dt, flags = ll
     return Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=not (flags & LAYOUT_NO_PAD_FILL),
-                  dense=bool(flags & LAYOUT_DENSE_ROUTING))
+                  dense=bool(flags & LAYOUT_DENSE_ROUTING),
+                  zero_tail=zero_tail or bool(flags & LAYOUT_ZERO_TAIL))
 
 
 def _pdtype(ll: Sequence[int]) -> torch.dtype:
@@ -74,8 +79,8 @@ def _(topk_idx, handle, layout):
 def dispatch(tokens: Tensor, topk_weights: Tensor, handle: Tensor,
              layout: List[int]) -> Tuple[Tensor, Tensor]:
     """(recv_tokens [cap,H], recv_topk_weights fp32 [cap]); rows past the live
-    total are unspecified."""
-    L = _layout(layout)
+    total are zeros."""
+    L = _layout(layout, zero_tail=True)
     recv = torch.empty(L.cap, L.H, dtype=tokens.dtype, device=tokens.device)
     recv_w = torch.empty(L.cap, dtype=torch.float32, device=tokens.device)
     _dispatch(L, handle, tokens, topk_weights, recv, recv_w)
@@ -147,8 +152,8 @@ def _(expert_out, handle, layout):
 def combine_bwd(grad: Tensor, handle: Tensor, layout: List[int]) -> Tensor:
     """grad_expert_out [cap,H]: each live row takes its token's gradient; pad
     rows zero (unless the layout skips the pad fill); rows past the live total
-    unspecified."""
-    L = _layout(layout)
+    zero (combine never reads them)."""
+    L = _layout(layout, zero_tail=True)
     out = torch.empty(L.cap, L.H, dtype=grad.dtype, device=grad.device)
     _combine_bwd(L, handle, grad, out)
     return out
@@ -195,8 +200,9 @@ def _(expert_out, recv_topk_weights, handle, layout):
 @torch.library.custom_op(f"{NS}::combine_weighted_bwd", mutates_args=())
 def combine_weighted_bwd(grad: Tensor, expert_out: Tensor, recv_topk_weights: Tensor,
                          handle: Tensor, layout: List[int]) -> Tuple[Tensor, Tensor]:
-    """(grad_expert_out [cap,H], grad_recv_topk_weights fp32 [cap])."""
-    L = _layout(layout)
+    """(grad_expert_out [cap,H], grad_recv_topk_weights fp32 [cap]); rows past
+    the live total zero in both."""
+    L = _layout(layout, zero_tail=True)
     gr = torch.empty(L.cap, L.H, dtype=grad.dtype, device=grad.device)
     gw = torch.empty(L.cap, dtype=torch.float32, device=grad.device)
     _combine_weighted_bwd(L, handle, grad, expert_out, recv_topk_weights, gr, gw)

@@ -40,7 +40,8 @@
  *  - All pointers are device pointers unless stated otherwise. Payload
  *    pointers must be 16-byte aligned and H must be a multiple of 8. A
  *    pointer to a buffer with no element (T == 0 for [T,...] buffers,
- *    recv_capacity == 0 for [recv_capacity,...] buffers) may be NULL.
+ *    recv_capacity == 0 for [recv_capacity,...] buffers) may be NULL; every
+ *    other required pointer must not be, whatever the other sizes are.
  *  - Work is enqueued on `stream` and nothing waits for it: no call below
  *    synchronises, allocates, frees or keeps a pointer after it returns,
  *    except ep_read_status, which waits for the stream. The caller owns
@@ -103,8 +104,19 @@ enum {
  * routing maps: one prepared handle serves both policies. */
 enum {
   EP_LAYOUT_NO_PAD_FILL = 1u,
-  EP_LAYOUT_DENSE_ROUTING = 2u
+  EP_LAYOUT_DENSE_ROUTING = 2u,
+  EP_LAYOUT_ZERO_TAIL = 4u
 };
+
+/* EP_LAYOUT_ZERO_TAIL: the payload ops that write expert-major rows
+ * (ep_dispatch's rows and weights, ep_combine_bwd's rows, and the weighted
+ * backward's rows and weight gradients) also write +0 to every row at or past
+ * min(total, recv_capacity), so that the whole [recv_capacity,...] buffer is
+ * defined. This is the library's own addition: combine never reads those
+ * rows, so their gradient is zero, and a caller that applies one function to
+ * the whole receive buffer (a parameter shared by every row, a reduction
+ * over it) then sees zeros there instead of stale memory. It costs one
+ * zero write per tail row. */
 
 /* EP_LAYOUT_DENSE_ROUTING: the caller states that every entry of topk_idx is
  * a valid expert id (no -1 masks), as when all of a layer's experts are local.

@@ -97,8 +97,8 @@ def test_bad_layouts_rejected(kw, code):
 
 @pytest.mark.parametrize("dtype,flags,ok", [
     (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True), (0, 2, True),
-    (1, 3, True), (3, 0, False), (0xFFFF, 0, False), (0, 4, False), (0, 6, False),
-    (0, 0x8001, False),
+    (1, 3, True), (0, 4, True), (2, 7, True), (3, 0, False), (0xFFFF, 0, False),
+    (0, 8, False), (0, 12, False), (0, 0x8001, False),
 ])
 def test_payload_type_and_flags_validated(dtype, flags, ok):
     L = lay()
@@ -106,8 +106,8 @@ def test_payload_type_and_flags_validated(dtype, flags, ok):
     L.flags = flags
     n = ep.handle_mem_size(L)
     if ok:
-        # neither the payload type, the pad policy nor the dense-routing hint
-        # changes the handle
+        # neither the payload type, the pad and tail policies nor the
+        # dense-routing hint changes the handle
         assert n == ep.handle_mem_size(lay())
     else:
         assert n == 0
@@ -226,3 +226,38 @@ def test_weighted_entry_points_error_paths():
     assert cwb(C.byref(L), P, n, MIS, P2, P2, P2, P2, None) == ep.EP_ERR_ALIGN
     assert cwb(C.byref(L), P, n, P, MIS, P2, P2, P2, None) == ep.EP_ERR_ALIGN
     assert cwb(C.byref(L), P, n, P, P2, P2, MIS, P2, None) == ep.EP_ERR_ALIGN
+
+
+@pytest.mark.parametrize("flags", [0, 2, 4])
+def test_token_buffers_required_even_without_receive_rows(flags):
+    """A [T,...] buffer may be NULL only when T == 0: with tokens but no
+    receive capacity the token-side pointers are still required, and the
+    call fails before any HIP call (no kernel could read through them)."""
+    L = lay(T=16, cap=0)
+    L.flags = flags
+    n = ep.handle_mem_size(L)
+    assert n > 0
+    # dispatch: tokens NULL, receive buffers NULL (allowed: cap == 0)
+    assert ep.lib.ep_dispatch(C.byref(L), P, n, None, None, None, None, None) == \
+        ep.EP_ERR_NULL
+    # combine_bwd: gradient of the result NULL
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, n, None, None, None) == ep.EP_ERR_NULL
+    # combine / dispatch_bwd: the [T,H] output NULL
+    assert ep.lib.ep_combine(C.byref(L), P, n, None, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, n, None, None, None, None, None) == \
+        ep.EP_ERR_NULL
+    # weighted backward: the [T,H] gradient NULL
+    assert ep.lib.ep_combine_weighted_bwd(C.byref(L), P, n, None, None, None, None, None,
+                                          None) == ep.EP_ERR_NULL
+
+
+def test_receive_buffers_required_without_tokens():
+    """With recv_capacity > 0 the [recv_capacity,...] inputs are required even
+    when T == 0."""
+    L = lay(T=0, cap=64)
+    n = ep.handle_mem_size(L)
+    assert ep.lib.ep_combine(C.byref(L), P, n, None, None, None) == ep.EP_ERR_NULL
+    assert ep.lib.ep_dispatch_bwd(C.byref(L), P, n, None, None, None, None, None) == \
+        ep.EP_ERR_NULL
+    assert ep.lib.ep_combine_weighted(C.byref(L), P, n, None, None, None, None) == \
+        ep.EP_ERR_NULL

@@ -1,6 +1,6 @@
 """Host-side checks of the memory-pattern ceiling library (no GPU needed).
 
-- it loads and exports its five entry points;
+- it loads and exports its entry points (five patterns and the cache flush);
 - every size it does not take is refused with 2 before any HIP call (each
   case fails validation, so the fake device addresses are never used);
 - the benchmark's pattern sizes fit the buffers it allocates.
@@ -12,7 +12,7 @@ import pytest
 import bench
 
 NAMES = ("epc_write_linear", "epc_write_rows", "epc_read_linear", "epc_copy_linear",
-         "epc_gather_sum")
+         "epc_gather_sum", "epc_flush")
 P = C.c_void_p(0x10000)
 P2 = C.c_void_p(0x20000)
 S = C.c_void_p(0)
@@ -40,6 +40,10 @@ def test_sizes_it_does_not_take_are_refused():
     assert lib.epc_gather_sum(P, 0, 1024, 4, 2, P2, S) == 2
     assert lib.epc_gather_sum(P, 16, 1000, 4, 2, P2, S) == 2
     assert lib.epc_gather_sum(None, 16, 1024, 4, 2, P2, S) == 2
+    assert lib.epc_flush(None, P2, 1024, P, S) == 2
+    assert lib.epc_flush(P, None, 1024, P, S) == 2
+    assert lib.epc_flush(P, P2, 1024, None, S) == 2
+    assert lib.epc_flush(P, P2, 1000, P, S) == 2
 
 
 @pytest.mark.parametrize("T,K,H", [(4096, 8, 7168), (32768, 8, 7168), (8192, 8, 2048),

@@ -181,3 +181,45 @@ def test_payload_types_through_autograd(dt):
     o_gt, _ = oracle.dispatch_bwd(p, h(recv.grad), None, want_grad_w=False, dtype=dt)
     assert np.array_equal(bits(h(xt.grad)), bits(o_gt))
     assert wt.grad is not None and wt.grad.shape == (cfg.T, cfg.K)
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_shared_expert_over_whole_buffer_gets_exact_grads(weighted):
+    # One Linear-style expert applied to the whole [cap,H] receive buffer (a
+    # parameter shared by every row). Its weight gradient sums over all rows,
+    # so it is only right if every row the routing does not fill (pads and
+    # the tail past the live total) carries zeros forward and a zero
+    # gradient back. The buffers are allocated uninitialised and filled with
+    # NaN beforehand, so stale memory would show. The reference takes the
+    # live rows only.
+    cfg, r, idx, x, w = _setup(name="masked", T=900, H=256, seed=3)
+    torch.cuda.synchronize()
+    junk = torch.full((1 << 24,), float("nan"), device="cuda")   # poison the allocator's
+    del junk                                                      # free blocks with NaN
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H)
+    cap = routing.layout.cap
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    W = (torch.randn(cfg.H, cfg.H, generator=gen, device="cuda") / 16).requires_grad_(True)
+    recv, recv_w = epa.dispatch(x, w, routing)
+    h = (recv.float() @ W).to(torch.bfloat16)                   # the shared expert
+    y = epa.combine(h, routing, recv_w if weighted else None)
+    g = workloads.randn_bf16_torch((cfg.T, cfg.H), 78)
+    (y.float() * g.float()).sum().backward()
+    assert torch.isfinite(W.grad).all()
+    live = int(routing.expert_offsets[-1].item())
+    assert live < cap                   # the worst-case buffer has a tail
+    # reference: the same expert on the live rows only, in fp32 on the CPU
+    recv_l = recv.detach()[:live].float().cpu()
+    W_c = W.detach().cpu()
+    h_l = (recv_l @ W_c).to(torch.bfloat16).requires_grad_(True)
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, cap)
+    # d(sum(y*g))/dh on the live rows: combine_bwd of g (weighted: times w)
+    gh = torch.from_numpy(oracle.combine_bwd(p, host_bf16(g))[:live].view(np.int16)).view(
+        torch.bfloat16).float()
+    if weighted:
+        gh = (gh * recv_w.detach()[:live].cpu()[:, None]).to(torch.bfloat16).float()
+    want = recv_l.t() @ gh
+    got = W.grad.cpu()
+    # the same products; only the summation order of the two GEMMs differs
+    assert torch.allclose(got, want, rtol=1e-3, atol=1e-3 * want.abs().max().item())

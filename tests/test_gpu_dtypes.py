@@ -98,11 +98,13 @@ def gamma(H, dt):
     return n * u / (1 - n * u)
 
 
-def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense=False):
+def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense=False,
+             zero_tail=False):
     T, K = idx.shape
-    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} dense={dense} T={T} K={K} E={E} "
-        f"A={A} H={H} cap={cap}")
-    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads, dense=dense)
+    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} dense={dense} zero_tail={zero_tail} "
+        f"T={T} K={K} E={E} A={A} H={H} cap={cap}")
+    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads, dense=dense,
+                  zero_tail=zero_tail)
     handle = ep.new_handle(L)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ep.prepare(L, torch.from_numpy(idx).cuda(), counts, handle)
@@ -116,7 +118,7 @@ def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense
     Gw = rng.standard_normal(cap).astype(np.float32)
     rw = rng.standard_normal(cap).astype(np.float32)
     xd, Yd, gd, Gd = dev(x, dt), dev(Y, dt), dev(g, dt), dev(G, dt)
-    kw = dict(dtype=dt, fill_pads=fill_pads)
+    kw = dict(dtype=dt, fill_pads=fill_pads, zero_tail=zero_tail)
 
     # dispatch
     recv, recv_w = canary_rows(cap, H, dt), canary_w(cap)
@@ -165,7 +167,7 @@ def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense
         assert (err <= gamma(H, dt) * o_abs[tok] + 1e-45).all(), f"{label} weighted_bwd w"
         want_pad = 0.0 if fill_pads else float(CANARY_W)
         assert (got[pad] == want_pad).all()
-        assert (got[live:] == float(CANARY_W)).all()
+        assert (got[live:] == (0.0 if zero_tail else float(CANARY_W))).all()
     assert ep.read_status(handle) == p.status
 
 
@@ -220,15 +222,17 @@ def test_payload_type_special_values(dt):
              np.random.default_rng(77), specials=True)
 
 
-@pytest.mark.parametrize("dt", ["fp16", "fp32"])
-def test_full_size_dsv3_dispatch_combine(dt):
-    # the DeepSeek-V3-shaped workload at full size: dispatch and combine
+@pytest.mark.parametrize("dt,dense", [("fp16", False), ("fp32", False), ("fp32", True)])
+def test_full_size_dsv3_dispatch_combine(dt, dense):
+    # the DeepSeek-V3-shaped workload at full size: dispatch, combine and
+    # combine_bwd, by the scatter and (with the dense-routing hint, as the
+    # benchmark times fp32 dispatch) by the run-entry copy
     cfg = workloads.CONFIGS["dsv3"]
     r = workloads.make_routing(cfg)
     T, K, E, A, H = cfg.T, cfg.K, cfg.E, cfg.A, cfg.H
     cap = oracle.recv_capacity_worst(T, K, E, A)
-    log(f"dtypes full dsv3 {dt}: T={T} H={H} cap={cap}")
-    L = ep.Layout(T, K, E, A, H, cap, dtype=dt)
+    log(f"dtypes full dsv3 {dt} dense={dense}: T={T} H={H} cap={cap}")
+    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, dense=dense)
     handle = ep.new_handle(L)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ep.prepare(L, torch.from_numpy(r.topk_idx).cuda(), counts, handle)
@@ -240,7 +244,47 @@ def test_full_size_dsv3_dispatch_combine(dt):
     got = host(recv, dt)
     want, _ = oracle.dispatch(p, x, None, recv_init=canary_host(cap, H, dt), dtype=dt)
     assert np.array_equal(bits(got), bits(want))
+    del recv, got, want
     Y = payload(rng, (cap, H), dt)
     out = canary_rows(T, H, dt)
     ep.combine(L, handle, dev(Y, dt), out)
     assert np.array_equal(bits(host(out, dt)), bits(oracle.combine(p, Y, dtype=dt)))
+    del Y, out
+    g = payload(rng, (T, H), dt)
+    gx = canary_rows(cap, H, dt)
+    ep.combine_bwd(L, handle, dev(g, dt), gx)
+    want = oracle.combine_bwd(p, g, init=canary_host(cap, H, dt), dtype=dt)
+    assert np.array_equal(bits(host(gx, dt)), bits(want))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("dense", [False, True])
+@pytest.mark.parametrize("fill_pads", [True, False])
+@pytest.mark.parametrize("name,T,H", [("masked", 1500, 512), ("dsv3", 200, 1024)])
+def test_zero_tail_parity(dt, dense, fill_pads, name, T, H):
+    # the tail policy: rows past the live total of every expert-major output
+    # are zeros (canaries elsewhere where the pad policy leaves rows alone),
+    # on both copy paths, with and without the pad fill
+    c = workloads.scaled(workloads.CONFIGS[name], T=T, H=H)
+    r = workloads.make_routing(c)
+    cap = oracle.recv_capacity_worst(T, c.K, c.E, c.A)
+    run_case(f"{name}-tail", r.topk_idx, c.E, c.A, H, cap, dt, fill_pads,
+             np.random.default_rng(zlib.crc32(f"{name}{dt}{dense}{fill_pads}".encode())),
+             dense=dense, zero_tail=True)
+
+
+def test_zero_tail_without_tokens():
+    # T = 0: every row is past the live total (which is 0)
+    L = ep.Layout(0, 4, 8, 16, 64, 300, zero_tail=True)
+    handle = ep.new_handle(L)
+    counts = torch.empty(8, dtype=torch.int32, device="cuda")
+    ep.prepare(L, torch.empty(0, 4, dtype=torch.int64, device="cuda"), counts, handle)
+    recv, recv_w = canary_rows(300, 64, "bf16"), canary_w(300)
+    ep.dispatch(L, handle, torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(0, 4, device="cuda"), recv, recv_w)
+    gx = canary_rows(300, 64, "bf16")
+    ep.combine_bwd(L, handle, torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), gx)
+    torch.cuda.synchronize()
+    assert (host(recv, "bf16") == 0).all() and (recv_w.cpu().numpy() == 0).all()
+    assert (host(gx, "bf16") == 0).all()
+    assert ep.read_status(handle) == 0

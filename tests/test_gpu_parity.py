@@ -70,12 +70,10 @@ def test_parity_full_size(name):
     r = workloads.make_routing(cfg)
     p = oracle.prepare(r.topk_idx, cfg.E, cfg.A,
                        oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A))
-    # the benchmark sizes its receive buffers to the worst case, except for
-    # the masked workloads whose worst case (every route local) is 7.6x the
-    # live rows; those use the live total rounded up, as a caller knowing its
-    # slice would
-    cap = p.cap if cfg.local_slice is None else (p.total + 4095) // 4096 * 4096
-    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A, cap)
+    # the receive buffers at the worst-case capacity, as the benchmark sizes
+    # them (for the masked workloads 7.6x the live rows: most of the buffer
+    # is tail, which must keep its canary)
+    cap = p.cap
     log(f"{name}-full: prepare T={cfg.T} H={cfg.H} cap={cap} total={p.total}")
     run = GpuRun(r.topk_idx, cfg.E, cfg.A, cfg.H, cap)
     run.prepare()
@@ -88,6 +86,36 @@ def test_parity_full_size(name):
     g_recv_w = np.random.default_rng(15).standard_normal(cap, dtype=np.float32)
     check_all_ops(run, p, host["x"], r.topk_weights, host["rows"], host["g_result"],
                   host["g_recv"], g_recv_w, label=f"{name}-full", dev=dev)
+
+
+def test_masked_local_slice_as_subset_of_global_experts():
+    # The masked workload's local slice [0,32) of 256 experts: prepared with
+    # E = 32 and with E = 256 on the GPU, every route lands in the same row,
+    # the 224 experts past the slice get empty segments, and dispatch writes
+    # the same receive buffer.
+    cfg = workloads.scaled(workloads.CONFIGS["masked"], T=4096, H=1024)
+    r = workloads.make_routing(cfg)
+    x = workloads.make_tokens(cfg)
+    cap32 = oracle.recv_capacity_worst(cfg.T, cfg.K, 32, cfg.A)
+    cap256 = cap32 + 224 * (cfg.A - 1)
+    out = {}
+    for E, cap in ((32, cap32), (256, cap256)):
+        run = GpuRun(r.topk_idx, E, cfg.A, cfg.H, cap)
+        run.prepare()
+        p = oracle.prepare(r.topk_idx, E, cfg.A, cap)
+        check_prepare(run, p)
+        recv, recv_w = run.dispatch(dev_bf16(x), dev_f32(r.topk_weights))
+        torch.cuda.synchronize()
+        out[E] = (run.maps(), run.counts.cpu().numpy(), run.offsets.cpu().numpy(),
+                  host_bf16(recv), host_f32(recv_w), p.live)
+    m32, c32, o32, rv32, rw32, live = out[32]
+    m256, c256, o256, rv256, rw256, live256 = out[256]
+    assert live == live256
+    assert np.array_equal(m32["slot"], m256["slot"])
+    assert np.array_equal(c256[:32], c32) and (c256[32:] == 0).all()
+    assert np.array_equal(o256[:33], o32) and (np.diff(o256[32:]) == 0).all()
+    assert np.array_equal(rv32[:live], rv256[:live])
+    assert np.array_equal(bits32(rw32[:live]), bits32(rw256[:live]))
 
 
 # ---------------------------------------------------------------------------
