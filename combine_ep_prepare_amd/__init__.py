@@ -108,7 +108,7 @@ class HandleRegions(C.Structure):
     """ep_handle_regions_t: byte offsets of the routing maps in a handle."""
     _fields_ = [("status", C.c_size_t), ("counts", C.c_size_t), ("offsets", C.c_size_t),
                 ("slot", C.c_size_t), ("row_src", C.c_size_t), ("bytes", C.c_size_t),
-                ("runs", C.c_size_t)]
+                ("runs", C.c_size_t), ("maps_bytes", C.c_size_t)]
 
 
 class EpError(RuntimeError):

@@ -90,7 +90,7 @@ ep_status_t payload_common(const ep_layout_t* L, const void* handle_mem, size_t 
   if (!handle_mem) return EP_ERR_NULL;
   const HandleLayout hl =
       handle_layout(L->num_tokens, L->topk, L->num_experts, L->recv_capacity);
-  if (handle_bytes < hl.bytes) return EP_ERR_HANDLE_SIZE;
+  if (handle_bytes < hl.maps_bytes) return EP_ERR_HANDLE_SIZE;
   if (!aligned16(handle_mem)) return EP_ERR_ALIGN;
   *d = dims_of(L, hl.num_units);
   *hv = handle_view(const_cast<void*>(handle_mem), hl);
@@ -129,6 +129,7 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
   out->row_src = hl.row_src;
   out->runs = hl.runs;
   out->bytes = hl.bytes;
+  out->maps_bytes = hl.maps_bytes;
   return EP_OK;
 }
 

@@ -40,10 +40,10 @@ constexpr int kWavesPerBlock = 4;
 constexpr uint32_t kScramble = 2654435761u;
 
 // The routing kernels' streaming store (cache-policy bits sc0 sc1 nt), with
-// the one wait state a 128-bit store needs before its data registers may be
-// overwritten.
+// the two wait states a 128-bit store needs on gfx950 before a VALU
+// instruction may overwrite its data registers.
 __device__ __forceinline__ void store_stream(vec4* p, vec4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 0" ::"v"(p), "v"(v)
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v)
                : "memory");
 }
 

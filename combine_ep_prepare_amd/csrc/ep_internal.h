@@ -54,9 +54,12 @@ struct HandleHeader {
 static_assert(sizeof(HandleHeader) <= 256, "header too large");
 
 // Byte offsets of the regions of a handle; every region is 256-byte aligned.
+// The routing maps come first (maps_bytes of them: everything the payload ops
+// read); prepare's scratch (the per-unit histograms and bad-id flags of its
+// two-kernel form) closes the handle.
 struct HandleLayout {
-  size_t header, counts, offsets, pad_offsets, slot, row_src, pad_rows, unit_hist,
-      unit_flags, runs, bytes;
+  size_t header, counts, offsets, pad_offsets, slot, row_src, pad_rows, runs, maps_bytes,
+      unit_hist, unit_flags, bytes;
   int32_t num_units;
 };
 
@@ -64,6 +67,16 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 inline int32_t prep_units(int64_t routes) {
   return (int32_t)((routes + kUnitRoutes - 1) / kUnitRoutes);
+}
+
+// Bytes of prepare's per-unit histograms (the first part of its scratch).
+inline size_t scratch_hist_bytes(int32_t num_units, int32_t E) {
+  return align256(sizeof(int32_t) * (size_t)num_units * (size_t)E);
+}
+
+// Bytes of prepare's whole scratch: the histograms, then the bad-id flags.
+inline size_t scratch_bytes(int32_t num_units, int32_t E) {
+  return scratch_hist_bytes(num_units, E) + align256(sizeof(int32_t) * (size_t)num_units);
 }
 
 inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) {
@@ -78,9 +91,10 @@ inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) 
   h.slot = at;         at += align256(sizeof(int32_t) * (size_t)routes);
   h.row_src = at;      at += align256(sizeof(int32_t) * (size_t)cap);
   h.pad_rows = at;     at += align256(sizeof(int32_t) * (size_t)cap);
-  h.unit_hist = at;    at += align256(sizeof(int32_t) * (size_t)h.num_units * (size_t)E);
-  h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
   h.runs = at;         at += align256(sizeof(RunEntry) * (size_t)routes);
+  h.maps_bytes = at;
+  h.unit_hist = at;    at += scratch_hist_bytes(h.num_units, E);
+  h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
   h.bytes = at;
   return h;
 }

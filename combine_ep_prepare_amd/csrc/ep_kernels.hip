@@ -847,12 +847,14 @@ __device__ __forceinline__ row16_t load_row16(const row16_t* p) {
 // dirty in the L2 until they are evicted, where they push out rows that are
 // still to be read; measured on the MI355X, the dsv3 dispatch by run entries
 // takes 118 µs with the write-through form against 125 µs (its token rows
-// are then read from HBM once), and no op is slower. The compiler emits no such store
-// from C++, so it is written out; the s_nop gives the one wait state that a
-// 128-bit store needs before a VALU instruction may overwrite its data
-// registers, which the compiler does not insert after an asm statement.
+// are then read from HBM once), and no op is slower. The compiler emits no
+// such store from C++, so it is written out. A store of more than 64 bits of
+// data needs two wait states on the gfx940 family (gfx950 included) before a
+// VALU instruction may overwrite its data registers, and the compiler inserts
+// none after an asm statement: `s_nop 1` gives both. With one (`s_nop 0`) a
+// GPU test saw the next loop step's index stored in place of the data.
 __device__ __forceinline__ void store_stream16(row16_t* p, row16_t v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 0" ::"v"(p), "v"(v)
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v)
                : "memory");
 }
 

@@ -177,6 +177,10 @@ size_t ep_handle_mem_size(const ep_layout_t* layout);
  *   row_src  [recv_capacity]  route held by received row r, -1 for a pad row;
  *            entries at or past min(total, recv_capacity) are unspecified
  *   bytes    == ep_handle_mem_size(layout)
+ *   maps_bytes  the size of the routing maps alone (<= bytes): the handle
+ *            region every payload op reads. A handle of maps_bytes serves the
+ *            payload ops; ep_prepare needs all `bytes` (its scratch closes the
+ *            handle).
  *   runs     [T*K] pairs (row, route): the run entries. The tokens are cut
  *            into chunks of C = min(256, ceil(T/8)) consecutive tokens, and
  *            chunk c owns entries [c*C*K, min((c+1)*C*K, T*K)): its routes
@@ -192,6 +196,7 @@ typedef struct ep_handle_regions {
   size_t row_src;
   size_t bytes;
   size_t runs;
+  size_t maps_bytes;
 } ep_handle_regions_t;
 
 ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* out);

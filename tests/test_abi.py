@@ -63,7 +63,10 @@ def test_handle_size_and_regions():
     assert r.slot + 4 * 4096 * 8 <= r.row_src
     assert r.row_src + 4 * L.cap <= n
     assert r.runs % 256 == 0 and r.row_src + 4 * L.cap <= r.runs
-    assert r.runs + 8 * 4096 * 8 == n             # the run entries close the handle
+    assert r.runs + 8 * 4096 * 8 == r.maps_bytes  # the run entries close the maps
+    # prepare's scratch closes the handle: 64 units of 512 routes, 256-expert
+    # histograms and one flag per unit, each part 256-byte aligned
+    assert n - r.maps_bytes == 64 * 256 * 4 + 256
     # the handle grows with the capacity and does not depend on H
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=512)) == n
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=7168, cap=L.cap * 2)) > n
@@ -151,15 +154,19 @@ def test_null_layout_and_pointers():
 
 
 def test_handle_too_small():
-    L = lay()
+    # prepare needs the whole handle (maps and its scratch); the payload ops
+    # read only the maps
+    L = lay(T=4096, K=8, E=256, A=128, H=7168)
     n = ep.handle_mem_size(L)
+    m = ep.handle_regions(L).maps_bytes
+    assert m < n
     assert ep.lib.ep_prepare(C.byref(L), P, P, None, P, n - 1, None) == ep.EP_ERR_HANDLE_SIZE
-    assert ep.lib.ep_dispatch(C.byref(L), P, n - 1, P, None, P2, None, None) == \
+    assert ep.lib.ep_dispatch(C.byref(L), P, m - 1, P, None, P2, None, None) == \
         ep.EP_ERR_HANDLE_SIZE
     assert ep.lib.ep_combine(C.byref(L), P, 0, P, P2, None) == ep.EP_ERR_HANDLE_SIZE
     assert ep.lib.ep_dispatch_bwd(C.byref(L), P, 7, P, None, P2, None, None) == \
         ep.EP_ERR_HANDLE_SIZE
-    assert ep.lib.ep_combine_bwd(C.byref(L), P, n - 256, P, P2, None) == \
+    assert ep.lib.ep_combine_bwd(C.byref(L), P, m - 256, P, P2, None) == \
         ep.EP_ERR_HANDLE_SIZE
 
 
@@ -214,7 +221,8 @@ def test_weighted_entry_points_error_paths():
     assert cw(C.byref(L), P, n, None, P2, P2, None) == ep.EP_ERR_NULL      # rows
     assert cw(C.byref(L), P, n, P, None, P2, None) == ep.EP_ERR_NULL      # weights
     assert cw(C.byref(L), P, n, P, P2, None, None) == ep.EP_ERR_NULL      # result
-    assert cw(C.byref(L), P, n - 1, P, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
+    m = ep.handle_regions(L).maps_bytes       # the payload ops read the maps only
+    assert cw(C.byref(L), P, m - 1, P, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
     assert cw(C.byref(L), P, n, MIS, P2, P2, None) == ep.EP_ERR_ALIGN
     assert cw(C.byref(L), P, n, P, P2, MIS, None) == ep.EP_ERR_ALIGN
     assert cwb(C.byref(L), P, n, None, P2, P2, P2, P2, None) == ep.EP_ERR_NULL   # grad
@@ -222,7 +230,7 @@ def test_weighted_entry_points_error_paths():
     assert cwb(C.byref(L), P, n, P, P2, P2, None, P2, None) == ep.EP_ERR_NULL   # grad rows
     # a weight gradient needs the expert rows
     assert cwb(C.byref(L), P, n, P, None, P2, P2, P2, None) == ep.EP_ERR_NULL
-    assert cwb(C.byref(L), P, n - 1, P, P2, P2, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
+    assert cwb(C.byref(L), P, m - 1, P, P2, P2, P2, P2, None) == ep.EP_ERR_HANDLE_SIZE
     assert cwb(C.byref(L), P, n, MIS, P2, P2, P2, P2, None) == ep.EP_ERR_ALIGN
     assert cwb(C.byref(L), P, n, P, MIS, P2, P2, P2, None) == ep.EP_ERR_ALIGN
     assert cwb(C.byref(L), P, n, P, P2, P2, MIS, P2, None) == ep.EP_ERR_ALIGN

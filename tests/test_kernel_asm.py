@@ -2,9 +2,10 @@
 
 The streaming store is written out in an asm statement (the compiler emits no
 store with the write-through policy from C++), so the compiler cannot see it
-as a store when it places wait states. A vector store of 128 bits needs one
-wait state before a VALU instruction may overwrite its data registers; the
-asm statement carries it. This test compiles both libraries' device code to
+as a store when it places wait states. A vector store of 128 bits needs two
+wait states on gfx950 before a VALU instruction may overwrite its data
+registers; the asm statement carries them (`s_nop 1`). With one, a GPU test
+saw the next loop index stored in place of the data. This test compiles both libraries' device code to
 assembly with the build's own flags and checks that every such store is
 followed by its wait state, and that the payload kernels do use it.
 """
@@ -50,7 +51,7 @@ def test_stream_stores_carry_their_wait_state(tmp_path, source, kernels):
     stores = [i for i, s in enumerate(ins) if STREAM_STORE.match(s)]
     assert stores, "no write-through store emitted"
     for i in stores:
-        assert i + 1 < len(ins) and ins[i + 1] == "s_nop 0", \
+        assert i + 1 < len(ins) and ins[i + 1] == "s_nop 1", \
             f"store without its wait state: {ins[i]!r} then {ins[i + 1:i + 2]!r}"
     # each payload kernel's body holds at least one such store
     text = "\n".join(lines)
