@@ -30,6 +30,8 @@ EP_ERR_HANDLE_SIZE = 4
 EP_ERR_CAPACITY = 5
 EP_ERR_DEVICE = 6
 EP_ERR_HIP = 7
+EP_ERR_SCRATCH = 8
+PREPARE_STATIC_SCRATCH_BYTES = 4 << 20
 
 STATUS_BAD_EXPERT = 1
 STATUS_OVERFLOW = 2
@@ -49,7 +51,7 @@ _CODE_OF = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16, torch.float32
             "bf16": DTYPE_BF16, "fp16": DTYPE_FP16, "fp32": DTYPE_FP32}
 
 ENTRY_POINTS = ("ep_recv_capacity_worst", "ep_handle_mem_size", "ep_handle_regions",
-                "ep_prepare", "ep_dispatch",
+                "ep_prepare", "ep_prepare_static", "ep_dispatch",
                 "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_weighted",
                 "ep_combine_weighted_bwd", "ep_read_status", "ep_status_str")
 
@@ -132,6 +134,7 @@ def _load_library(path: str = LIB_PATH):
     lib.ep_handle_regions.argtypes = [lp, C.POINTER(HandleRegions)]
     lib.ep_handle_regions.restype = C.c_int
     lib.ep_prepare.argtypes = [lp, vp, vp, vp, vp, sz, vp]
+    lib.ep_prepare_static.argtypes = [lp, vp, vp, vp, vp, sz, vp]
     lib.ep_dispatch.argtypes = [lp, vp, sz, vp, vp, vp, vp, vp]
     lib.ep_combine.argtypes = [lp, vp, sz, vp, vp, vp]
     lib.ep_dispatch_bwd.argtypes = [lp, vp, sz, vp, vp, vp, vp, vp]
@@ -139,7 +142,8 @@ def _load_library(path: str = LIB_PATH):
     lib.ep_combine_weighted.argtypes = [lp, vp, sz, vp, vp, vp, vp]
     lib.ep_combine_weighted_bwd.argtypes = [lp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.ep_read_status.argtypes = [vp, C.POINTER(C.c_uint32), vp]
-    for name in ("ep_prepare", "ep_dispatch", "ep_combine", "ep_dispatch_bwd",
+    for name in ("ep_prepare", "ep_prepare_static", "ep_dispatch", "ep_combine",
+                 "ep_dispatch_bwd",
                  "ep_combine_bwd", "ep_combine_weighted", "ep_combine_weighted_bwd",
                  "ep_read_status"):
         getattr(lib, name).restype = C.c_int
@@ -237,6 +241,21 @@ def prepare(layout: Layout, topk_idx: torch.Tensor, token_counts: torch.Tensor,
     _check(lib.ep_prepare(C.byref(layout), _ptr(topk_idx), _ptr(token_counts),
                           _ptr(expert_offsets), _ptr(handle), handle.numel(),
                           _stream(stream)), "ep_prepare")
+
+
+def prepare_static(layout: Layout, topk_idx: torch.Tensor, token_counts: torch.Tensor,
+                   handle: torch.Tensor, expert_offsets: Optional[torch.Tensor] = None,
+                   stream=None):
+    """prepare with its scratch in the library's static device array: the
+    handle needs only ``handle_regions(layout).maps_bytes`` bytes. Calls that
+    overlap on one device race."""
+    _need(topk_idx, "topk_idx", torch.int64, (layout.T, layout.K))
+    _need(token_counts, "token_counts", torch.int32, (layout.E,))
+    _need(expert_offsets, "expert_offsets", torch.int32, (layout.E + 1,), allow_none=True)
+    _need(handle, "handle", torch.uint8)
+    _check(lib.ep_prepare_static(C.byref(layout), _ptr(topk_idx), _ptr(token_counts),
+                                 _ptr(expert_offsets), _ptr(handle), handle.numel(),
+                                 _stream(stream)), "ep_prepare_static")
 
 
 def dispatch(layout: Layout, handle: torch.Tensor, tokens: torch.Tensor,

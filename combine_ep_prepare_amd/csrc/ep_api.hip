@@ -1,6 +1,7 @@
 // ep_api.hip -- the C ABI of include/ep.h: argument validation, handle
 // layout and kernel launches. Stateless apart from a per-device cache of the
-// architecture check and compute-unit count.
+// architecture check and compute-unit count, and the static scratch array of
+// ep_prepare_static with its per-device address.
 
 #include <hip/hip_runtime.h>
 
@@ -21,6 +22,40 @@ constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other architecture; then the CU count.
 std::atomic<int> g_dev_kind[kMaxDevices];
 std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Device address of `scratch` (below) on each device, 0 until looked up.
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+static_assert(EP_PREPARE_STATIC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+
+}  // namespace
+
+// ep_prepare_static's scratch: prepare's per-unit histograms and bad-id flags
+// (up to EP_PREPARE_STATIC_SCRATCH_BYTES), in place of the handle's scratch
+// region. Each device holds its own copy until the process ends. In host code
+// this name is only a stand-in for the device array: its device address comes
+// from hipGetSymbolAddress, once per device (static_scratch below).
+static __device__ __align__(256) int32_t scratch[EP_PREPARE_STATIC_SCRATCH_BYTES / 4];
+
+namespace {
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device with the device current.
+ep_status_t static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return EP_ERR_DEVICE;
+  uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return EP_ERR_HIP;
+    a = reinterpret_cast<uintptr_t>(p);
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *out = reinterpret_cast<void*>(a);
+  return EP_OK;
+}
 
 ep_status_t check_layout(const ep_layout_t* L) {
   if (!L) return EP_ERR_NULL;
@@ -150,6 +185,40 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
   if (st != EP_OK) return st;
   const Dims d = dims_of(layout, hl.num_units);
   const HandleView hv = handle_view(handle_mem, hl);
+  if (launch_prepare(d, hv, topk_idx, token_counts, expert_offsets, num_cus, stream) !=
+      hipSuccess)
+    return EP_ERR_HIP;
+  return EP_OK;
+}
+
+ep_status_t ep_prepare_static(const ep_layout_t* layout, const int64_t* topk_idx,
+                              int32_t* token_counts, int32_t* expert_offsets, void* handle_mem,
+                              size_t handle_bytes, hipStream_t stream) {
+  ep_status_t st = check_layout(layout);
+  if (st != EP_OK) return st;
+  if (!token_counts || !handle_mem) return EP_ERR_NULL;
+  if (layout->num_tokens > 0 && !topk_idx) return EP_ERR_NULL;
+  const HandleLayout hl =
+      handle_layout(layout->num_tokens, layout->topk, layout->num_experts,
+                    layout->recv_capacity);
+  if (handle_bytes < hl.maps_bytes) return EP_ERR_HANDLE_SIZE;
+  if (scratch_bytes(hl.num_units, layout->num_experts) > EP_PREPARE_STATIC_SCRATCH_BYTES)
+    return EP_ERR_SCRATCH;
+  if (!aligned16(handle_mem)) return EP_ERR_ALIGN;
+  int num_cus = 0;
+  st = current_device(&num_cus);
+  if (st != EP_OK) return st;
+  void* sp = nullptr;
+  st = static_scratch(&sp);
+  if (st != EP_OK) return st;
+  const Dims d = dims_of(layout, hl.num_units);
+  HandleView hv = handle_view(handle_mem, hl);
+  // the histograms and flags go to the static array instead of the handle;
+  // the hist kernel writes every entry before the slot kernel reads it, so
+  // nothing there has to start at zero
+  hv.unit_hist = static_cast<int32_t*>(sp);
+  hv.unit_flags = reinterpret_cast<int32_t*>(static_cast<char*>(sp) +
+                                             scratch_hist_bytes(hl.num_units, d.E));
   if (launch_prepare(d, hv, topk_idx, token_counts, expert_offsets, num_cus, stream) !=
       hipSuccess)
     return EP_ERR_HIP;
@@ -312,6 +381,8 @@ const char* ep_status_str(ep_status_t status) {
     case EP_ERR_CAPACITY: return "recv_capacity is negative or not below 2^31";
     case EP_ERR_DEVICE: return "the current device is not gfx950";
     case EP_ERR_HIP: return "a HIP call or kernel launch failed";
+    case EP_ERR_SCRATCH:
+      return "the layout needs more prepare scratch than ep_prepare_static's static buffer holds";
   }
   return "unknown ep_status_t";
 }

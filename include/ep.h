@@ -72,7 +72,9 @@ typedef enum ep_status {
   EP_ERR_HANDLE_SIZE = 4, /* handle_bytes < ep_handle_mem_size(layout) */
   EP_ERR_CAPACITY = 5,    /* recv_capacity < 0 or >= 2^31 */
   EP_ERR_DEVICE = 6,      /* the current device is not gfx950 */
-  EP_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+  EP_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  EP_ERR_SCRATCH = 8      /* ep_prepare_static: the layout's prepare scratch
+                             exceeds EP_PREPARE_STATIC_SCRATCH_BYTES */
 } ep_status_t;
 
 /* Sticky device-side bits of a handle's status word. */
@@ -219,6 +221,29 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
 ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
                        int32_t* token_counts, int32_t* expert_offsets, void* handle_mem,
                        size_t handle_bytes, hipStream_t stream);
+
+/*
+ * ep_prepare_static: ep_prepare for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation)
+ * and so cannot give the handle room for prepare's scratch. The same work and
+ * the same routing maps, bit for bit, but the scratch (the per-unit expert
+ * histograms and bad-id flags of the prepare kernels) lives in a static
+ * device array of the library, EP_PREPARE_STATIC_SCRATCH_BYTES per device,
+ * held until the process ends; so handle_mem needs only the routing maps,
+ * `maps_bytes` of ep_handle_regions (ep_handle_mem_size also suffices).
+ * Allocates nothing: the array's device address is looked up on the first
+ * call on each device. Every call on one device shares that device's array,
+ * so calls of ep_prepare_static that overlap on one device (several streams,
+ * no ordering between them) race and must not be made; ep_prepare and the
+ * payload ops do not touch the array. A layout whose scratch, 4 bytes per
+ * expert per 512 routes plus 4 per 512 routes (each part rounded up to
+ * 256 bytes), exceeds the array returns EP_ERR_SCRATCH before any HIP call.
+ */
+#define EP_PREPARE_STATIC_SCRATCH_BYTES (4u << 20)
+
+ep_status_t ep_prepare_static(const ep_layout_t* layout, const int64_t* topk_idx,
+                              int32_t* token_counts, int32_t* expert_offsets, void* handle_mem,
+                              size_t handle_bytes, hipStream_t stream);
 
 /*
  * dispatch: recv_tokens[r,:] = tokens[s/K,:] and recv_topk_weights[r] =

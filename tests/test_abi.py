@@ -269,3 +269,31 @@ def test_receive_buffers_required_without_tokens():
         ep.EP_ERR_NULL
     assert ep.lib.ep_combine_weighted(C.byref(L), P, n, None, None, None, None) == \
         ep.EP_ERR_NULL
+
+
+def test_prepare_static_host_checks():
+    """ep_prepare_static: the same argument checks as ep_prepare, a handle of
+    the routing maps alone is enough, and a layout whose scratch exceeds the
+    static array is refused with EP_ERR_SCRATCH, all before any HIP call."""
+    fn = ep.lib.ep_prepare_static
+    L = lay(T=4096, K=8, E=256, A=128, H=7168)
+    m = ep.handle_regions(L).maps_bytes
+    assert fn(C.byref(lay(K=0)), P, P, None, P, 1 << 30, None) == ep.EP_ERR_SHAPE
+    assert fn(None, P, P, None, P, m, None) == ep.EP_ERR_NULL
+    assert fn(C.byref(L), None, P, None, P, m, None) == ep.EP_ERR_NULL
+    assert fn(C.byref(L), P, None, None, P, m, None) == ep.EP_ERR_NULL
+    assert fn(C.byref(L), P, P, None, None, m, None) == ep.EP_ERR_NULL
+    assert fn(C.byref(L), P, P, None, P, m - 1, None) == ep.EP_ERR_HANDLE_SIZE
+    assert fn(C.byref(L), P, P, None, MIS, m, None) == ep.EP_ERR_ALIGN
+    # 2^20 tokens x 8 routes over 2048 experts: 16384 units of 2048-entry
+    # histograms, 128 MiB of scratch
+    big = lay(T=1 << 20, K=8, E=2048, A=1, H=64, cap=64)
+    assert ep.handle_mem_size(big) > 0
+    assert fn(C.byref(big), P, P, None, P, 1 << 40, None) == ep.EP_ERR_SCRATCH
+    assert "static" in ep.status_str(ep.EP_ERR_SCRATCH)
+    # the largest layout it takes at E = 256: 4 MiB holds 4080 units of
+    # 256-entry histograms (4080 KiB) plus their flags (16 KiB), 4081 do not
+    for units, want_ok in ((4080, True), (4081, False)):
+        Lu = lay(T=units * 64, K=8, E=256, A=1, H=64, cap=64)
+        code = fn(C.byref(Lu), P, P, None, MIS, 1 << 40, None)
+        assert code == (ep.EP_ERR_ALIGN if want_ok else ep.EP_ERR_SCRATCH)
