@@ -57,43 +57,37 @@ CEILINGS_LIB = os.path.join(ROOT, "combine_ep_prepare_amd", "libep_ceilings.so")
 CEILING_BUFFER_BYTES = 1 << 30     # each pattern moves 1 GiB (or the largest fit)
 
 # op -> the library kernel that runs it
-KERNEL_OF_OP = {"dispatch": "scatter_rows_kernel", "combine_bwd": "scatter_rows_kernel",
+KERNEL_OF_OP = {"dispatch": "run_rows_kernel", "combine_bwd": "run_rows_kernel",
                 "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel",
                 "combine_weighted": "reduce_rows_kernel",
                 "combine_weighted_bwd": "weighted_bwd_kernel",
-                "dispatch_nopad": "scatter_rows_kernel",
-                "combine_bwd_nopad": "scatter_rows_kernel",
+                "dispatch_nopad": "run_rows_kernel",
+                "combine_bwd_nopad": "run_rows_kernel",
                 "combine_fp16": "reduce_rows_kernel",
-                "dispatch_fp32": "scatter_rows_kernel",
-                "combine_fp32": "reduce_rows_kernel",
-                "dispatch_scatter": "scatter_rows_kernel"}
+                "dispatch_fp32": "run_rows_kernel",
+                "combine_fp32": "reduce_rows_kernel"}
 PAYLOAD_KERNELS = ("scatter_rows_kernel", "reduce_rows_kernel", "weighted_bwd_kernel",
                    "run_rows_kernel")
-# ops that copy over the run entries when the routing is dense (no masked
-# route, EP_LAYOUT_DENSE_ROUTING); "dispatch_scatter" is dispatch without the
-# flag, timed beside it
-DENSE_OPS = ("dispatch", "combine_bwd", "dispatch_nopad", "combine_bwd_nopad", "dispatch_fp32")
 PREPARE_KERNELS = ("prepare_hist_kernel", "prepare_slots_kernel", "prepare_fused_kernel",
                    "prepare_runs_kernel")
-
 
 COLD = "@cold"      # suffix of the launches timed after a cache flush
 
 
-def kernel_of(op: str, dense: bool) -> str:
-    """The library kernel that runs ``op`` (dispatch and combine_bwd take the
-    run-entry copy on a dense routing); a cold launch runs the op's kernel."""
+def kernel_of(op: str, dense: bool = False) -> str:
+    """The library kernel that runs ``op`` (a cold launch runs the op's
+    kernel)."""
     op = op[:-len(COLD)] if op.endswith(COLD) else op
-    if dense and op in DENSE_OPS:
-        return "run_rows_kernel"
     return KERNEL_OF_OP[op]
 
-# ops timed after the step: op -> (payload type, pads filled, dense path allowed)
-EXTRA_OPS = {"combine_weighted": ("bf16", True, True),
-             "combine_weighted_bwd": ("bf16", True, True),
-             "dispatch_nopad": ("bf16", False, True), "combine_bwd_nopad": ("bf16", False, True),
-             "combine_fp16": ("fp16", True, True), "dispatch_fp32": ("fp32", True, True),
-             "combine_fp32": ("fp32", True, True), "dispatch_scatter": ("bf16", True, False)}
+# ops timed after the step: op -> (payload type, pads filled); the fp32 ops
+# use a handle prepared with the fp32 layout (its run chunks sized for fp32
+# rows), as a caller with fp32 payloads would prepare it
+EXTRA_OPS = {"combine_weighted": ("bf16", True),
+             "combine_weighted_bwd": ("bf16", True),
+             "dispatch_nopad": ("bf16", False), "combine_bwd_nopad": ("bf16", False),
+             "combine_fp16": ("fp16", True), "dispatch_fp32": ("fp32", True),
+             "combine_fp32": ("fp32", True)}
 ESIZE = {"bf16": 2, "fp16": 2, "fp32": 4}
 
 
@@ -156,7 +150,7 @@ def algorithmic_bytes(T, K, E, H, topk_idx, counts_np, offsets_np, esize=2, fill
 
 def base_op(op: str) -> str:
     """dispatch_fp32 -> dispatch, combine_bwd_nopad -> combine_bwd, ..."""
-    for suffix in ("_nopad", "_fp16", "_fp32", "_scatter"):
+    for suffix in ("_nopad", "_fp16", "_fp32"):
         if op.endswith(suffix):
             return op[:-len(suffix)]
     return op
@@ -498,10 +492,8 @@ def main():
     log(f"workload {cfg.name}: T={T} H={H} E={E} K={K} A={A}")
     r = workloads.make_routing(cfg)
     cap = ep.recv_capacity_worst(T, K, E, A)
-    # a routing with no masked route takes the dense-routing copy (the flag a
-    # caller sets when all of a layer's experts are local)
-    dense = bool((r.topk_idx >= 0).all())
-    L = ep.Layout(T, K, E, A, H, cap, dense=dense)
+    dense = bool((r.topk_idx >= 0).all())       # reported only
+    L = ep.Layout(T, K, E, A, H, cap)
     dev = torch.device("cuda")
     handle = ep.new_handle(L)
     idx = torch.from_numpy(r.topk_idx).to(dev)
@@ -662,9 +654,12 @@ def main():
     # launches after the same warmup.
     extra = {}
     if not args.no_extra_ops:
-        lay = {key: ep.Layout(T, K, E, A, H, cap, dtype=key[0], fill_pads=key[1],
-                              dense=dense and key[2])
+        lay = {key: ep.Layout(T, K, E, A, H, cap, dtype=key[0], fill_pads=key[1])
                for key in set(EXTRA_OPS.values())}
+        # the fp32 ops' own handle, prepared with the fp32 layout
+        handle32 = ep.new_handle(lay[("fp32", True)])
+        counts32 = torch.empty(E, dtype=torch.int32, device=dev)
+        ep.prepare(lay[("fp32", True)], idx, counts32, handle32)
         result_w = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         g_rows_w = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
         g_recv_w2 = torch.empty(cap, dtype=torch.float32, device=dev)
@@ -686,13 +681,10 @@ def main():
             "dispatch_nopad": lambda Lx: ep.dispatch(Lx, handle, x, w, recv_np, recv_w_np),
             "combine_bwd_nopad": lambda Lx: ep.combine_bwd(Lx, handle, g_result, g_exp_np),
             "combine_fp16": lambda Lx: ep.combine(Lx, handle, eo16, res16),
-            "dispatch_fp32": lambda Lx: ep.dispatch(Lx, handle, x32, w, recv32, recv_w32),
-            "combine_fp32": lambda Lx: ep.combine(Lx, handle, eo32, res32),
-            "dispatch_scatter": lambda Lx: ep.dispatch(Lx, handle, x, w, recv_np, recv_w_np),
+            "dispatch_fp32": lambda Lx: ep.dispatch(Lx, handle32, x32, w, recv32, recv_w32),
+            "combine_fp32": lambda Lx: ep.combine(Lx, handle32, eo32, res32),
         }
         for op, key in EXTRA_OPS.items():
-            if op == "dispatch_scatter" and not dense:
-                continue                      # the same launch as dispatch itself
             dt, fill = key[0], key[1]
             Lx = lay[key]
             fn = fns[op]

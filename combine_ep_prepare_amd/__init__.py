@@ -110,7 +110,9 @@ class HandleRegions(C.Structure):
     """ep_handle_regions_t: byte offsets of the routing maps in a handle."""
     _fields_ = [("status", C.c_size_t), ("counts", C.c_size_t), ("offsets", C.c_size_t),
                 ("slot", C.c_size_t), ("row_src", C.c_size_t), ("bytes", C.c_size_t),
-                ("runs", C.c_size_t), ("maps_bytes", C.c_size_t)]
+                ("runs", C.c_size_t), ("maps_bytes", C.c_size_t),
+                ("stream_live", C.c_size_t), ("run_units", C.c_size_t),
+                ("run_list_entries", C.c_size_t)]
 
 
 class EpError(RuntimeError):
@@ -191,7 +193,9 @@ def handle_maps(layout: Layout, handle: torch.Tensor) -> dict:
         "offsets": view(r.offsets, layout.E + 1, torch.int32),
         "slot": view(r.slot, layout.T * layout.K, torch.int32),
         "row_src": view(r.row_src, layout.cap, torch.int32),
-        "runs": view(r.runs, 2 * layout.T * layout.K, torch.int32).view(-1, 2),
+        "runs": view(r.runs, 8 * 2 * r.run_list_entries, torch.int32).view(8, -1, 2),
+        "stream_live": view(r.stream_live, 8, torch.int32),
+        "run_units": view(r.run_units, 1, torch.int32),
     }
 
 

@@ -165,6 +165,9 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
   out->runs = hl.runs;
   out->bytes = hl.bytes;
   out->maps_bytes = hl.maps_bytes;
+  out->stream_live = hl.header + offsetof(HandleHeader, stream_live);
+  out->run_units = hl.header + offsetof(HandleHeader, run_units);
+  out->run_list_entries = (size_t)run_stream_cap(hl.num_units);
   return EP_OK;
 }
 
@@ -243,12 +246,9 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(tokens) || !aligned16(recv_tokens)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  const hipError_t e =
-      d.dense ? launch_run_rows(d, hv, tokens, topk_weights, recv_tokens, recv_topk_weights,
-                                stream)
-              : launch_scatter_rows(d, hv, tokens, topk_weights, recv_tokens,
-                                    recv_topk_weights, num_cus, stream);
-  if (e != hipSuccess) return EP_ERR_HIP;
+  if (launch_run_rows(d, hv, tokens, topk_weights, recv_tokens, recv_topk_weights, num_cus,
+                      stream) != hipSuccess)
+    return EP_ERR_HIP;
   return EP_OK;
 }
 
@@ -301,11 +301,9 @@ ep_status_t ep_combine_bwd(const ep_layout_t* layout, const void* handle_mem,
   if (!aligned16(grad) || !aligned16(grad_expert_out)) return EP_ERR_ALIGN;
   st = current_device(&num_cus);
   if (st != EP_OK) return st;
-  const hipError_t e =
-      d.dense ? launch_run_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, stream)
-              : launch_scatter_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, num_cus,
-                                    stream);
-  if (e != hipSuccess) return EP_ERR_HIP;
+  if (launch_run_rows(d, hv, grad, nullptr, grad_expert_out, nullptr, num_cus, stream) !=
+      hipSuccess)
+    return EP_ERR_HIP;
   return EP_OK;
 }
 

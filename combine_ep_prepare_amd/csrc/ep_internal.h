@@ -18,24 +18,50 @@ constexpr uint32_t kHandleMagic = 0x45504D49u;  // "EPMI"
 constexpr int kPrepRounds = 8;
 constexpr int kUnitRoutes = kPrepRounds * kWave;
 
-// Run entries: the valid routes of each chunk of run_chunk_tokens(T)
-// consecutive tokens, in ascending received-row order (so the rows an expert
-// receives from one chunk, a contiguous run, are adjacent). Chunk c owns the
-// entries [c*C*K, c*C*K + routes of the chunk); a route that holds no row
-// (masked, a bad id, or dropped past the capacity) leaves an empty entry at
-// the end of its chunk's range.
+// Run entries. The routes are cut into chunks of run_units consecutive
+// prepare units (RU * 512 routes, RU in {1, 2, 4}), and chunk c belongs to
+// XCD stream c mod 8. A chunk's entries are its routes that hold a row, in
+// ascending received-row order (so the rows an expert receives from the
+// chunk, one contiguous run, are adjacent), then one empty entry for each of
+// its valid routes dropped past the capacity. Each stream's chunks are laid
+// out one after another in that stream's list, which starts at
+// x * stream_cap(U) entries; the header holds each list's length.
 struct RunEntry {
   int32_t row;    // received row, or -1 for an empty entry
   int32_t route;  // route index s = t*K + k
 };
-constexpr int kRunXcds = 8;          // chunks are dealt round-robin to 8 streams
-constexpr int64_t kRunChunkMax = 256;
+constexpr int kRunXcds = 8;             // chunks are dealt round-robin to 8 streams
+constexpr int kRunMaxUnits = 4;         // at most 4 units (2048 routes) per chunk
+constexpr int64_t kRunChunkBytes = 3584 * 1024;   // token rows of one chunk, at most
 
-// Tokens per chunk: 256, or fewer so that a small batch still spans all eight
-// streams. Depends on T only, so prepare and the payload ops agree.
-inline int64_t run_chunk_tokens(int64_t T) {
-  const int64_t c = (T + kRunXcds - 1) / kRunXcds;
-  return c < 1 ? 1 : (c > kRunChunkMax ? kRunChunkMax : c);
+// Units per chunk: the most (up to 4) whose tokens' rows (RU * 512 / K of
+// them) fit in kRunChunkBytes, so that a chunk's token rows stay in one XCD's
+// 4 MB L2 while its runs are written; fewer if that leaves some stream with
+// no chunk. Chosen by prepare from its layout's row size and kept in the
+// header, so payload ops of another payload type read the same entries.
+inline int32_t run_chunk_units(int32_t units, int32_t K, int64_t row_bytes) {
+  int32_t ru = kRunMaxUnits;
+  while (ru > 1 && (int64_t)ru * kUnitRoutes / K * row_bytes > kRunChunkBytes) ru /= 2;
+  while (ru > 1 && (units + ru - 1) / ru < kRunXcds) ru /= 2;
+  return ru;
+}
+
+// Entries each stream's list can hold: its chunks, at most ceil(ceil(U/RU)/8)
+// of RU * 512 entries, which is at most 64 U + 2048 for any RU <= 4.
+__host__ __device__ inline int64_t run_stream_cap(int32_t units) {
+  return (int64_t)units * (kUnitRoutes / kRunXcds) + (int64_t)kRunMaxUnits * kUnitRoutes;
+}
+
+// The most entries one stream receives when every route holds a row, over
+// the chunk sizes prepare may choose: what a run copy's grid is sized for.
+inline int64_t run_stream_dense(int32_t units, int64_t routes) {
+  int64_t m = 0;
+  for (int32_t ru = 1; ru <= kRunMaxUnits; ru *= 2) {
+    const int64_t nch = (units + ru - 1) / ru;
+    const int64_t e = (nch + kRunXcds - 1) / kRunXcds * ru * kUnitRoutes;
+    if (e > m) m = e;
+  }
+  return m < routes ? m : routes;
 }
 
 // Header at the start of every handle (256 bytes reserved).
@@ -50,6 +76,8 @@ struct HandleHeader {
   int64_t recv_capacity;
   int32_t total;        // offsets[E]
   int32_t pads_live;    // pad rows below recv_capacity
+  int32_t run_units;    // units per run chunk (RU)
+  int32_t stream_live[kRunXcds];  // entries in each stream's run list
 };
 static_assert(sizeof(HandleHeader) <= 256, "header too large");
 
@@ -91,7 +119,8 @@ inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) 
   h.slot = at;         at += align256(sizeof(int32_t) * (size_t)routes);
   h.row_src = at;      at += align256(sizeof(int32_t) * (size_t)cap);
   h.pad_rows = at;     at += align256(sizeof(int32_t) * (size_t)cap);
-  h.runs = at;         at += align256(sizeof(RunEntry) * (size_t)routes);
+  h.runs = at;
+  at += align256(sizeof(RunEntry) * (size_t)kRunXcds * (size_t)run_stream_cap(h.num_units));
   h.maps_bytes = at;
   h.unit_hist = at;    at += scratch_hist_bytes(h.num_units, E);
   h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
@@ -109,7 +138,7 @@ struct HandleView {
   int32_t* row_src;
   int32_t* pad_rows;
   int32_t* unit_hist;
-  int32_t* unit_flags;
+  int32_t* unit_flags;   // per unit: (valid routes << 1) | bad-id flag
   RunEntry* runs;
 };
 
@@ -153,11 +182,11 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
 hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,
                                const float* w, void* dst, float* dst_w, int num_cus,
                                hipStream_t stream);
-// rw != nullptr selects the weighted sum (weights of the received rows).
-// The same map D over the run entries (dense routings): one launch sized
-// exactly from T and K.
+// The map D over the run entries (every routing): one launch sized for a
+// dense routing, its work read on the device.
 hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
-                           const float* w, void* dst, float* dst_w, hipStream_t stream);
+                           const float* w, void* dst, float* dst_w, int num_cus,
+                           hipStream_t stream);
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
                               const float* rw, const float* g_w, void* dst, float* dst_w,
                               int num_cus, hipStream_t stream);

@@ -152,7 +152,8 @@ __device__ __forceinline__ int64_t unit_id(const int64_t (&ids)[kPrepRounds], in
 // 64-route round is added once, by its lowest lane, with the peer count. The
 // count before the add plus the route's rank among its peers is the route's
 // rank among the unit's routes of its expert: it is left in slot[s], packed
-// with the expert id, for prepare_slots_kernel.
+// with the expert id, for prepare_slots_kernel. The unit's flag word holds
+// its count of valid routes and whether it saw a bad id.
 __global__ void __launch_bounds__(512)
 prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int nbits) {
   extern __shared__ int32_t lds[];
@@ -167,6 +168,7 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
   const int64_t routes = d.T * d.K;
   const int32_t u = blockIdx.x * nw + w;
   bool bad_any = false;
+  int32_t nvalid = 0;
   if (u < d.num_units) {
     const int64_t base = (int64_t)u * kUnitRoutes;
     int64_t ids[kPrepRounds];
@@ -182,6 +184,7 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
       valid[i] = id >= 0 && id < E;
       const bool bad = !valid[i] && id != -1;
       bad_any |= wave_ballot(bad) != 0;
+      nvalid += __popcll(wave_ballot(valid[i]));
       key[i] = valid[i] ? (uint32_t)id : 0u;
       peers[i] = match_peers(key[i], valid[i], nbits);
     });
@@ -207,7 +210,7 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
   if (u < d.num_units) {
     int32_t* out = hv.unit_hist + (int64_t)u * E;
     for (int e = lane; e < E; e += kWave) out[e] = hist[e];
-    if (lane == 0) hv.unit_flags[u] = bad_any ? 1 : 0;
+    if (lane == 0) hv.unit_flags[u] = (nvalid << 1) | (bad_any ? 1 : 0);
   }
 }
 
@@ -218,11 +221,15 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
 // slot[s].
 __global__ void __launch_bounds__(512)
 prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
-                     int32_t* __restrict__ user_offsets, int32_t run_units, int32_t run_ck) {
+                     int32_t* __restrict__ user_offsets, int32_t ru, int32_t in_slot) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t s_wave_tot[2][16];
   __shared__ int32_t s_pads_live;
-  __shared__ int32_t s_run_tot[16];
+  __shared__ int32_t s_run_tot[16];     // kept entries of each of this block's chunks
+  __shared__ int32_t s_run_valid[16];   // valid routes of each of this block's chunks
+  __shared__ int32_t s_run_base[16];    // each chunk's start in its stream's list
+  __shared__ int32_t s_live[kRunXcds];
+  const int32_t run_units = in_slot ? ru : 0;
   const int nthr = blockDim.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -353,7 +360,8 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
   }
   __syncthreads();
 
-  // 3. Block 0 publishes counts, offsets and the header.
+  // 3. Block 0 publishes counts, offsets and the header, with the length of
+  //    each stream's run list (the valid routes of its chunks).
   if (blockIdx.x == 0) {
     for (int e = tid; e <= E; e += nthr) {
       hv.offsets[e] = s_offs[e];
@@ -364,9 +372,16 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
         user_counts[e] = s_counts[e];
       }
     }
+    if (tid < kRunXcds) s_live[tid] = 0;
+    __syncthreads();
     int32_t f = 0;
-    for (int32_t u = tid; u < U; u += nthr) f |= hv.unit_flags[u];
+    for (int32_t u = tid; u < U; u += nthr) {
+      const int32_t fl = hv.unit_flags[u];
+      f |= fl & 1;
+      atomicAdd(&s_live[(u / ru) % kRunXcds], fl >> 1);
+    }
     const int any_bad = __syncthreads_or(f);
+    if (tid < kRunXcds) hv.header->stream_live[tid] = s_live[tid];
     if (tid == 0) {
       HandleHeader* h = hv.header;
       const int32_t total = s_offs[E];
@@ -380,6 +395,7 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
       h->recv_capacity = d.cap;
       h->total = total;
       h->pads_live = s_pads_live;
+      h->run_units = ru;
       h->magic = kHandleMagic;
     }
   }
@@ -439,8 +455,39 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
       }
     }
     if (tid == nthr - 1) s_run_tot[q] = ex;
+    __syncthreads();          // every wave has read s_wave_tot for its scan
+    // the chunk's start in its stream's list: the valid routes of the
+    // stream's earlier chunks (whole chunks of ru units each), and the
+    // chunk's own valid routes
+    const int32_t c = (u0 + qa) / ru;
+    const int32_t nprev = c / kRunXcds * ru;
+    int32_t vb = 0, vo = 0;
+    for (int32_t i = tid; i < nprev; i += nthr) {
+      const int32_t cp = c % kRunXcds + kRunXcds * (i / ru);
+      vb += hv.unit_flags[cp * ru + i % ru] >> 1;
+    }
+    for (int32_t i = tid; i < qb - qa; i += nthr) vo += hv.unit_flags[u0 + qa + i] >> 1;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      vb += __shfl_xor(vb, off);
+      vo += __shfl_xor(vo, off);
+    }
+    if (lane == 0) {
+      s_wave_tot[0][w] = vb;
+      s_wave_tot[1][w] = vo;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int32_t b = 0, o = 0;
+      for (int qq = 0; qq < nw; ++qq) {
+        b += s_wave_tot[0][qq];
+        o += s_wave_tot[1][qq];
+      }
+      s_run_base[q] = b;
+      s_run_valid[q] = o;
+    }
     __syncthreads();
   }
+  const int64_t scap = run_stream_cap(U);
 
   // 5. Stable slots: the unit's start row of the route's expert plus the
   //    route's rank among the unit's routes of that expert.
@@ -459,19 +506,18 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
         if (keep && run_units > 0) {
           const int q = w / run_units;
           const int32_t first = s_cursor[q * run_units * E + e];
-          const int64_t chunk = (int64_t)(u0 + q * run_units) / run_units;
-          hv.runs[chunk * run_ck + s_rbase[q * E + e] + ((int32_t)row - first)] =
-              RunEntry{(int32_t)row, (int32_t)s};
+          const int32_t chunk = (u0 + q * run_units) / run_units;
+          hv.runs[(chunk % kRunXcds) * scap + s_run_base[q] + s_rbase[q * E + e] +
+                  ((int32_t)row - first)] = RunEntry{(int32_t)row, (int32_t)s};
         }
       }
     });
   }
-  // the chunks' remaining entries are empty
+  // a chunk's valid routes dropped past the capacity leave empty entries
   for (int q = 0; q < nchb; ++q) {
-    const int64_t chunk = (int64_t)(u0 + q * run_units) / run_units;
-    const int64_t n_c = routes - chunk * run_ck < run_ck ? routes - chunk * run_ck : run_ck;
-    for (int64_t i = s_run_tot[q] + tid; i < n_c; i += nthr)
-      hv.runs[chunk * run_ck + i] = RunEntry{-1, -1};
+    const int32_t chunk = (u0 + q * run_units) / run_units;
+    for (int32_t i = s_run_tot[q] + tid; i < s_run_valid[q]; i += nthr)
+      hv.runs[(chunk % kRunXcds) * scap + s_run_base[q] + i] = RunEntry{-1, -1};
   }
 
   // 6. Pad rows: row_src = -1 and the list of live pad rows (ascending, so
@@ -503,7 +549,7 @@ constexpr int kFusedWaves = 16;
 __global__ void __launch_bounds__(kFusedWaves * kWave)
 prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
                      int32_t* __restrict__ user_counts, int32_t* __restrict__ user_offsets,
-                     int nbits) {
+                     int nbits, int32_t ru) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t s_wave_tot[2][kFusedWaves];
   __shared__ int32_t s_pads_live;
@@ -648,8 +694,12 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
     h->recv_capacity = d.cap;
     h->total = total;
     h->pads_live = s_pads_live;
+    h->run_units = ru;
     h->magic = kHandleMagic;
   }
+  // the run lists' lengths: set by the run-entry kernel that follows (no
+  // route: every list stays empty)
+  if (tid < kRunXcds) hv.header->stream_live[tid] = 0;
   for (int i = tid; i < kFusedWaves * E; i += nthr) s_cur[i] += s_offs[i % E];
   __syncthreads();
 
@@ -694,43 +744,69 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
 // prepare: run entries
 // ---------------------------------------------------------------------------
 
-// Run entries (after the slot map is final). One block per chunk of C tokens:
-// the chunk's routes to expert e hold a contiguous run of e's rows (rows of a
-// segment follow route order, and a chunk's routes are consecutive), starting
-// at the smallest of them. A route's entry goes to the count of the chunk's
-// routes of lower experts plus its row's offset in its run, so the entries of
-// a chunk are in ascending row order; the chunk's remaining entries (routes
-// without a row) are marked empty.
+// Run entries (after the slot map is final). One block per chunk of ru
+// units: the chunk's routes to expert e hold a contiguous run of e's rows
+// (rows of a segment follow route order, and a chunk's routes are
+// consecutive), starting at the smallest of them. A route's entry goes to the
+// count of the chunk's routes of lower experts plus its row's offset in its
+// run, so the chunk's entries are in ascending row order; its valid routes
+// dropped past the capacity then leave empty entries. The chunk's entries
+// start, in the list of stream c mod 8, after the valid routes of the
+// stream's earlier chunks (read from the units' flag words). With
+// write_live (routings of at most 8 units, prepared by the one-block kernel,
+// which writes no unit flags: each stream then has at most one chunk, whose
+// entries start its list) the block also publishes its stream's list length.
 constexpr int kRunThreads = 1024;
 
 __global__ void __launch_bounds__(kRunThreads)
-prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int64_t C) {
+prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int32_t ru,
+                    int32_t write_live) {
   extern __shared__ int32_t s_run[];                // base[E] (counts first), first[E]
   __shared__ int32_t s_wave_tot[kRunThreads / kWave];
   __shared__ int32_t s_total;
+  __shared__ int32_t s_valid;
+  __shared__ int32_t s_sbase;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & (kWave - 1), w = tid / kWave;
   const int E = d.E;
   int32_t* s_base = s_run;
   int32_t* s_first = s_run + E;
-  const int64_t CK = C * d.K;
+  const int32_t c = blockIdx.x;
+  const int64_t CK = (int64_t)ru * kUnitRoutes;
   const int64_t routes = d.T * (int64_t)d.K;
-  const int64_t s0 = (int64_t)blockIdx.x * CK;
+  const int64_t s0 = (int64_t)c * CK;
   const int64_t s1 = s0 + CK < routes ? s0 + CK : routes;
   const int n = (int)(s1 - s0);
   for (int e = tid; e < E; e += nthr) {
     s_base[e] = 0;
     s_first[e] = 0x7FFFFFFF;
   }
+  if (tid == 0) {
+    s_valid = 0;
+    s_sbase = 0;
+  }
   __syncthreads();
+  // the chunk's start in its stream's list
+  if (!write_live) {
+    const int32_t nprev = c / kRunXcds * ru;
+    int32_t vb = 0;
+    for (int32_t i = tid; i < nprev; i += nthr)
+      vb += hv.unit_flags[(c % kRunXcds + kRunXcds * (i / ru)) * ru + i % ru] >> 1;
+    for (int off = kWave / 2; off > 0; off >>= 1) vb += __shfl_xor(vb, off);
+    if (lane == 0 && vb != 0) atomicAdd(&s_sbase, vb);
+  }
+  int32_t nv = 0;
   for (int i = tid; i < n; i += nthr) {
+    const int64_t id = topk_idx[s0 + i];
+    nv += (id >= 0 && id < E) ? 1 : 0;
     const int32_t sl = hv.slot[s0 + i];
     if (sl >= 0) {
-      const int e = (int)topk_idx[s0 + i];
-      atomicAdd(&s_base[e], 1);
-      atomicMin(&s_first[e], sl);
+      atomicAdd(&s_base[id], 1);
+      atomicMin(&s_first[id], sl);
     }
   }
+  for (int off = kWave / 2; off > 0; off >>= 1) nv += __shfl_xor(nv, off);
+  if (lane == 0 && nv != 0) atomicAdd(&s_valid, nv);
   __syncthreads();
   // exclusive scan of the counts over experts, in place: a contiguous block
   // of experts per thread, a shuffle scan per wavefront, then wave totals
@@ -750,23 +826,28 @@ prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
   for (int q = 0; q < w; ++q) ex += s_wave_tot[q];
   for (int i = 0; i < per; ++i) {
     if (b0 + i < E) {
-      const int32_t c = s_base[b0 + i];
+      const int32_t cnt = s_base[b0 + i];
       s_base[b0 + i] = ex;
-      ex += c;
+      ex += cnt;
     }
   }
   if (tid == nthr - 1) s_total = ex;
   __syncthreads();
   const int total = s_total;
+  RunEntry* list = hv.runs + (int64_t)(c % kRunXcds) * run_stream_cap(d.num_units) + s_sbase;
   for (int i = tid; i < n; i += nthr) {
     const int32_t sl = hv.slot[s0 + i];
     if (sl >= 0) {
       const int e = (int)topk_idx[s0 + i];
-      const int pos = s_base[e] + (sl - s_first[e]);
-      hv.runs[s0 + pos] = RunEntry{sl, (int32_t)(s0 + i)};
+      list[s_base[e] + (sl - s_first[e])] = RunEntry{sl, (int32_t)(s0 + i)};
     }
   }
-  for (int i = total + tid; i < n; i += nthr) hv.runs[s0 + i] = RunEntry{-1, -1};
+  for (int i = total + tid; i < s_valid; i += nthr) list[i] = RunEntry{-1, -1};
+  if (write_live && tid == 0) {
+    hv.header->stream_live[c] = s_valid;
+    if (c == 0)
+      for (int x = (int)gridDim.x; x < kRunXcds; ++x) hv.header->stream_live[x] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -805,9 +886,6 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #endif
 #ifndef EP_BWD_BLOCKS_PER_CU
 #define EP_BWD_BLOCKS_PER_CU 16
-#endif
-#ifndef EP_REDUCE_CH
-#define EP_REDUCE_CH 1
 #endif
 #ifndef EP_BLOCKS_PER_CU
 #define EP_BLOCKS_PER_CU 128
@@ -1082,19 +1160,38 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
   }
 }
 
-// D over the run entries, for dense routings. Block i takes stream i mod 8
-// (the chunks i mod 8, i mod 8 + 8, ... of the run entries, one after
-// another) and in it 8P consecutive 1 KiB pieces, P per wavefront; piece q of
-// a stream is column piece q mod npc of the stream's entry q div npc. The
-// hardware deals blocks round-robin over the eight XCDs, so one stream's
-// blocks share one L2: a chunk's token rows are read from memory once and
-// then from that L2, and consecutive blocks of a stream write consecutive
-// pieces of the chunk's runs (the rows an expert receives from the chunk,
-// adjacent in memory). Each block also zeroes its slice of its XCD's share of
-// the pad rows. Every block runs once and exits, so blocks are issued in
-// order and each XCD's write fronts stay dense bands; measured on the
-// MI355X, contiguous runs of 128 KiB and more written this way reach
-// 6.5 TB/s against 5.1 TB/s for rows in scattered order.
+// D over the run entries, for every routing. Block (x, k) = (i mod 8, i div 8)
+// of the copy blocks takes stream x's list and in it the step of 8P
+// consecutive 1 KiB pieces starting at 8P k, P per wavefront and
+// interleaved, so that each step of a block writes 8 consecutive pieces; then
+// the steps 8P (k + bps), 8P (k + 2 bps), ... while the stream has pieces
+// (bps = blocks per stream). Piece q of a stream is column piece q mod npc
+// of the list's entry q div npc. The hardware deals blocks round-robin over
+// the eight XCDs, so one stream's blocks share one L2: a chunk's token rows
+// are read from memory once and then from that L2, and consecutive blocks
+// write consecutive pieces of the chunk's runs (the rows an expert receives
+// from the chunk, adjacent in memory). Each block also zeroes its slice of its
+// XCD's share of the zero rows (live pads; the tail under the tail policy).
+// Blocks are issued in order and, when the grid covers every step once (the
+// launcher sizes it for a dense routing, capped), run once and exit, so each
+// XCD's write front stays one dense band; measured on the MI355X, runs of
+// 128 KiB and more written this way reach 6.5 TB/s against 5.1 TB/s for rows
+// in scattered order. A routing with masked routes has shorter lists, read
+// from the header on the device: the same grid covers them with fewer steps
+// per block, and blocks past the end only zero their pad slice.
+//
+// The first step's entries are loaded before the header (they lie inside the
+// list's capacity whatever it holds), so that the header, entry and token
+// loads of a dense routing are two dependent rounds, not three.
+//
+// npf leading blocks, when the launcher asks for them, first stream the
+// token rows through the caches with plain loads: when the rows are few
+// (they fit the 256 MB Infinity Cache with room) and each is read by many
+// routes, they are then served from there instead of from HBM at the start
+// of every chunk. Measured on the MI355X with the caches flushed before the
+// op: dsv3 dispatch 139.9 -> 134.7 us, combine_bwd 138.3 -> 129.9 us; with
+// two routes per token (mixtral) it costs 7 us instead, so it is not used
+// there.
 //
 // P, the pieces per wavefront, depends on the row length and on the pad
 // fill. Measured on the MI355X with A/B runs on one device (dispatch /
@@ -1106,33 +1203,102 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // (qwen3) take 58.4 / 54.7 at P = 6 against 60.1 / 56.3 at P = 4, while a
 // launch-bound routing of 1 KiB rows in 16 blocks (T = 256) loses 0.8 µs at
 // P = 6, so six pieces need a grid that fills the device.
-#ifndef EP_RUN_PIECES_LONG
-#define EP_RUN_PIECES_LONG 3
-#endif
-#ifndef EP_RUN_PIECES_SHORT
-#define EP_RUN_PIECES_SHORT 4
-#endif
-
 constexpr int kRunWaves = 8;
-constexpr int kRunPiecesLong = EP_RUN_PIECES_LONG;    // rows of kRunLongRow pieces or more, pads filled
-constexpr int kRunPiecesShort = EP_RUN_PIECES_SHORT;  // the rest
-constexpr int kRunPiecesNarrow = 6;                   // rows of kRunNarrowRow pieces or fewer, pads filled
-constexpr int64_t kRunLongRow = 12;                   // 1 KiB pieces
+constexpr int kRunPiecesLong = 3;     // rows of kRunLongRow pieces or more, pads filled
+constexpr int kRunPiecesShort = 4;    // the rest
+constexpr int kRunPiecesNarrow = 6;   // rows of kRunNarrowRow pieces or fewer, pads filled
+constexpr int64_t kRunLongRow = 12;   // 1 KiB pieces
 constexpr int64_t kRunNarrowRow = 4;
 constexpr int64_t kRunNarrowMinBlocks = 2048;
+// Copy blocks per CU at most (the grid of a routing with masked routes is
+// sized for the dense case and capped here).
+constexpr int64_t kRunBlocksPerCU = 96;
+// Token rows streamed by leading blocks when they are at most this many bytes
+// in all, each row is at least kRunPrefetchMinRow bytes and each token has at
+// least kRunPrefetchMinK routes.
+constexpr int64_t kRunPrefetchMaxBytes = (int64_t)96 << 20;
+constexpr int kRunPrefetchMinK = 4;
+constexpr int64_t kRunPrefetchMinRow = 8192;
+constexpr int64_t kRunPrefetchBlocks = 2048;
 
-// Sizes of a run-entry copy, computed on the host; every index of the launch
-// is below 2^32 (the launcher checks), so all index arithmetic is 32-bit and
-// no 64-bit division sits before a wavefront's loads.
+// Sizes of a run-entry copy, computed on the host; every piece index of the
+// launch is below 2^32 (the launcher checks), so index arithmetic is 32-bit.
 struct RunGeom {
-  uint32_t npc;         // 1 KiB pieces per row
-  uint32_t CK;          // routes (entries) per chunk
-  uint32_t nch;         // chunks
-  uint32_t last_short;  // entries the last chunk lacks: nch*CK - T*K
-  uint32_t tok_blocks;  // blocks of the launch
+  uint32_t npc;       // 1 KiB pieces per row
+  uint32_t bps;       // copy blocks per stream
+  uint32_t npf;       // leading blocks that stream the token rows
+  uint32_t pf_per;    // 16-byte vectors each lane of a streaming block loads
+  uint32_t cap_pieces;  // pieces a stream's list can hold: scap * npc
+  int64_t scap;       // entries a stream's list can hold
 };
 
-template <int kRunTokPieces>
+namespace {
+
+// The entries of one step: piece base + 8 j + wv of the stream (j < P), its
+// column piece and entry; a piece past the list's capacity gets an empty entry
+// (and reads entry 0, so every load is in bounds and unconditional).
+template <int P>
+__device__ __forceinline__ void run_step_entries(const RunEntry* __restrict__ list,
+                                                 uint32_t base, uint32_t wv,
+                                                 const RunGeom& g, RunEntry (&ent)[P],
+                                                 uint32_t (&col)[P]) {
+  static_for<P>([&](auto j) {
+    const uint32_t q = base + j * kRunWaves + wv;
+    const bool in = q < g.cap_pieces;
+    const uint32_t qq = in ? q : 0u;
+    const uint32_t qe = qq / g.npc;
+    col[j] = qq - qe * g.npc;
+    ent[j] = list[qe];
+    if (!in) ent[j].row = -1;
+  });
+}
+
+// Copies one step's pieces: those below `pieces` whose entry names a row
+// below the capacity and a route of the routing. All token loads are issued
+// before the first store.
+template <int P>
+__device__ __forceinline__ void run_step_copy(const Dims& d, uint32_t base, uint32_t wv,
+                                              uint32_t lane, uint32_t pieces, uint32_t routes,
+                                              RunEntry (&ent)[P], const uint32_t (&col)[P],
+                                              const row16_t* __restrict__ src4,
+                                              const float* __restrict__ w,
+                                              row16_t* __restrict__ dst4,
+                                              float* __restrict__ dst_w) {
+  const int64_t V = d.V;
+  static_for<P>([&](auto j) {
+    if (base + j * kRunWaves + wv >= pieces || (int64_t)ent[j].row >= d.cap ||
+        (uint32_t)ent[j].route >= routes)
+      ent[j].row = -1;
+  });
+  row16_t val[P];
+  static_for<P>([&](auto j) {
+    const uint32_t t = ent[j].row >= 0 ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
+    const int64_t v = (int64_t)(col[j] * kWave + lane);
+    val[j] = load_row16<kScatterNtLoad>(src4 + (int64_t)t * V + (v < V ? v : V - 1));
+  });
+  // the weights of the pieces that start a row are loaded with the token
+  // slices, not after the stores, so that their latency overlaps
+  const bool weights = w != nullptr && dst_w != nullptr;
+  float wt[P];
+  static_for<P>([&](auto j) {
+    wt[j] = (weights && ent[j].row >= 0 && col[j] == 0) ? w[ent[j].route] : 0.0f;
+  });
+  consume(val);
+  static_for<P>([&](auto j) {
+    const int64_t v = (int64_t)(col[j] * kWave + lane);
+    if (ent[j].row >= 0 && v < V)
+      store_row16<kScatterNtStore>(dst4 + (int64_t)ent[j].row * V + v, val[j]);
+  });
+  if (weights && lane == 0) {
+    static_for<P>([&](auto j) {
+      if (ent[j].row >= 0 && col[j] == 0) dst_w[ent[j].row] = wt[j];
+    });
+  }
+}
+
+}  // namespace
+
+template <int P>
 __global__ void __launch_bounds__(kRunWaves * kWave)
 run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __restrict__ runs,
                 const int32_t* __restrict__ pad_rows, uint32_t* status,
@@ -1141,66 +1307,58 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t V = d.V;
-  const uint32_t tb = blockIdx.x;
-  // Block k of stream x holds pieces k*8P .. k*8P + 8P-1 of the stream,
-  // wavefront wv the pieces k*8P + 8j + wv (j < P): at each step the block
-  // writes 8 consecutive pieces. Entries and rows are loaded without
-  // conditions (a piece past the stream reads entry 0 and is dropped), so
-  // all loads of a step are in flight together.
-  const uint32_t x = tb % kRunXcds;
-  const uint32_t q0 = (tb / kRunXcds) * (kRunWaves * kRunTokPieces) + wv;
-  uint32_t len = 0;
-  if (x < g.nch) {
-    len = ((g.nch - 1 - x) / kRunXcds + 1) * g.CK;
-    if ((g.nch - 1) % kRunXcds == x) len -= g.last_short;
+  if (blockIdx.x < g.npf) {
+    // stream a slice of the token rows through the caches
+    const int64_t nvec = d.T * V;
+    const int64_t base = ((int64_t)blockIdx.x * kRunWaves + wv) * g.pf_per * kWave + lane;
+    row16_t acc = row16_t{0u, 0u, 0u, 0u};
+    for (uint32_t i = 0; i < g.pf_per; ++i) {
+      const int64_t vv = base + (int64_t)i * kWave;
+      if (vv < nvec) acc ^= src4[vv];
+    }
+    asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
+    return;
   }
-  const uint32_t pieces = len * g.npc;
-  RunEntry ent[kRunTokPieces];
-  uint32_t col[kRunTokPieces];
-  static_for<kRunTokPieces>([&](auto j) {
-    const uint32_t q = q0 + j * kRunWaves;
-    const bool in = q < pieces;
-    const uint32_t qq = in ? q : 0;
-    const uint32_t qe = qq / g.npc;
-    col[j] = qq - qe * g.npc;
-    const uint32_t c = qe / g.CK;
-    ent[j] = runs[in ? (x + c * kRunXcds) * g.CK + (qe - c * g.CK) : 0u];
-    if (!in) ent[j].row = -1;
-  });
+  const uint32_t tb = blockIdx.x - g.npf;
+  const uint32_t x = tb % kRunXcds;
+  const uint32_t k = tb / kRunXcds;
+  const RunEntry* __restrict__ list = runs + (int64_t)x * g.scap;
+  constexpr uint32_t kStep = kRunWaves * P;
+  // the first step's entries, before the header
+  RunEntry ent[P];
+  uint32_t col[P];
+  run_step_entries<P>(list, k * kStep, wv, g, ent, col);
   const HandleHeader hh = *h;
   if (!handle_matches(hh, d)) {
     if (tb == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
-  row16_t val[kRunTokPieces];
-  static_for<kRunTokPieces>([&](auto j) {
-    const uint32_t t = ent[j].row >= 0 ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
-    const int64_t v = (int64_t)(col[j] * kWave + lane);
-    val[j] = load_row16<kScatterNtLoad>(src4 + (int64_t)t * V + (v < V ? v : V - 1));
-  });
-  consume(val);
-  static_for<kRunTokPieces>([&](auto j) {
-    const int64_t v = (int64_t)(col[j] * kWave + lane);
-    if (ent[j].row >= 0 && v < V)
-      store_row16<kScatterNtStore>(dst4 + (int64_t)ent[j].row * V + v, val[j]);
-  });
-  if (w != nullptr && dst_w != nullptr && lane == 0) {
-    static_for<kRunTokPieces>([&](auto j) {
-      if (ent[j].row >= 0 && col[j] == 0) dst_w[ent[j].row] = w[ent[j].route];
-    });
+  // the list's length (read from the handle itself: indexing the header copy
+  // by x would put the copy in private memory), bounded by its capacity; an
+  // entry is used only if it names a row below the capacity and a route of
+  // the routing
+  const uint32_t live = (uint32_t)h->stream_live[x];
+  const uint32_t pieces = (live < (uint32_t)g.scap ? live : (uint32_t)g.scap) * g.npc;
+  const uint32_t routes = (uint32_t)(d.T * d.K);
+  if (k * kStep < pieces)
+    run_step_copy<P>(d, k * kStep, wv, lane, pieces, routes, ent, col, src4, w, dst4, dst_w);
+  // later steps, when the grid holds fewer blocks than the stream has steps
+  for (uint32_t b = (k + g.bps) * kStep; b < pieces; b += g.bps * kStep) {
+    RunEntry e2[P];
+    uint32_t c2[P];
+    run_step_entries<P>(list, b, wv, g, e2, c2);
+    run_step_copy<P>(d, b, wv, lane, pieces, routes, e2, c2, src4, w, dst4, dst_w);
   }
   if (d.fill_pads || d.zero_tail) {
     // Zero rows (the live pads, and the tail under the tail policy): their
     // pieces are split into kRunXcds contiguous shares and share x is split
     // over stream x's blocks in order, so the zeros of each XCD are written
     // as one dense band alongside its token runs (two pieces per wavefront
-    // and step). The launch has blocks whenever T > 0.
+    // and step).
     const ZeroRows zr = zero_rows_of(hh, d);
     const uint32_t all = (uint32_t)zr.n * g.npc;
     const uint32_t share = (all + kRunXcds - 1) / kRunXcds;
-    const uint32_t bpx = g.tok_blocks / kRunXcds;
-    const uint32_t qn = (share + bpx - 1) / bpx;
-    const uint32_t k = tb / kRunXcds;
+    const uint32_t qn = (share + g.bps - 1) / g.bps;
     const uint32_t send = (x + 1) * share < all ? (x + 1) * share : all;
     const uint32_t lo = x * share + k * qn;
     const uint32_t hi = lo + qn < send ? lo + qn : send;
@@ -1228,161 +1386,218 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 
 namespace {
 
-// acc (+)= the N elements of one 16-byte vector, widened exactly to fp32,
-// with the term kept only if `use`: acc = use ? (have ? acc + x : x) : acc,
-// written as selects so that every buffer is read on every path.
-template <int DT>
-__device__ __forceinline__ void accumulate_sel(float (&acc)[Payload<DT>::N], row16_t v,
-                                               bool use, bool have) {
-  static_for<Payload<DT>::N>([&](auto q) {
-    constexpr int i = q;
-    const float x = Payload<DT>::template get<i>(v);
-    const float s = acc[i] + x;
-    acc[i] = use ? (have ? s : x) : acc[i];
-  });
-}
-
-// Weighted form: the first kept term is the product w * x, later kept terms
-// are fused multiply-adds fma(w, x, acc) (one rounding each).
-template <int DT>
-__device__ __forceinline__ void accumulate_wsel(float (&acc)[Payload<DT>::N], row16_t v,
-                                                bool use, bool have, float w) {
-  static_for<Payload<DT>::N>([&](auto q) {
-    constexpr int i = q;
-    const float x = Payload<DT>::template get<i>(v);
-    const float f = __builtin_fmaf(w, x, acc[i]);
-    const float p = w * x;
-    acc[i] = use ? (have ? f : p) : acc[i];
-  });
-}
-
 }  // namespace
 
-// Items: (token, column block). The valid rows' slices are all loaded first
-// (up to G of them in flight per lane), then summed in fp32 in ascending k
-// from the first valid one, then rounded once to the payload type.
-template <int KT, int CH, bool WEIGHTED, int DT>
+// Items: (group of G consecutive tokens, 1 KiB column block), G a power of
+// two up to 64 / K, so that a group's routes fit one wavefront. Lane l loads
+// the slot of the group's route l (one coalesced load) and the wavefront
+// walks the group's valid routes in ascending route order, kReduceBatch row
+// slices in flight at a time. A token's slices are summed in fp32 in
+// ascending k from its first valid one; when its routes end, the sum is
+// rounded once to the payload type and stored; a token with no valid route
+// gets +0. Everything that steers the walk comes from a ballot, so its
+// branches are scalar.
+//
+// G follows the routing's density, read from the handle header on the
+// device: the largest power of two up to T*K / R (R the live valid routes),
+// so that a group holds about K valid routes, capped by the launcher (g_max)
+// so that the items still fill the grid. A dense routing (G = 1) loads a
+// token's K rows at once, as a per-token walk would; a sparse one (masking
+// leaves one in eight routes valid) keeps eight slices in flight per
+// wavefront instead of about one, and writes its tokens' zero rows from the
+// same wavefronts. The first item's G = 1 slots are loaded together with the
+// header and reloaded only when G > 1; later items' slots are loaded before
+// the current item's stores.
+constexpr int kReduceBatch = 8;
+
+template <int KT, bool WEIGHTED, int DT>
 __global__ void __launch_bounds__(kBlock)
 reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
                    const int32_t* __restrict__ slot, uint32_t* status,
                    const row16_t* __restrict__ src4, const float* __restrict__ rw,
                    const float* __restrict__ g_w, row16_t* __restrict__ dst4,
-                   float* __restrict__ dst_w) {
+                   float* __restrict__ dst_w, int g_max) {
   using P = Payload<DT>;
-  constexpr int G = KT > 0 ? KT : 8;
   const int K = KT > 0 ? KT : d.K;
   const int lane = lane_id();
   const int64_t V = d.V;
-  constexpr int64_t CB = (int64_t)kWave * CH;
-  const int64_t ncb = (V + CB - 1) / CB;
-  const int64_t n_items = d.T * ncb;
+  const int64_t ncb = (V + kWave - 1) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  int64_t it = wave_index();
-  if (it >= n_items) return;
-  // The first item's slots are loaded together with the header (both in
-  // bounds: the slot region has T*K entries whatever the header holds).
-  const HandleHeader hh = *h;
-  int32_t sl_first[KT > 0 ? KT : 1];
-  if constexpr (KT > 0) {
-    const int64_t t = it / ncb;
-    static_for<KT>([&](auto k) { sl_first[k] = slot[t * KT + k]; });
+  const int64_t routes = d.T * (int64_t)K;
+  const int64_t w0 = wave_index();
+  // items and their indices fit 32 bits whenever the buffers fit in memory;
+  // the 64-bit division stays for a launch where they would not
+  const bool small = d.T * ncb + nwaves < ((int64_t)1 << 31);
+  auto udiv = [&](int64_t x, int64_t y) -> int64_t {
+    return small ? (int64_t)((uint32_t)x / (uint32_t)y) : x / y;
+  };
+  if (w0 >= d.T * ncb) return;
+  // the first token's slots (the G = 1 guess) are loaded with the header
+  constexpr bool kUnrolled = KT > 0 && KT <= kReduceBatch;
+  int32_t sl1[kUnrolled ? KT : 1];
+  if constexpr (kUnrolled) {
+    const int64_t t = udiv(w0, ncb);
+    static_for<KT>([&](auto k) { sl1[k] = slot[t * KT + k]; });
   }
+  const HandleHeader hh = *h;
   if (!handle_matches(hh, d)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
+  int G = 1;
+  {
+    const int64_t live = (int64_t)hh.total < d.cap ? (int64_t)hh.total : d.cap;
+    const int64_t R = live - (int64_t)hh.pads_live;
+    while (2 * G <= g_max && (int64_t)2 * G * (R > 0 ? R : 1) <= routes) G *= 2;
+  }
 
-  bool first = true;
-  for (; it < n_items; it += nwaves) {
-    const int64_t t = it / ncb;
-    const int64_t cb = it - t * ncb;
-    const int64_t v0 = cb * CB + lane;
-    float acc[CH][P::N];
-    bool have = false;
-    if constexpr (KT > 0) {
-      int32_t sl[KT];
-      static_for<KT>([&](auto k) { sl[k] = first ? sl_first[k] : slot[t * KT + k]; });
-      first = false;
-      int32_t mine = -1;
-      static_for<KT>([&](auto k) {
-        if (lane == k) mine = sl[k];
-      });
-      if (cb == 0 && dst_w != nullptr) {
-        if (lane < KT) dst_w[t * KT + lane] = (mine >= 0 && g_w != nullptr) ? g_w[mine] : 0.0f;
-      }
-      // weighted form: lane k fetches the weight of route k, then every lane
-      // reads it back as a scalar
-      float wl = 0.0f;
-      if constexpr (WEIGHTED) {
-        if (lane < KT && mine >= 0) wl = rw[mine];
-      }
-      // Loads only for valid routes (uniform branches); the sums below read
-      // every buffer and keep or drop each term with a select, so no buffer
-      // is left possibly in flight at the end of an item.
-      row16_t buf[KT][CH];
-      static_for<KT>([&](auto k) {
-        if (sl[k] >= 0) {
-          const row16_t* srow = src4 + (int64_t)sl[k] * V;
-          static_for<CH>([&](auto j) {
-            const int64_t v = v0 + j * kWave;
-            buf[k][j] = load_row16<kReduceNtLoad>(srow + (v < V ? v : V - 1));
-          });
-        }
-      });
-      static_for<KT>([&](auto k) {
-        const bool use = sl[k] >= 0;
-        if constexpr (WEIGHTED) {
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
-          static_for<CH>([&](auto j) { accumulate_wsel<DT>(acc[j], buf[k][j], use, have, wk); });
-        } else {
-          static_for<CH>([&](auto j) { accumulate_sel<DT>(acc[j], buf[k][j], use, have); });
-        }
-        have |= use;
-      });
-    } else {
-      const int32_t sl = lane < K ? slot[t * K + lane] : -1;
-      const uint64_t vm = wave_ballot(sl >= 0);
-      if (cb == 0 && dst_w != nullptr && lane < K)
-        dst_w[t * K + lane] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
-      float wl = 0.0f;
-      if constexpr (WEIGHTED) {
-        if (sl >= 0) wl = rw[sl];
-      }
-      for (int k0 = 0; k0 < K; k0 += G) {
-        row16_t buf[G][CH];
-        static_for<G>([&](auto g) {
-          const int k = k0 + g;
-          if (k < K && ((vm >> k) & 1ull)) {
-            const int32_t r = __builtin_amdgcn_readlane(sl, k);
-            const row16_t* srow = src4 + (int64_t)r * V;
-            static_for<CH>([&](auto j) {
-              const int64_t v = v0 + j * kWave;
-              buf[g][j] = load_row16<kReduceNtLoad>(srow + (v < V ? v : V - 1));
-            });
-          }
+  if constexpr (kUnrolled) {
+    if (G == 1) {
+      // One token per item, its K routes unrolled at compile time: a dense
+      // routing spends less here than on the walk's bookkeeping.
+      bool first = true;
+      for (int64_t it = w0; it < d.T * ncb; it += nwaves) {
+        const int64_t t = udiv(it, ncb);
+        const int64_t cb = it - t * ncb;
+        const int64_t v = cb * kWave + lane;
+        const int64_t vc = v < V ? v : V - 1;
+        int32_t sl[KT];
+        static_for<KT>([&](auto k) { sl[k] = first ? sl1[k] : slot[t * KT + k]; });
+        first = false;
+        int32_t mine = -1;
+        static_for<KT>([&](auto k) {
+          if (lane == k) mine = sl[k];
         });
-        static_for<G>([&](auto g) {
-          const int k = k0 + g;
-          const bool use = k < K && ((vm >> k) & 1ull);
-          if constexpr (WEIGHTED) {
-            const float wk = __int_as_float(
-                __builtin_amdgcn_readlane(__float_as_int(wl), k < K ? k : 0));
-            static_for<CH>([&](auto j) {
-              accumulate_wsel<DT>(acc[j], buf[g][j], use, have, wk);
-            });
-          } else {
-            static_for<CH>([&](auto j) { accumulate_sel<DT>(acc[j], buf[g][j], use, have); });
-          }
+        if (cb == 0 && dst_w != nullptr && lane < KT)
+          dst_w[t * KT + lane] = (mine >= 0 && g_w != nullptr) ? g_w[mine] : 0.0f;
+        float wl = 0.0f;
+        if constexpr (WEIGHTED) {
+          if (lane < KT && mine >= 0) wl = rw[mine];
+        }
+        row16_t buf[KT];
+        static_for<KT>([&](auto k) {
+          if (sl[k] >= 0) buf[k] = load_row16<kReduceNtLoad>(src4 + (int64_t)sl[k] * V + vc);
+        });
+        // the terms are kept or dropped with selects, not branches, so that
+        // every buffer is read on every path and no load is left possibly in
+        // flight when the sum is stored
+        float acc[P::N];
+        bool have = false;
+        static_for<KT>([&](auto k) {
+          const bool use = sl[k] >= 0;
+          float wk = 0.0f;
+          if constexpr (WEIGHTED)
+            wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+          static_for<P::N>([&](auto q) {
+            constexpr int i = q;
+            const float x = P::template get<i>(buf[k]);
+            float term;
+            if constexpr (WEIGHTED) {
+              term = have ? __builtin_fmaf(wk, x, acc[i]) : wk * x;
+            } else {
+              term = have ? acc[i] + x : x;
+            }
+            acc[i] = use ? term : acc[i];
+          });
           have |= use;
         });
+        if (v < V)
+          store_row16<kReduceNtStore>(dst4 + t * V + v,
+                                      have ? P::pack(acc) : row16_t{0u, 0u, 0u, 0u});
       }
+      return;
     }
-    row16_t* drow = dst4 + t * V;
-    static_for<CH>([&](auto j) {
-      const int64_t v = v0 + j * kWave;
-      if (v < V)
-        store_row16<kReduceNtStore>(drow + v, have ? P::pack(acc[j]) : row16_t{0u, 0u, 0u, 0u});
-    });
+  }
+
+  // The walk over groups of G tokens.
+  const int GK = G * K;
+  const int64_t n_items = (d.T + G - 1) / G * ncb;
+  auto group_slot = [&](int64_t item) -> int32_t {
+    const int64_t s = udiv(item, ncb) * GK + lane;
+    return (lane < GK && s < routes) ? slot[s] : -1;
+  };
+  if (w0 >= n_items) return;
+  int32_t sl_next = group_slot(w0);
+  for (int64_t it = w0; it < n_items; it += nwaves) {
+    const int64_t g = udiv(it, ncb);
+    const int64_t cb = it - g * ncb;
+    const int32_t sl = sl_next;
+    const int64_t v = cb * kWave + lane;
+    const bool vin = v < V;
+    const int64_t vc = vin ? v : V - 1;
+    const int64_t t0 = g * G;
+    const int ntok = (int)((int64_t)G < d.T - t0 ? (int64_t)G : d.T - t0);
+    const int64_t s = g * GK + lane;
+    if (cb == 0 && dst_w != nullptr && lane < GK && s < routes)
+      dst_w[s] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
+    float wl = 0.0f;
+    if constexpr (WEIGHTED) {
+      if (sl >= 0) wl = rw[sl];
+    }
+    uint64_t vm = wave_ballot(sl >= 0);
+    float acc[P::N];
+    auto store_tok = [&](int tk, bool have) {
+      if (vin)
+        store_row16<kReduceNtStore>(dst4 + (t0 + tk) * V + v,
+                                    have ? P::pack(acc) : row16_t{0u, 0u, 0u, 0u});
+    };
+    int cur = -1;     // token (in the group) whose sum is in acc
+    int done = 0;     // tokens of the group stored so far
+    while (vm) {
+      int lb[kReduceBatch];
+      row16_t buf[kReduceBatch];
+      // the batch's routes (lane numbers, ascending), one load each; the
+      // branches are uniform, and a place past the end loads nothing
+      static_for<kReduceBatch>([&](auto j) {
+        lb[j] = vm ? __ffsll((unsigned long long)vm) - 1 : -1;
+        vm &= vm - 1;
+        if (lb[j] >= 0) {
+          const int32_t r = __builtin_amdgcn_readlane(sl, lb[j]);
+          buf[j] = load_row16<kReduceNtLoad>(src4 + (int64_t)r * V + vc);
+        }
+      });
+      static_for<kReduceBatch>([&](auto j) {
+        if (lb[j] >= 0) {
+          const int tk = lb[j] / K;
+          float wk = 0.0f;
+          if constexpr (WEIGHTED)
+            wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), lb[j]));
+          if (tk != cur) {
+            if (cur >= 0) {
+              store_tok(cur, true);
+              done = cur + 1;
+            }
+            for (; done < tk; ++done) store_tok(done, false);
+            cur = tk;
+            static_for<P::N>([&](auto q) {
+              constexpr int i = q;
+              const float x = P::template get<i>(buf[j]);
+              if constexpr (WEIGHTED) {
+                acc[i] = wk * x;
+              } else {
+                acc[i] = x;
+              }
+            });
+          } else {
+            static_for<P::N>([&](auto q) {
+              constexpr int i = q;
+              const float x = P::template get<i>(buf[j]);
+              if constexpr (WEIGHTED) {
+                acc[i] = __builtin_fmaf(wk, x, acc[i]);
+              } else {
+                acc[i] = acc[i] + x;
+              }
+            });
+          }
+        }
+      });
+    }
+    if (it + nwaves < n_items) sl_next = group_slot(it + nwaves);
+    if (cur >= 0) {
+      store_tok(cur, true);
+      done = cur + 1;
+    }
+    for (; done < ntok; ++done) store_tok(done, false);
   }
 }
 
@@ -1521,8 +1736,8 @@ constexpr int kScatterCH = EP_SCATTER_CH;
 constexpr int kScatterBlocksPerCU = EP_SCATTER_BLOCKS_PER_CU;
 constexpr int kScatterIlvBlocksPerCU = EP_SCATTER_ILV_BLOCKS_PER_CU;
 constexpr int64_t kScatterIlvMaxRow = EP_SCATTER_ILV_MAX_ROW;
-constexpr int kReduceCH = EP_REDUCE_CH;
 constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
+
 
 int grid_for(int64_t items, int num_cus) {
   const int64_t waves_per_block = kBlock / kWave;
@@ -1564,12 +1779,11 @@ row16_t* rows_out(void* p) { return static_cast<row16_t*>(p); }
 namespace {
 
 hipError_t launch_prepare_runs(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
-                               hipStream_t stream) {
+                               int32_t ru, int write_live, hipStream_t stream) {
   if (d.T == 0) return hipSuccess;
-  const int64_t C = run_chunk_tokens(d.T);
-  const int64_t chunks = (d.T + C - 1) / C;
+  const int64_t chunks = ((int64_t)d.num_units + ru - 1) / ru;
   hipLaunchKernelGGL(prepare_runs_kernel, dim3((unsigned)chunks), dim3(kRunThreads),
-                     2 * sizeof(int32_t) * (size_t)d.E, stream, d, hv, topk_idx, C);
+                     2 * sizeof(int32_t) * (size_t)d.E, stream, d, hv, topk_idx, ru, write_live);
   return hipGetLastError();
 }
 
@@ -1581,13 +1795,15 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   (void)num_cus;
   const int nbits = key_bits(d.E);
   const int U = d.num_units;
+  // run chunks sized from this layout's payload row
+  const int32_t ru = run_chunk_units(U, d.K, d.V * (int64_t)sizeof(row16_t));
   const size_t fused_lds = sizeof(int32_t) * ((size_t)(kFusedWaves + 3) * d.E + 2);
   if (d.T * (int64_t)d.K <= (int64_t)kPrepFusedMaxRoutes && fused_lds <= kLdsBudget) {
     hipLaunchKernelGGL(prepare_fused_kernel, dim3(1), dim3(kFusedWaves * kWave), fused_lds,
-                       stream, d, hv, topk_idx, user_counts, user_offsets, nbits);
+                       stream, d, hv, topk_idx, user_counts, user_offsets, nbits, ru);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_prepare_runs(d, hv, topk_idx, stream);
+    return launch_prepare_runs(d, hv, topk_idx, ru, 1, stream);
   }
   if (U > 0) {
     int nw1 = 8;
@@ -1598,19 +1814,15 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // The slot kernel also builds the run entries when a chunk is a whole
-  // number of units (at least two) and its blocks hold whole chunks;
-  // otherwise they take their own launch. Measured on the MI355X: this saves
-  // 1.3-2.2 us of prepare at 4 units per chunk and costs 6 us at 1 (eight
-  // chunk scans per block).
-  const int64_t ck = run_chunk_tokens(d.T) * (int64_t)d.K;
-  const int run_units = (d.T > 0 && ck % kUnitRoutes == 0) ? (int)(ck / kUnitRoutes) : 0;
+  // The slot kernel also builds the run entries when a chunk is two or more
+  // units and its blocks hold whole chunks; otherwise they take their own
+  // launch. Measured on the MI355X: this saves 1.3-2.2 us of prepare at 4
+  // units per chunk and costs 6 us at 1 (eight chunk scans per block).
   int nw2 = 8;
   int in_slots = 0;
-  if (run_units >= 2 && run_units <= 8) {
-    while (nw2 >= run_units && slots_lds_bytes(d.E, nw2, nw2 / run_units) > kLdsBudget) nw2 /= 2;
-    in_slots = nw2 >= run_units && nw2 % run_units == 0 &&
-               slots_lds_bytes(d.E, nw2, nw2 / run_units) <= kLdsBudget;
+  if (ru >= 2) {
+    while (nw2 >= ru && slots_lds_bytes(d.E, nw2, nw2 / ru) > kLdsBudget) nw2 /= 2;
+    in_slots = nw2 >= ru && nw2 % ru == 0 && slots_lds_bytes(d.E, nw2, nw2 / ru) <= kLdsBudget;
   }
   if (!in_slots) {
     nw2 = 8;
@@ -1619,11 +1831,11 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   int grid2 = (U + nw2 - 1) / nw2;
   if (grid2 < 1) grid2 = 1;
   hipLaunchKernelGGL(prepare_slots_kernel, dim3(grid2), dim3(nw2 * kWave),
-                     slots_lds_bytes(d.E, nw2, in_slots ? nw2 / run_units : 0), stream, d, hv,
-                     user_counts, user_offsets, in_slots ? run_units : 0, (int32_t)ck);
+                     slots_lds_bytes(d.E, nw2, in_slots ? nw2 / ru : 0), stream, d, hv,
+                     user_counts, user_offsets, ru, in_slots);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return in_slots ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, stream);
+  return in_slots ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 0, stream);
 }
 
 hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,
@@ -1650,53 +1862,55 @@ hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* 
 }
 
 hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
-                           const float* w, void* dst, float* dst_w, hipStream_t stream) {
-  // no token: no route, so no row and no pad row (a zeroed tail needs a grid
-  // the run entries do not size; the scatter takes it); no capacity: nothing
-  // to write
-  if (d.T == 0 || d.cap == 0) {
-    if (d.cap == 0 || !d.zero_tail) return hipSuccess;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidValue;
-    return launch_scatter_rows(d, hv, src, w, dst, dst_w, cus, stream);
-  }
+                           const float* w, void* dst, float* dst_w, int num_cus,
+                           hipStream_t stream) {
+  if (d.cap == 0) return hipSuccess;        // nothing to write
+  // no token: no route, so no entry and no pad row; a zeroed tail still
+  // needs a grid, which the scatter sizes from the capacity
+  if (d.T == 0)
+    return d.zero_tail ? launch_scatter_rows(d, hv, src, w, dst, dst_w, num_cus, stream)
+                       : hipSuccess;
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t routes = d.T * (int64_t)d.K;
-  const int64_t C = run_chunk_tokens(d.T);
-  const int64_t nch = (d.T + C - 1) / C;
-  // stream 0 holds the most chunks; a shorter stream's extra blocks copy no
-  // token piece (they still zero their slice of the pads)
-  const int64_t entries = (nch + kRunXcds - 1) / kRunXcds * C * d.K;
+  const int64_t scap = run_stream_cap(d.num_units);
+  const int64_t dense = run_stream_dense(d.num_units, routes);
   int P = !d.fill_pads ? kRunPiecesShort
           : npc >= kRunLongRow ? kRunPiecesLong
           : npc <= kRunNarrowRow ? kRunPiecesNarrow : kRunPiecesShort;
   // narrow rows take six pieces only while the grid still fills the device
   if (P == kRunPiecesNarrow &&
-      (entries * npc + kRunWaves * P - 1) / (kRunWaves * P) * kRunXcds < kRunNarrowMinBlocks)
+      (dense * npc + kRunWaves * P - 1) / (kRunWaves * P) * kRunXcds < kRunNarrowMinBlocks)
     P = kRunPiecesShort;
   const int64_t per_block = (int64_t)kRunWaves * P;
-  const int64_t grid = kRunXcds * ((entries * npc + per_block - 1) / per_block);
-  int64_t pad_rows_max = d.zero_tail ? d.cap : (int64_t)d.E * (d.A - 1);
-  if (pad_rows_max > d.cap) pad_rows_max = d.cap;
-  // 32-bit indices: pieces of a stream and of the pads, entries, blocks
+  int64_t bps = (dense * npc + per_block - 1) / per_block;
+  const int64_t bps_cap = (int64_t)num_cus * kRunBlocksPerCU / kRunXcds;
+  if (bps > bps_cap) bps = bps_cap;
+  if (bps < 1) bps = 1;
+  const int64_t zero_max = d.zero_tail ? d.cap : ((int64_t)d.E * (d.A - 1) < d.cap
+                                                      ? (int64_t)d.E * (d.A - 1) : d.cap);
+  // 32-bit piece indices: a stream's list, the steps past it, the zero rows
   const int64_t lim = (int64_t)1 << 31;
-  if (grid * per_block >= lim || routes * npc >= lim || nch * C * d.K >= lim ||
-      pad_rows_max * npc >= lim) {
+  if (scap * npc + bps * per_block >= lim || zero_max * npc >= lim) {
     // a size no buffer in memory reaches; the scatter takes any size
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidValue;
-    return launch_scatter_rows(d, hv, src, w, dst, dst_w, cus, stream);
+    return launch_scatter_rows(d, hv, src, w, dst, dst_w, num_cus, stream);
   }
   RunGeom g;
   g.npc = (uint32_t)npc;
-  g.CK = (uint32_t)(C * d.K);
-  g.nch = (uint32_t)nch;
-  g.last_short = (uint32_t)(nch * C * d.K - routes);
-  g.tok_blocks = (uint32_t)grid;
+  g.bps = (uint32_t)bps;
+  g.cap_pieces = (uint32_t)(scap * npc);
+  g.scap = scap;
+  g.npf = 0;
+  g.pf_per = 0;
+  const int64_t row_bytes = d.V * (int64_t)sizeof(row16_t);
+  if (d.K >= kRunPrefetchMinK && row_bytes >= kRunPrefetchMinRow &&
+      d.T * row_bytes <= kRunPrefetchMaxBytes) {
+    const int64_t nvec = d.T * d.V;
+    int64_t npf = (nvec + (int64_t)kRunWaves * kWave * 4 - 1) / ((int64_t)kRunWaves * kWave * 4);
+    if (npf > kRunPrefetchBlocks) npf = kRunPrefetchBlocks;
+    g.npf = (uint32_t)npf;
+    g.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
+  }
+  const int64_t grid = (int64_t)g.npf + kRunXcds * bps;
   if (P == kRunPiecesLong)
     hipLaunchKernelGGL(run_rows_kernel<kRunPiecesLong>, dim3((unsigned)grid),
                        dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
@@ -1715,23 +1929,28 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
 hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* src,
                               const float* rw, const float* g_w, void* dst, float* dst_w,
                               int num_cus, hipStream_t stream) {
-  const int64_t CB = (int64_t)kWave * kReduceCH;
-  const int64_t ncb = (d.V + CB - 1) / CB;
-  const int64_t items = d.T * ncb;
-  if (items == 0) return hipSuccess;
-  const int grid = grid_for(items, num_cus);
+  const int64_t ncb = (d.V + kWave - 1) / kWave;
+  if (d.T * ncb == 0) return hipSuccess;
+  // tokens per item: chosen on the device from the routing's density, at
+  // most g_max, the largest power of two up to 64 / K that leaves at least
+  // half a grid's worth of items
+  const int grid = grid_for(d.T * ncb, num_cus);
+  const int64_t half = (int64_t)grid * (kBlock / kWave) / 2;
+  int g_max = 1;
+  while (2 * g_max * d.K <= kWave && (d.T + 2 * g_max - 1) / (2 * g_max) * ncb >= half)
+    g_max *= 2;
   return with_dtype(d.dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
     return with_topk(d.K, [&](auto kt) {
       constexpr int KT = decltype(kt)::value;
       if (rw != nullptr) {
-        hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, true, DT>), dim3(grid),
-                           dim3(kBlock), 0, stream, d, hv.header, hv.slot, &hv.header->status,
-                           rows_in(src), rw, g_w, rows_out(dst), dst_w);
+        hipLaunchKernelGGL((reduce_rows_kernel<KT, true, DT>), dim3(grid), dim3(kBlock), 0,
+                           stream, d, hv.header, hv.slot, &hv.header->status, rows_in(src), rw,
+                           g_w, rows_out(dst), dst_w, g_max);
       } else {
-        hipLaunchKernelGGL((reduce_rows_kernel<KT, kReduceCH, false, DT>), dim3(grid),
-                           dim3(kBlock), 0, stream, d, hv.header, hv.slot, &hv.header->status,
-                           rows_in(src), nullptr, g_w, rows_out(dst), dst_w);
+        hipLaunchKernelGGL((reduce_rows_kernel<KT, false, DT>), dim3(grid), dim3(kBlock), 0,
+                           stream, d, hv.header, hv.slot, &hv.header->status, rows_in(src),
+                           nullptr, g_w, rows_out(dst), dst_w, g_max);
       }
       return hipGetLastError();
     });

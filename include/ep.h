@@ -183,12 +183,18 @@ size_t ep_handle_mem_size(const ep_layout_t* layout);
  *            region every payload op reads. A handle of maps_bytes serves the
  *            payload ops; ep_prepare needs all `bytes` (its scratch closes the
  *            handle).
- *   runs     [T*K] pairs (row, route): the run entries. The tokens are cut
- *            into chunks of C = min(256, ceil(T/8)) consecutive tokens, and
- *            chunk c owns entries [c*C*K, min((c+1)*C*K, T*K)): its routes
- *            that hold a row, in ascending row order, then (-1, -1) for
- *            its other routes. dispatch and combine_bwd read them under
- *            EP_LAYOUT_DENSE_ROUTING.
+ *   runs     8 lists of run_list_entries (row, route) int32 pairs: the run
+ *            entries that dispatch and combine_bwd copy by. The routes are
+ *            cut into chunks of run_units * 512 consecutive routes; chunk c
+ *            belongs to list c mod 8, and a list holds its chunks one after
+ *            another, each as its routes that hold a row in ascending row
+ *            order, then (-1, -1) for each of its valid routes dropped past
+ *            the capacity.
+ *   stream_live  int32 [8]: the number of entries in each list
+ *   run_units    int32: units of 512 routes per chunk (1, 2 or 4), chosen
+ *            by prepare from its layout's payload row size
+ *   run_list_entries  (a count, not an offset) the entries each list can
+ *            hold, 64 * ceil(T*K/512) + 2048
  * Every offset is a multiple of 256. Host only. */
 typedef struct ep_handle_regions {
   size_t status;
@@ -199,6 +205,9 @@ typedef struct ep_handle_regions {
   size_t bytes;
   size_t runs;
   size_t maps_bytes;
+  size_t stream_live;
+  size_t run_units;
+  size_t run_list_entries;
 } ep_handle_regions_t;
 
 ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* out);

@@ -102,6 +102,34 @@ class GpuRun:
         return gt, gw
 
 
+def check_run_entries(m: dict, slot: np.ndarray, topk_idx: np.ndarray, E: int):
+    """The run entries against their definition and the oracle's slot map:
+    chunks of run_units * 512 routes, chunk c in list c mod 8 after the
+    stream's earlier chunks; each chunk's routes that hold a row in ascending
+    row order, then (-1, -1) for each valid route dropped past the capacity;
+    each list's length in stream_live."""
+    runs, live, ru = m["runs"], m["stream_live"], int(m["run_units"][0])
+    assert ru in (1, 2, 4)
+    CK = ru * 512
+    routes = slot.size
+    ids = topk_idx.reshape(-1)
+    pos = np.zeros(8, np.int64)
+    for c in range((routes + CK - 1) // CK):
+        s0, s1 = c * CK, min((c + 1) * CK, routes)
+        x = c % 8
+        nvalid = int(((ids[s0:s1] >= 0) & (ids[s0:s1] < E)).sum())
+        e = runs[x, pos[x]:pos[x] + nvalid]
+        want = np.arange(s0, s1)[slot[s0:s1] >= 0]
+        n = len(want)
+        assert (e[n:] == -1).all(), f"chunk {c}: empty entries"
+        got_rows, got_routes = e[:n, 0], e[:n, 1]
+        assert (np.diff(got_rows) > 0).all(), f"chunk {c}: rows not ascending"
+        assert np.array_equal(np.sort(got_routes), want), f"chunk {c}: routes"
+        assert np.array_equal(slot[got_routes], got_rows), f"chunk {c}: rows of routes"
+        pos[x] += nvalid
+    assert np.array_equal(live, pos), "stream list lengths"
+
+
 def check_prepare(run: GpuRun, p: oracle.Prepared):
     m = run.maps()
     counts = run.counts.cpu().numpy()
@@ -112,6 +140,7 @@ def check_prepare(run: GpuRun, p: oracle.Prepared):
     assert np.array_equal(m["offsets"], p.offsets), "handle offsets"
     assert np.array_equal(m["slot"], p.slot), "slot map"
     assert np.array_equal(m["row_src"][:p.live], p.row_src[:p.live]), "row_src"
+    check_run_entries(m, p.slot, run.idx.cpu().numpy(), run.E)
     assert run.status() == p.status, "status"
 
 

@@ -63,7 +63,9 @@ def test_handle_size_and_regions():
     assert r.slot + 4 * 4096 * 8 <= r.row_src
     assert r.row_src + 4 * L.cap <= n
     assert r.runs % 256 == 0 and r.row_src + 4 * L.cap <= r.runs
-    assert r.runs + 8 * 4096 * 8 == r.maps_bytes  # the run entries close the maps
+    # the run entries close the maps: eight stream lists of 64 U + 2048
+    # entries each (U = 64 units of 512 routes), 8 bytes an entry
+    assert r.runs + 8 * (64 * 64 + 2048) * 8 == r.maps_bytes
     # prepare's scratch closes the handle: 64 units of 512 routes, 256-expert
     # histograms and one flag per unit, each part 256-byte aligned
     assert n - r.maps_bytes == 64 * 256 * 4 + 256

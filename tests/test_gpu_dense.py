@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_harness import GpuRun, check_all_ops, check_prepare, host_bf16, log
+from gpu_harness import GpuRun, check_all_ops, check_prepare, check_run_entries, host_bf16, log
 from test_gpu_dtypes import run_case
 from test_gpu_parity import EDGE, _edge_ids, _inputs, _random_payloads
 
@@ -29,25 +29,6 @@ def _gpu():
     oracle.build()
 
 
-def check_run_entries(runs: np.ndarray, slot: np.ndarray, T: int, K: int):
-    """The run entries against their definition and the oracle's slot map:
-    chunk c of C = min(256, ceil(T/8)) tokens owns entries [c*C*K, ...), its
-    routes that hold a row in ascending row order, then (-1, -1)."""
-    C = min(256, max(1, (T + 7) // 8))
-    CK = C * K
-    routes = T * K
-    for c in range((T + C - 1) // C):
-        s0, s1 = c * CK, min((c + 1) * CK, routes)
-        e = runs[s0:s1]
-        want = np.arange(s0, s1)[slot[s0:s1] >= 0]
-        n = len(want)
-        assert (e[n:] == -1).all(), f"chunk {c}: empty entries"
-        got_rows, got_routes = e[:n, 0], e[:n, 1]
-        assert (np.diff(got_rows) > 0).all(), f"chunk {c}: rows not ascending"
-        assert np.array_equal(np.sort(got_routes), want), f"chunk {c}: routes"
-        assert np.array_equal(slot[got_routes], got_rows), f"chunk {c}: rows of routes"
-
-
 def _dense_case(idx, E, A, H, cap, x, w, rows, g_result, g_recv, g_recv_w, label, dev=None):
     log(f"{label}: dense prepare T={idx.shape[0]} K={idx.shape[1]} E={E} A={A} H={H} cap={cap}")
     run = GpuRun(idx, E, A, H, cap, dense=True)
@@ -55,7 +36,7 @@ def _dense_case(idx, E, A, H, cap, x, w, rows, g_result, g_recv, g_recv_w, label
     p = oracle.prepare(idx, E, A, cap)
     check_prepare(run, p)
     if idx.shape[0] > 0:
-        check_run_entries(run.maps()["runs"], p.slot, idx.shape[0], idx.shape[1])
+        check_run_entries(run.maps(), p.slot, idx, E)
     check_all_ops(run, p, x, w, rows, g_result, g_recv, g_recv_w, label=label, dev=dev)
     return p
 

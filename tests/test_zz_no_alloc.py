@@ -32,6 +32,8 @@ def _maps(L, handle, live):
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in m.items()}
     out["row_src"] = out["row_src"][:live]
+    # each run list up to its length (the rest of the region is not written)
+    out["runs"] = np.concatenate([out["runs"][x, :out["stream_live"][x]] for x in range(8)])
     return out
 
 
