@@ -60,21 +60,21 @@ CEILING_BUFFER_BYTES = 1 << 30     # each pattern moves 1 GiB (or the largest fi
 KERNEL_OF_OP = {"dispatch": "run_rows_kernel", "combine_bwd": "run_rows_kernel",
                 "combine": "reduce_rows_kernel", "dispatch_bwd": "reduce_rows_kernel",
                 "combine_weighted": "reduce_rows_kernel",
-                "combine_weighted_bwd": "weighted_bwd_kernel",
+                "combine_weighted_bwd": "run_wbwd_kernel",
                 "dispatch_nopad": "run_rows_kernel",
                 "combine_bwd_nopad": "run_rows_kernel",
                 "combine_fp16": "reduce_rows_kernel",
                 "dispatch_fp32": "run_rows_kernel",
                 "combine_fp32": "reduce_rows_kernel"}
 PAYLOAD_KERNELS = ("scatter_rows_kernel", "reduce_rows_kernel", "weighted_bwd_kernel",
-                   "run_rows_kernel")
+                   "run_rows_kernel", "run_wbwd_kernel")
 PREPARE_KERNELS = ("prepare_hist_kernel", "prepare_slots_kernel", "prepare_fused_kernel",
                    "prepare_runs_kernel")
 
 COLD = "@cold"      # suffix of the launches timed after a cache flush
 
 
-def kernel_of(op: str, dense: bool = False) -> str:
+def kernel_of(op: str) -> str:
     """The library kernel that runs ``op`` (a cold launch runs the op's
     kernel)."""
     op = op[:-len(COLD)] if op.endswith(COLD) else op
@@ -156,7 +156,7 @@ def base_op(op: str) -> str:
     return op
 
 
-def attribute(kernel_names, schedule, dense=False):
+def attribute(kernel_names, schedule):
     """Pair the library's payload-kernel dispatches (demangled names in
     dispatch order, all other kernels already left out) with the ops recorded
     in launch order. Raises if the two do not line up."""
@@ -164,7 +164,7 @@ def attribute(kernel_names, schedule, dense=False):
         raise SystemExit(f"{len(kernel_names)} payload dispatches profiled but "
                          f"{len(schedule)} launches recorded")
     for i, (name, op) in enumerate(zip(kernel_names, schedule)):
-        if kernel_of(op, dense) not in name:
+        if kernel_of(op) not in name:
             raise SystemExit(f"dispatch {i}: {name} does not run {op}")
     return list(schedule)
 
@@ -180,24 +180,24 @@ def _read_csv_rows(directory: str, suffix: str):
 
 
 def _schedule(directory: str):
-    """(ops in launch order, whether the run took the dense-routing path)."""
+    """The ops of the payload launches, in launch order."""
     with open(os.path.join(directory, "schedule.json")) as f:
         d = json.load(f)
-    return d["ops"], bool(d.get("dense", False))
+    return d["ops"]
 
 
 def _is_payload(name: str) -> bool:
     return any(k in name for k in PAYLOAD_KERNELS)
 
 
-def _pmc_path(op: str, workload: str, dense: bool = False) -> str:
-    return os.path.join(PROFILE_DIR, f"{kernel_of(op, dense)}_{op}_{workload}_pmc.txt")
+def _pmc_path(op: str, workload: str) -> str:
+    return os.path.join(PROFILE_DIR, f"{kernel_of(op)}_{op}_{workload}_pmc.txt")
 
 
-def load_traffic(op: str, workload: str, src_hash: str, dense: bool = False):
+def load_traffic(op: str, workload: str, src_hash: str):
     """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
     used only when it was taken on the current kernel sources."""
-    path = _pmc_path(op, workload, dense)
+    path = _pmc_path(op, workload)
     if not os.path.exists(path):
         return None
     try:
@@ -234,9 +234,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         expected_kib = copy_mib * 1024.0
         factor = float(np.median([float(r["Counter_Value"]) for r in calib])) / expected_kib
         pay = [r for r in rows if _is_payload(r["Kernel_Name"])]
-        sched, dense = _schedule(d)
-        ops = attribute([r["Kernel_Name"] for r in pay], sched, dense)
-        res["dense"] = dense
+        sched = _schedule(d)
+        ops = attribute([r["Kernel_Name"] for r in pay], sched)
         per_op = {}
         for r, op in zip(pay, ops):
             per_op.setdefault(op, []).append(float(r["Counter_Value"]) / factor * 1024.0)
@@ -258,11 +257,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         if fb is None or wb is None:
             continue
         summary = dict(out)
-        kern = kernel_of(op, res["dense"])
-        summary.update({"op": op, "kernel": kern, "dense_routing": res["dense"],
+        kern = kernel_of(op)
+        summary.update({"op": op, "kernel": kern,
                         "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                         "hbm_bytes_per_launch": fb + wb})
-        path = _pmc_path(op, workload, res["dense"])
+        path = _pmc_path(op, workload)
         with open(path, "w") as f:
             f.write(f"# HBM traffic of {kern} ({op}), workload {workload}\n")
             f.write(f"# command: {cmd}\n")
@@ -286,8 +285,8 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
     trace = _read_csv_rows(trace_dir, "kernel_trace.csv")
     trace.sort(key=lambda r: int(r["Dispatch_Id"]))
     pay = [r for r in trace if _is_payload(r["Kernel_Name"])]
-    sched, dense = _schedule(trace_dir)
-    ops = attribute([r["Kernel_Name"] for r in pay], sched, dense)
+    sched = _schedule(trace_dir)
+    ops = attribute([r["Kernel_Name"] for r in pay], sched)
     per_op = {}
     for r, op in zip(pay, ops):
         per_op.setdefault(op, []).append(
@@ -320,7 +319,7 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
         f.write(f"{'op':24s} {'kernel':22s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
                 f"{'max_us':>9s}\n")
         for op, v in list(per_op.items()) + list(prep.items()):
-            kern = kernel_of(op, dense) if op.replace(COLD, "") in KERNEL_OF_OP else op
+            kern = kernel_of(op) if op.replace(COLD, "") in KERNEL_OF_OP else op
             f.write(f"{op:24s} {kern:22s} {len(v):6d} {np.mean(v):9.2f} {np.min(v):9.2f} "
                     f"{np.max(v):9.2f}\n")
     print(path, flush=True)
@@ -713,7 +712,7 @@ def main():
     if args.schedule_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.schedule_out)), exist_ok=True)
         with open(args.schedule_out, "w") as f:
-            json.dump({"ops": schedule, "dense": dense}, f)
+            json.dump({"ops": schedule}, f)
 
     def gbs(op, nb):
         return nb / (avg[op] * 1e-3) / 1e9
@@ -747,9 +746,9 @@ def main():
     dominant = max(("dispatch", "combine", "combine_bwd", "dispatch_bwd"),
                    key=lambda op: avg[op])
     src_hash = kernel_source_hash()
-    traffic = load_traffic(dominant, cfg.name, src_hash, dense)
+    traffic = load_traffic(dominant, cfg.name, src_hash)
     achieved = gbs(dominant, nbytes[dominant])
-    roofline = {"bound": "hbm", "kernel": f"{kernel_of(dominant, dense)} ({dominant})",
+    roofline = {"bound": "hbm", "kernel": f"{kernel_of(dominant)} ({dominant})",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -809,7 +808,7 @@ def main():
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} topk={K} alignment={A} "
                                f"routing={cfg.routing} cap={cap}",
                    "global_batch": T, "parallelism": "none (one GPU's share)",
-                   "dense_routing": dense},
+                   "masked_routes": not dense},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / pair_s, 1),
         "value_is": args.headline,

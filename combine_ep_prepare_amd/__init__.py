@@ -41,7 +41,6 @@ DTYPE_BF16 = 0
 DTYPE_FP16 = 1
 DTYPE_FP32 = 2
 LAYOUT_NO_PAD_FILL = 1
-LAYOUT_DENSE_ROUTING = 2
 LAYOUT_ZERO_TAIL = 4
 
 # payload type code -> torch dtype of the rows
@@ -59,20 +58,16 @@ ENTRY_POINTS = ("ep_recv_capacity_worst", "ep_handle_mem_size", "ep_handle_regio
 class Layout(C.Structure):
     """ep_layout_t. ``dtype`` is the payload type (a torch dtype, "bf16",
     "fp16", "fp32" or a DTYPE_* code); ``fill_pads=False`` sets
-    LAYOUT_NO_PAD_FILL; ``dense=True`` sets LAYOUT_DENSE_ROUTING (the caller
-    states that topk_idx holds no masked route: a speed hint for dispatch and
-    combine_bwd that never changes a result); ``zero_tail=True`` sets
-    LAYOUT_ZERO_TAIL (expert-major outputs also get zeros in the rows past the
-    live total)."""
+    LAYOUT_NO_PAD_FILL; ``zero_tail=True`` sets LAYOUT_ZERO_TAIL
+    (expert-major outputs also get zeros in the rows past the live total)."""
     _fields_ = [("num_tokens", C.c_int64), ("topk", C.c_int32), ("num_experts", C.c_int32),
                 ("alignment", C.c_int32), ("dtype", C.c_uint16), ("flags", C.c_uint16),
                 ("hidden", C.c_int64), ("recv_capacity", C.c_int64)]
 
     def __init__(self, num_tokens, topk, num_experts, alignment, hidden, recv_capacity,
-                 dtype=DTYPE_BF16, fill_pads=True, dense=False, zero_tail=False):
+                 dtype=DTYPE_BF16, fill_pads=True, zero_tail=False):
         code = dtype if isinstance(dtype, int) else _CODE_OF[dtype]
-        flags = ((0 if fill_pads else LAYOUT_NO_PAD_FILL) |
-                 (LAYOUT_DENSE_ROUTING if dense else 0) | (LAYOUT_ZERO_TAIL if zero_tail else 0))
+        flags = (0 if fill_pads else LAYOUT_NO_PAD_FILL) | (LAYOUT_ZERO_TAIL if zero_tail else 0)
         super().__init__(num_tokens, topk, num_experts, alignment, code, flags, hidden,
                          recv_capacity)
 

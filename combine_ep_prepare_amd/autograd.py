@@ -45,14 +45,11 @@ class EpRouting:
     """One prepared routing: handle, token counts and segment offsets. The
     handle does not depend on the payload type, so one routing serves bf16,
     fp16 and fp32 payloads; ``fill_pads=False`` leaves pad rows unwritten;
-    ``dense=True`` states that ``topk_idx`` holds no masked route (-1), which
-    lets dispatch and its backward copy rows in received-row order (faster;
-    the results are the same either way); ``zero_tail=False`` leaves the rows
-    past the live total unwritten."""
+    ``zero_tail=False`` leaves the rows past the live total unwritten."""
 
     def __init__(self, topk_idx: torch.Tensor, num_experts: int, alignment: int, hidden: int,
                  recv_capacity: Optional[int] = None, fill_pads: bool = True,
-                 dense: bool = False, zero_tail: bool = True):
+                 zero_tail: bool = True):
         if topk_idx.dtype != torch.int64:
             raise TypeError("topk_idx must be int64")
         T, K = topk_idx.shape
@@ -60,7 +57,6 @@ class EpRouting:
             recv_capacity = recv_capacity_worst(T, K, num_experts, alignment)
         self._dims = (T, K, num_experts, alignment, hidden, recv_capacity)
         self.fill_pads = fill_pads
-        self.dense = dense
         self.zero_tail = zero_tail
         self._layouts = {}
         self.layout = self.layout_for(torch.bfloat16)
@@ -75,7 +71,7 @@ class EpRouting:
         """The layout of this routing for payloads of ``dtype``."""
         if dtype not in self._layouts:
             self._layouts[dtype] = Layout(*self._dims, dtype=dtype, fill_pads=self.fill_pads,
-                                          dense=self.dense, zero_tail=self.zero_tail)
+                                          zero_tail=self.zero_tail)
         return self._layouts[dtype]
 
 

@@ -66,8 +66,7 @@ ep_status_t check_layout(const ep_layout_t* L) {
   if (L->alignment < 1) return EP_ERR_SHAPE;
   if (L->dtype != EP_DTYPE_BF16 && L->dtype != EP_DTYPE_FP16 && L->dtype != EP_DTYPE_FP32)
     return EP_ERR_SHAPE;
-  if ((L->flags &
-       ~(uint32_t)(EP_LAYOUT_NO_PAD_FILL | EP_LAYOUT_DENSE_ROUTING | EP_LAYOUT_ZERO_TAIL)) != 0)
+  if ((L->flags & ~(uint32_t)(EP_LAYOUT_NO_PAD_FILL | EP_LAYOUT_ZERO_TAIL)) != 0)
     return EP_ERR_SHAPE;
   if (L->hidden < 8 || L->hidden % 8 != 0 || L->hidden >= kInt32Limit) return EP_ERR_SHAPE;
   const int64_t routes = L->num_tokens * (int64_t)L->topk;
@@ -111,7 +110,6 @@ Dims dims_of(const ep_layout_t* L, int32_t num_units) {
   d.V = L->hidden * esize / 16;
   d.dtype = L->dtype;
   d.fill_pads = (L->flags & EP_LAYOUT_NO_PAD_FILL) ? 0 : 1;
-  d.dense = (L->flags & EP_LAYOUT_DENSE_ROUTING) ? 1 : 0;
   d.zero_tail = (L->flags & EP_LAYOUT_ZERO_TAIL) ? 1 : 0;
   return d;
 }

@@ -170,7 +170,6 @@ struct Dims {
   int64_t V;          // 16-byte vectors per payload row: H * element size / 16
   int32_t dtype;      // EP_DTYPE_* of the payload rows
   int32_t fill_pads;  // 1: payload ops zero the live pad rows; 0: leave them
-  int32_t dense;      // 1: the caller states every route holds a valid expert id
   int32_t zero_tail;  // 1: payload ops also zero rows [min(total, cap), cap)
 };
 

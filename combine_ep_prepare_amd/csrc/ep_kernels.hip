@@ -884,9 +884,6 @@ typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 #ifndef EP_SCATTER_ILV_BLOCKS_PER_CU
 #define EP_SCATTER_ILV_BLOCKS_PER_CU 32
 #endif
-#ifndef EP_BWD_BLOCKS_PER_CU
-#define EP_BWD_BLOCKS_PER_CU 16
-#endif
 #ifndef EP_BLOCKS_PER_CU
 #define EP_BLOCKS_PER_CU 128
 #endif
@@ -1234,6 +1231,21 @@ struct RunGeom {
 
 namespace {
 
+// A leading block's work: stream its slice of the token rows [T, H] through
+// the caches with plain loads.
+__device__ __forceinline__ void stream_token_rows(const Dims& d, const RunGeom& g,
+                                                  const row16_t* __restrict__ src4,
+                                                  uint32_t wv, uint32_t lane) {
+  const int64_t nvec = d.T * d.V;
+  const int64_t base = ((int64_t)blockIdx.x * kRunWaves + wv) * g.pf_per * kWave + lane;
+  row16_t acc = row16_t{0u, 0u, 0u, 0u};
+  for (uint32_t i = 0; i < g.pf_per; ++i) {
+    const int64_t vv = base + (int64_t)i * kWave;
+    if (vv < nvec) acc ^= src4[vv];
+  }
+  asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
+}
+
 // The entries of one step: piece base + 8 j + wv of the stream (j < P), its
 // column piece and entry; a piece past the list's capacity gets an empty entry
 // (and reads entry 0, so every load is in bounds and unconditional).
@@ -1308,15 +1320,7 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t V = d.V;
   if (blockIdx.x < g.npf) {
-    // stream a slice of the token rows through the caches
-    const int64_t nvec = d.T * V;
-    const int64_t base = ((int64_t)blockIdx.x * kRunWaves + wv) * g.pf_per * kWave + lane;
-    row16_t acc = row16_t{0u, 0u, 0u, 0u};
-    for (uint32_t i = 0; i < g.pf_per; ++i) {
-      const int64_t vv = base + (int64_t)i * kWave;
-      if (vv < nvec) acc ^= src4[vv];
-    }
-    asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
+    stream_token_rows(d, g, src4, wv, lane);
     return;
   }
   const uint32_t tb = blockIdx.x - g.npf;
@@ -1376,6 +1380,133 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
           store_row16<kScatterNtStore>(dst4 + r1 * V + v1, row16_t{0u, 0u, 0u, 0u});
         if (c1 == 0 && dst_w != nullptr && lane == 0) dst_w[r1] = 0.0f;
       }
+    }
+  }
+}
+
+// The weighted combine's backward over the run entries. For the received
+// row r of route s (token t = s / K) with weight w_r:
+//   grad_rows[r] = payload(fp32(w_r * g_t))    grad_w[r] = sum_h g_t[h] * y_r[h]
+// Block (x, k) of stream x takes the rows of R consecutive entries of x's
+// list per step (entries kR, (k + bps)R, ...), their R * npc pieces dealt to
+// the eight wavefronts as in the run copy (so the block writes each row's
+// pieces as one dense band, and a chunk's token rows are read from memory
+// once and then from its XCD's L2). Each piece's share of the dot product is
+// a per-lane chain of fused multiply-adds over the piece's elements, then a
+// fixed xor butterfly over the 64 lanes; the partials go to LDS, and one
+// thread per row sums its npc partials in column order. So the weight
+// gradient has the same bits on every run, and it sums each product through
+// at most N + 6 + npc roundings (N elements per 16-byte vector). Zero rows
+// (pads, and the tail under the tail policy) are zeroed, with their weight
+// gradients, in each XCD's share as in the run copy.
+constexpr int kWbwdPieces = 4;                 // pieces per wavefront and round
+constexpr int kWbwdMaxPartials = 1024;         // LDS partials of one block step
+
+template <int DT, bool WANT_W>
+__global__ void __launch_bounds__(kRunWaves * kWave)
+run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __restrict__ runs,
+                const int32_t* __restrict__ pad_rows, uint32_t* status,
+                const row16_t* __restrict__ g4, const row16_t* __restrict__ y4,
+                const float* __restrict__ rw, row16_t* __restrict__ o4,
+                float* __restrict__ grad_w, RunGeom g, uint32_t rows_per_step) {
+  using Pl = Payload<DT>;
+  __shared__ float s_part[kWbwdMaxPartials];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t V = d.V;
+  if (blockIdx.x < g.npf) {
+    stream_token_rows(d, g, g4, wv, lane);
+    return;
+  }
+  const uint32_t tb = blockIdx.x - g.npf;
+  const uint32_t x = tb % kRunXcds;
+  const uint32_t k = tb / kRunXcds;
+  const RunEntry* __restrict__ list = runs + (int64_t)x * g.scap;
+  const HandleHeader hh = *h;
+  if (!handle_matches(hh, d)) {
+    if (tb == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
+    return;
+  }
+  const uint32_t live0 = (uint32_t)h->stream_live[x];
+  const uint32_t live = live0 < (uint32_t)g.scap ? live0 : (uint32_t)g.scap;
+  const uint32_t routes = (uint32_t)(d.T * d.K);
+  const uint32_t R = rows_per_step;
+  constexpr uint32_t kRound = kRunWaves * kWbwdPieces;
+  for (uint32_t e0 = k * R; e0 < live; e0 += g.bps * R) {
+    const uint32_t nrows = live - e0 < R ? live - e0 : R;
+    const uint32_t npieces = nrows * g.npc;
+    for (uint32_t r0 = 0; r0 < npieces; r0 += kRound) {
+      RunEntry ent[kWbwdPieces];
+      uint32_t col[kWbwdPieces];
+      bool use[kWbwdPieces];
+      static_for<kWbwdPieces>([&](auto j) {
+        const uint32_t pp = r0 + j * kRunWaves + wv;
+        const bool in = pp < npieces;
+        const uint32_t pq = in ? pp : 0u;
+        const uint32_t ei = pq / g.npc;
+        col[j] = pq - ei * g.npc;
+        ent[j] = list[e0 + ei];
+        use[j] = in && ent[j].row >= 0 && (int64_t)ent[j].row < d.cap &&
+                 (uint32_t)ent[j].route < routes;
+      });
+      row16_t gv[kWbwdPieces], yv[kWbwdPieces];
+      float wk[kWbwdPieces];
+      static_for<kWbwdPieces>([&](auto j) {
+        const uint32_t t = use[j] ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
+        const int64_t r = use[j] ? (int64_t)ent[j].row : 0;
+        const int64_t v = (int64_t)(col[j] * kWave + lane);
+        const int64_t vc = v < V ? v : V - 1;
+        gv[j] = load_row16<kScatterNtLoad>(g4 + (int64_t)t * V + vc);
+        if constexpr (WANT_W) yv[j] = load_row16<kReduceNtLoad>(y4 + r * V + vc);
+        wk[j] = rw[r];
+      });
+      static_for<kWbwdPieces>([&](auto j) {
+        const int64_t v = (int64_t)(col[j] * kWave + lane);
+        float prod[Pl::N];
+        float pd = 0.0f;
+        static_for<Pl::N>([&](auto q) {
+          constexpr int i = q;
+          const float gi = Pl::template get<i>(gv[j]);
+          prod[i] = wk[j] * gi;
+          if constexpr (WANT_W) pd = __builtin_fmaf(gi, Pl::template get<i>(yv[j]), pd);
+        });
+        if (use[j] && v < V)
+          store_row16<kScatterNtStore>(o4 + (int64_t)ent[j].row * V + v, Pl::pack(prod));
+        if constexpr (WANT_W) {
+          pd = v < V ? pd : 0.0f;
+          for (int off = kWave / 2; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
+          const uint32_t pp = r0 + j * kRunWaves + wv;
+          if (lane == 0 && pp < npieces) s_part[pp] = pd;
+        }
+      });
+    }
+    if constexpr (WANT_W) {
+      __syncthreads();
+      if (threadIdx.x < nrows) {
+        const RunEntry e = list[e0 + threadIdx.x];
+        if (e.row >= 0 && (int64_t)e.row < d.cap && (uint32_t)e.route < routes) {
+          float sum = 0.0f;
+          for (uint32_t c = 0; c < g.npc; ++c) sum += s_part[threadIdx.x * g.npc + c];
+          grad_w[e.row] = sum;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (d.fill_pads || d.zero_tail) {
+    const ZeroRows zr = zero_rows_of(hh, d);
+    const uint32_t all = (uint32_t)zr.n * g.npc;
+    const uint32_t share = (all + kRunXcds - 1) / kRunXcds;
+    const uint32_t qn = (share + g.bps - 1) / g.bps;
+    const uint32_t send = (x + 1) * share < all ? (x + 1) * share : all;
+    const uint32_t lo = x * share + k * qn;
+    const uint32_t hi = lo + qn < send ? lo + qn : send;
+    for (uint32_t p0 = lo + wv; p0 < hi; p0 += kRunWaves) {
+      const int64_t r0 = zero_row(zr, pad_rows, p0 / g.npc);
+      const uint32_t c0 = p0 - (p0 / g.npc) * g.npc;
+      const int64_t v0 = (int64_t)(c0 * kWave + lane);
+      if (v0 < V) store_row16<kScatterNtStore>(o4 + r0 * V + v0, row16_t{0u, 0u, 0u, 0u});
+      if (WANT_W && c0 == 0 && lane == 0) grad_w[r0] = 0.0f;
     }
   }
 }
@@ -1737,6 +1868,8 @@ constexpr int kScatterBlocksPerCU = EP_SCATTER_BLOCKS_PER_CU;
 constexpr int kScatterIlvBlocksPerCU = EP_SCATTER_ILV_BLOCKS_PER_CU;
 constexpr int64_t kScatterIlvMaxRow = EP_SCATTER_ILV_MAX_ROW;
 constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
+// The token-group weighted backward's grid, in blocks per CU.
+constexpr int kBwdBlocksPerCU = 16;
 
 
 int grid_for(int64_t items, int num_cus) {
@@ -1957,9 +2090,13 @@ hipError_t launch_reduce_rows(const Dims& d, const HandleView& hv, const void* s
   });
 }
 
-hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* g,
-                               const void* y, const float* rw, void* grad_rows, float* grad_w,
-                               int num_cus, hipStream_t stream) {
+namespace {
+
+// The token-group form of the weighted backward: the fallback for sizes the
+// run form's 32-bit indices or LDS partials do not take.
+hipError_t launch_weighted_bwd_groups(const Dims& d, const HandleView& hv, const void* g,
+                                      const void* y, const float* rw, void* grad_rows,
+                                      float* grad_w, int num_cus, hipStream_t stream) {
   const int64_t npc = (d.V + kWave - 1) / kWave;
   const int64_t G = kWave / d.K;
   const int64_t max_units =
@@ -1967,7 +2104,7 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
       (d.fill_pads || d.zero_tail ? (d.cap * npc + kBwdWaves - 1) / kBwdWaves : 0);
   if (max_units == 0) return hipSuccess;
   int64_t grid = max_units;
-  const int64_t limit = (int64_t)num_cus * EP_BWD_BLOCKS_PER_CU;
+  const int64_t limit = (int64_t)num_cus * kBwdBlocksPerCU;
   if (grid > limit) grid = limit;
   return with_dtype(d.dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
@@ -1981,6 +2118,64 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
                          dim3(kBwdWaves * kWave), 0, stream, d, hv.header, hv.slot, hv.pad_rows,
                          &hv.header->status, rows_in(g), nullptr, rw, rows_out(grad_rows),
                          nullptr);
+    }
+    return hipGetLastError();
+  });
+}
+
+}  // namespace
+
+hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* g,
+                               const void* y, const float* rw, void* grad_rows, float* grad_w,
+                               int num_cus, hipStream_t stream) {
+  if (d.cap == 0) return hipSuccess;
+  const int64_t npc = (d.V + kWave - 1) / kWave;
+  const int64_t routes = d.T * (int64_t)d.K;
+  const int64_t scap = run_stream_cap(d.num_units);
+  const int64_t zero_max = d.zero_tail ? d.cap : ((int64_t)d.E * (d.A - 1) < d.cap
+                                                      ? (int64_t)d.E * (d.A - 1) : d.cap);
+  const int64_t lim = (int64_t)1 << 31;
+  if (d.T == 0 || npc > kWbwdMaxPartials || scap * npc >= lim || zero_max * npc >= lim)
+    return launch_weighted_bwd_groups(d, hv, g, y, rw, grad_rows, grad_w, num_cus, stream);
+  // rows per block step: as many whole rows as fill about 8 * kWbwdPieces
+  // pieces (one round), at least one
+  const int64_t round = (int64_t)kRunWaves * kWbwdPieces;
+  int64_t R = round / npc;
+  if (R < 1) R = 1;
+  const int64_t dense = run_stream_dense(d.num_units, routes);
+  int64_t bps = (dense + R - 1) / R;
+  const int64_t bps_cap = (int64_t)num_cus * kRunBlocksPerCU / kRunXcds;
+  if (bps > bps_cap) bps = bps_cap;
+  if (bps < 1) bps = 1;
+  RunGeom geo;
+  geo.npc = (uint32_t)npc;
+  geo.bps = (uint32_t)bps;
+  geo.cap_pieces = (uint32_t)(scap * npc);
+  geo.scap = scap;
+  geo.npf = 0;
+  geo.pf_per = 0;
+  const int64_t row_bytes = d.V * (int64_t)sizeof(row16_t);
+  if (d.K >= kRunPrefetchMinK && row_bytes >= kRunPrefetchMinRow &&
+      d.T * row_bytes <= kRunPrefetchMaxBytes) {
+    const int64_t nvec = d.T * d.V;
+    int64_t npf = (nvec + (int64_t)kRunWaves * kWave * 4 - 1) / ((int64_t)kRunWaves * kWave * 4);
+    if (npf > kRunPrefetchBlocks) npf = kRunPrefetchBlocks;
+    geo.npf = (uint32_t)npf;
+    geo.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
+  }
+  const int64_t grid = (int64_t)geo.npf + kRunXcds * bps;
+  return with_dtype(d.dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if (grad_w != nullptr) {
+      hipLaunchKernelGGL((run_wbwd_kernel<DT, true>), dim3((unsigned)grid),
+                         dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                         &hv.header->status, rows_in(g), rows_in(y), rw, rows_out(grad_rows),
+                         grad_w, geo, (uint32_t)R);
+    } else {
+      hipLaunchKernelGGL((run_wbwd_kernel<DT, false>), dim3((unsigned)grid),
+                         dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                         &hv.header->status, rows_in(g), nullptr, rw, rows_out(grad_rows),
+                         nullptr, geo, (uint32_t)R);
     }
     return hipGetLastError();
   });

@@ -20,8 +20,7 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 from torch import Tensor
 
-from . import (DTYPE_BF16, LAYOUT_DENSE_ROUTING, LAYOUT_NO_PAD_FILL, LAYOUT_ZERO_TAIL,
-               TORCH_DTYPE, Layout,
+from . import (DTYPE_BF16, LAYOUT_NO_PAD_FILL, LAYOUT_ZERO_TAIL, TORCH_DTYPE, Layout,
                combine as _combine,
                combine_bwd as _combine_bwd, combine_weighted as _combine_weighted,
                combine_weighted_bwd as _combine_weighted_bwd, dispatch as _dispatch,
@@ -42,7 +41,6 @@ def _layout(ll: Sequence[int], zero_tail: bool = False) -> Layout:
     the live total are zeros rather than uninitialised memory."""
     T, K, E, A, H, cap, dt, flags = ll
     return Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=not (flags & LAYOUT_NO_PAD_FILL),
-                  dense=bool(flags & LAYOUT_DENSE_ROUTING),
                   zero_tail=zero_tail or bool(flags & LAYOUT_ZERO_TAIL))
 
 

@@ -106,7 +106,6 @@ enum {
  * routing maps: one prepared handle serves both policies. */
 enum {
   EP_LAYOUT_NO_PAD_FILL = 1u,
-  EP_LAYOUT_DENSE_ROUTING = 2u,
   EP_LAYOUT_ZERO_TAIL = 4u
 };
 
@@ -119,17 +118,6 @@ enum {
  * the whole receive buffer (a parameter shared by every row, a reduction
  * over it) then sees zeros there instead of stale memory. It costs one
  * zero write per tail row. */
-
-/* EP_LAYOUT_DENSE_ROUTING: the caller states that every entry of topk_idx is
- * a valid expert id (no -1 masks), as when all of a layer's experts are local.
- * It is a speed hint for ep_dispatch and ep_combine_bwd only and never changes
- * a result: with it they copy the rows in received-row order, chunk by chunk
- * of the tokens, in one launch sized from T and K (the valid-route count of a
- * dense routing), which writes each expert's rows from a chunk as one
- * contiguous run. Without it (or for a routing that breaks the statement,
- * which is then still handled correctly but more slowly) they walk the tokens
- * and scatter each route's row. The routing maps the copy needs are built by
- * every ep_prepare, whatever its flags. */
 
 /*
  * Per-layer sizes (the role of the layer configuration in the common C API,
@@ -337,9 +325,17 @@ ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_me
  *                               product, then the payload rounding)
  *   grad_recv_topk_weights[r] = sum over h of grad[t,h] * expert_out[r,h]
  * Pad rows get +0 in both (not written with EP_LAYOUT_NO_PAD_FILL). The
- * weight gradient is an fp32 dot product over H accumulated in a fixed order
- * (bit-identical from run to run, but not the sequential order: it is within
- * the summation error bound of the exact dot product). With
+ * weight gradient is an fp32 dot product over H accumulated in a fixed order,
+ * bit-identical from run to run but not the sequential order: the row is cut
+ * into P = ceil(H * elem / 1024) pieces of 64 16-byte vectors (N elements
+ * each: 8 for bf16 and fp16, 4 for fp32); each lane chains N fused
+ * multiply-adds over its vector, six butterfly adds combine a piece's lanes,
+ * and the P partials are added in piece order. So every product passes
+ * through at most n = N + P + 5 fp32 roundings and the result is within
+ * gamma_n * sum_h |grad[t,h] * expert_out[r,h]| of the exact dot product,
+ * gamma_n = n u / (1 - n u), u = 2^-24. (Rows of more than 1024 pieces, or
+ * sizes whose piece indices pass 2^31, take a token-group form whose lanes
+ * chain N * P multiply-adds: n = N * P + 6 there.) With
  * grad_recv_topk_weights NULL only the row gradient is computed and
  * expert_out may be NULL. Rows at or past min(total, recv_capacity) are not
  * written.

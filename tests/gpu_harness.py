@@ -57,9 +57,12 @@ class GpuRun:
     """One handle: prepare, then any of the payload ops."""
 
     def __init__(self, topk_idx: np.ndarray, E: int, A: int, H: int, cap: int,
-                 stream=None, dense: bool = False):
+                 stream=None, prepare_dtype="bf16"):
         T, K = topk_idx.shape
-        self.layout = ep.Layout(T, K, E, A, H, cap, dense=dense)
+        self.layout = ep.Layout(T, K, E, A, H, cap)
+        # prepare sizes the run chunks from its layout's row: a layout of
+        # another payload type gives another chunk size, same results
+        self.prepare_layout = ep.Layout(T, K, E, A, H, cap, dtype=prepare_dtype)
         self.T, self.K, self.E, self.A, self.H, self.cap = T, K, E, A, H, cap
         self.stream = stream
         self.handle = ep.new_handle(self.layout)
@@ -68,7 +71,7 @@ class GpuRun:
         self.offsets = torch.full((E + 1,), -5, dtype=torch.int32, device="cuda")
 
     def prepare(self, with_offsets=True):
-        ep.prepare(self.layout, self.idx, self.counts, self.handle,
+        ep.prepare(self.prepare_layout, self.idx, self.counts, self.handle,
                    self.offsets if with_offsets else None, stream=self.stream)
 
     def maps(self) -> dict:
@@ -100,6 +103,18 @@ class GpuRun:
         gw = _fill_f32(self.T * self.K).view(self.T, self.K) if want_w else None
         ep.dispatch_bwd(self.layout, self.handle, g, g_w, gt, gw, stream=self.stream)
         return gt, gw
+
+
+def wbwd_gamma(H: int, dt: str = "bf16") -> float:
+    """gamma_n = n u / (1 - n u) for the weighted backward's weight gradient:
+    each product passes through at most n = N + P + 5 fp32 roundings, N the
+    elements of a 16-byte vector and P = ceil(H * elem / 1024) the row's
+    64-lane pieces (a fused multiply-add chain of N per lane, six butterfly
+    adds per piece, P - 1 adds over the pieces), the bound ep.h states."""
+    elem = 4 if dt == "fp32" else 2
+    n = 16 // elem + -(-(H * elem) // 1024) + 5
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)
 
 
 def check_run_entries(m: dict, slot: np.ndarray, topk_idx: np.ndarray, E: int):

@@ -101,9 +101,9 @@ def test_bad_layouts_rejected(kw, code):
 
 
 @pytest.mark.parametrize("dtype,flags,ok", [
-    (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True), (0, 2, True),
-    (1, 3, True), (0, 4, True), (2, 7, True), (3, 0, False), (0xFFFF, 0, False),
-    (0, 8, False), (0, 12, False), (0, 0x8001, False),
+    (0, 0, True), (1, 0, True), (2, 0, True), (0, 1, True), (2, 1, True), (0, 4, True),
+    (1, 5, True), (3, 0, False), (0xFFFF, 0, False), (0, 2, False), (0, 3, False),
+    (2, 7, False), (0, 8, False), (0, 12, False), (0, 0x8001, False),
 ])
 def test_payload_type_and_flags_validated(dtype, flags, ok):
     L = lay()
@@ -111,8 +111,8 @@ def test_payload_type_and_flags_validated(dtype, flags, ok):
     L.flags = flags
     n = ep.handle_mem_size(L)
     if ok:
-        # neither the payload type, the pad and tail policies nor the
-        # dense-routing hint changes the handle
+        # neither the payload type nor the pad and tail policies change the
+        # handle
         assert n == ep.handle_mem_size(lay())
     else:
         assert n == 0
@@ -238,7 +238,7 @@ def test_weighted_entry_points_error_paths():
     assert cwb(C.byref(L), P, n, P, P2, P2, MIS, P2, None) == ep.EP_ERR_ALIGN
 
 
-@pytest.mark.parametrize("flags", [0, 2, 4])
+@pytest.mark.parametrize("flags", [0, 1, 4])
 def test_token_buffers_required_even_without_receive_rows(flags):
     """A [T,...] buffer may be NULL only when T == 0: with tokens but no
     receive capacity the token-side pointers are still required, and the

@@ -48,7 +48,7 @@ def test_variant_bytes():
 def test_attribution_follows_the_launch_schedule():
     names = ["epmi::run_rows_kernel<3>", "epmi::reduce_rows_kernel<8, false, 0>",
              "epmi::run_rows_kernel<3>", "epmi::reduce_rows_kernel<8, true, 0>",
-             "epmi::weighted_bwd_kernel<0, true>", "epmi::run_rows_kernel<4>"]
+             "epmi::run_wbwd_kernel<0, true>", "epmi::run_rows_kernel<4>"]
     sched = ["dispatch", "combine", "dispatch_fp32", "combine_weighted",
              "combine_weighted_bwd", "combine_bwd_nopad"]
     assert bench.attribute(names, sched) == sched

@@ -57,9 +57,12 @@ def test_layout_list_round_trip():
 
 
 def test_layout_flags_round_trip():
-    # the pad policy and the dense-routing hint both survive the op schema
-    for fill, dense in ((True, False), (False, False), (True, True), (False, True)):
-        L = ep.Layout(16, 2, 4, 8, 64, 100, dtype="fp16", fill_pads=fill, dense=dense)
+    # the pad and tail policies survive the op schema; the ops that allocate
+    # an expert-major output add the tail policy
+    for fill, tail in ((True, False), (False, False), (True, True), (False, True)):
+        L = ep.Layout(16, 2, 4, 8, 64, 100, dtype="fp16", fill_pads=fill, zero_tail=tail)
         back = cops._layout(cops.layout_list(L))
         assert back.flags == L.flags and back.dtype == L.dtype
         assert cops.layout_list(back) == cops.layout_list(L)
+        forced = cops._layout(cops.layout_list(L), zero_tail=True)
+        assert forced.flags == L.flags | ep.LAYOUT_ZERO_TAIL

@@ -14,7 +14,7 @@ import oracle
 import workloads
 from combine_ep_prepare_amd import autograd as epa
 from combine_ep_prepare_amd import handle_maps
-from gpu_harness import host_bf16
+from gpu_harness import host_bf16, wbwd_gamma
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,10 @@ def test_identity_round_trip_and_none_weight_grad():
     assert w.grad is not None and torch.count_nonzero(w.grad) == 0
 
 
-@pytest.mark.parametrize("dense", [False, True])
-def test_weighted_round_trip_grads_match_oracle(dense):
+@pytest.mark.parametrize("zero_tail", [False, True])
+def test_weighted_round_trip_grads_match_oracle(zero_tail):
     cfg, r, idx, x, w = _setup(name="qwen3", T=500, H=256, seed=1)
-    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H, dense=dense)
+    routing = epa.EpRouting(idx, cfg.E, cfg.A, cfg.H, zero_tail=zero_tail)
     x = x.clone().requires_grad_(True)
     w = w.clone().requires_grad_(True)
     recv, recv_w = epa.dispatch(x, w, routing)
@@ -136,9 +136,7 @@ def test_fused_weighted_combine_grads():
     o_gr, o_gw, o_abs = oracle.combine_weighted_bwd(p, host_bf16(g), h_recv, h_recv_w)
     assert np.array_equal(host_bf16(recv.grad)[:live], o_gr[:live])
     got = recv_w.grad.cpu().numpy()[:live].astype(np.float64)
-    n = 8 * -(-(cfg.H // 8) // 64) + 6     # the kernel's summation depth (one row per wavefront)
-    gamma = n * 2.0 ** -24 / (1 - n * 2.0 ** -24)
-    assert (np.abs(got - o_gw[:live]) <= gamma * o_abs[:live] + 1e-45).all()
+    assert (np.abs(got - o_gw[:live]) <= wbwd_gamma(cfg.H) * o_abs[:live] + 1e-45).all()
     # then through dispatch's backward, bit for bit
     o_gt, o_gwt = oracle.dispatch_bwd(p, host_bf16(recv.grad), recv_w.grad.cpu().numpy())
     assert np.array_equal(host_bf16(x.grad), o_gt)

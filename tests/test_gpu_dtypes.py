@@ -5,7 +5,6 @@ policy and is compared with the oracle bit for bit (the weighted backward's
 weight gradient within its summation bound), outputs pre-filled with a
 canary so that rows that must stay unwritten are checked too.
 """
-import math
 import zlib
 
 import numpy as np
@@ -15,7 +14,7 @@ import torch
 import combine_ep_prepare_amd as ep
 import oracle
 import workloads
-from gpu_harness import log
+from gpu_harness import log, wbwd_gamma
 
 pytestmark = pytest.mark.gpu
 
@@ -88,23 +87,12 @@ def payload(rng, shape, dt, specials=False):
     return out
 
 
-def gamma(H, dt):
-    # one wavefront per row: each lane chains n_per_vec * ceil(V/64) fused
-    # multiply-adds, then 6 butterfly adds
-    n_per_vec = 4 if dt == "fp32" else 8
-    V = H * (4 if dt == "fp32" else 2) // 16
-    n = n_per_vec * math.ceil(V / 64) + 6
-    u = 2.0 ** -24
-    return n * u / (1 - n * u)
-
-
-def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense=False,
+def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False,
              zero_tail=False):
     T, K = idx.shape
-    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} dense={dense} zero_tail={zero_tail} "
+    log(f"dtypes {label}: dt={dt} fill_pads={fill_pads} zero_tail={zero_tail} "
         f"T={T} K={K} E={E} A={A} H={H} cap={cap}")
-    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads, dense=dense,
-                  zero_tail=zero_tail)
+    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, fill_pads=fill_pads, zero_tail=zero_tail)
     handle = ep.new_handle(L)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     ep.prepare(L, torch.from_numpy(idx).cuda(), counts, handle)
@@ -164,7 +152,7 @@ def run_case(label, idx, E, A, H, cap, dt, fill_pads, rng, specials=False, dense
         tok = np.zeros(cap, bool)
         tok[:live] = ~pad[:live]
         err = np.abs(got[tok] - o_gwr[tok])
-        assert (err <= gamma(H, dt) * o_abs[tok] + 1e-45).all(), f"{label} weighted_bwd w"
+        assert (err <= wbwd_gamma(H, dt) * o_abs[tok] + 1e-45).all(), f"{label} weighted_bwd w"
         want_pad = 0.0 if fill_pads else float(CANARY_W)
         assert (got[pad] == want_pad).all()
         assert (got[live:] == (0.0 if zero_tail else float(CANARY_W))).all()
@@ -222,20 +210,22 @@ def test_payload_type_special_values(dt):
              np.random.default_rng(77), specials=True)
 
 
-@pytest.mark.parametrize("dt,dense", [("fp16", False), ("fp32", False), ("fp32", True)])
-def test_full_size_dsv3_dispatch_combine(dt, dense):
+@pytest.mark.parametrize("dt,prep", [("fp16", "fp16"), ("fp32", "fp32"), ("fp32", "bf16")])
+def test_full_size_dsv3_dispatch_combine(dt, prep):
     # the DeepSeek-V3-shaped workload at full size: dispatch, combine and
-    # combine_bwd, by the scatter and (with the dense-routing hint, as the
-    # benchmark times fp32 dispatch) by the run-entry copy
+    # combine_bwd, from a handle prepared for the same payload type (run
+    # chunks sized for its rows, as the benchmark prepares its fp32 ops) and
+    # from one prepared for bf16 rows (chunks twice as many fp32 bytes)
     cfg = workloads.CONFIGS["dsv3"]
     r = workloads.make_routing(cfg)
     T, K, E, A, H = cfg.T, cfg.K, cfg.E, cfg.A, cfg.H
     cap = oracle.recv_capacity_worst(T, K, E, A)
-    log(f"dtypes full dsv3 {dt} dense={dense}: T={T} H={H} cap={cap}")
-    L = ep.Layout(T, K, E, A, H, cap, dtype=dt, dense=dense)
+    log(f"dtypes full dsv3 {dt}, prepared for {prep}: T={T} H={H} cap={cap}")
+    L = ep.Layout(T, K, E, A, H, cap, dtype=dt)
     handle = ep.new_handle(L)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    ep.prepare(L, torch.from_numpy(r.topk_idx).cuda(), counts, handle)
+    ep.prepare(ep.Layout(T, K, E, A, H, cap, dtype=prep), torch.from_numpy(r.topk_idx).cuda(),
+               counts, handle)
     p = oracle.prepare(r.topk_idx, E, A, cap)
     rng = np.random.default_rng(5)
     x = payload(rng, (T, H), dt)
@@ -258,10 +248,10 @@ def test_full_size_dsv3_dispatch_combine(dt, dense):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
-@pytest.mark.parametrize("dense", [False, True])
 @pytest.mark.parametrize("fill_pads", [True, False])
-@pytest.mark.parametrize("name,T,H", [("masked", 1500, 512), ("dsv3", 200, 1024)])
-def test_zero_tail_parity(dt, dense, fill_pads, name, T, H):
+@pytest.mark.parametrize("name,T,H", [("masked", 1500, 512), ("dsv3", 200, 1024),
+                                     ("mixtral", 3000, 256)])
+def test_zero_tail_parity(dt, fill_pads, name, T, H):
     # the tail policy: rows past the live total of every expert-major output
     # are zeros (canaries elsewhere where the pad policy leaves rows alone),
     # on both copy paths, with and without the pad fill
@@ -269,8 +259,8 @@ def test_zero_tail_parity(dt, dense, fill_pads, name, T, H):
     r = workloads.make_routing(c)
     cap = oracle.recv_capacity_worst(T, c.K, c.E, c.A)
     run_case(f"{name}-tail", r.topk_idx, c.E, c.A, H, cap, dt, fill_pads,
-             np.random.default_rng(zlib.crc32(f"{name}{dt}{dense}{fill_pads}".encode())),
-             dense=dense, zero_tail=True)
+             np.random.default_rng(zlib.crc32(f"{name}{dt}{fill_pads}".encode())),
+             zero_tail=True)
 
 
 def test_zero_tail_without_tokens():

@@ -87,17 +87,16 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 
 # dsv3 at T=700 and masked_hot take the two-kernel prepare; tiny and dsv3 at
-# T=400 (at most 4096 routes) the one-block prepare
-# (dense: dispatch and combine_bwd through the run entries; on masked_hot the
-# flag's statement does not hold and the results must not change)
-@pytest.mark.parametrize("name,T,H,dense", [
+# T=400 (at most 4096 routes) the one-block prepare; zero_tail: the rows past
+# the live total are zeroed on every replay too
+@pytest.mark.parametrize("name,T,H,zero_tail", [
     ("dsv3", 700, 1024, False), ("masked_hot", 2048, 512, False), ("tiny", 256, 512, False),
     ("dsv3", 400, 1024, False), ("dsv3", 700, 1024, True), ("tiny", 256, 512, True),
     ("masked_hot", 2048, 512, True)])
-def test_graph_replays_match_eager_and_oracle(name, T, H, dense):
+def test_graph_replays_match_eager_and_oracle(name, T, H, zero_tail):
     cfg = workloads.CONFIGS[name]
     cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
-    L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap, dense=dense)
+    L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap, zero_tail=zero_tail)
     g_step, e_step = Step(L), Step(L)
     _fill(g_step, cfg, 0)
     # warm up on a side stream, then capture
@@ -120,11 +119,15 @@ def test_graph_replays_match_eager_and_oracle(name, T, H, dense):
         graph.replay()
         torch.cuda.synchronize()
         # receive-side outputs are defined on live rows only (rows past the
-        # live total keep what an earlier routing left there)
+        # live total keep what an earlier routing left there), on every row
+        # under the tail policy, which zeroes the tail
         live = min(int(e_step.offsets[-1].item()), cap)
         for a, b in zip(g_step.outputs(), e_step.outputs()):
             if a.shape[0] == cap and cap != L.T:
-                a, b = a[:live], b[:live]
+                if zero_tail:
+                    assert not a[live:].view(torch.uint8).any(), f"replay {seed}: tail"
+                else:
+                    a, b = a[:live], b[:live]
             assert _same(a, b), f"replay {seed} differs from eager"
         assert ep.read_status(g_step.handle) == 0
         if seed == 2:

@@ -61,18 +61,21 @@ def _tail_untouched(t, live):
                  np.array([CANARY_BF16], np.uint16).view(np.int16)[0].item()).all())
 
 
-def _prepared(cfg, r, cap, dense):
-    L = ep.Layout(cfg.T, cfg.K, cfg.E, cfg.A, cfg.H, cap, dense=dense)
+def _prepared(cfg, r, cap, prepare_dtype):
+    # prepare's chunk size follows its layout's row: bf16 rows give chunks
+    # of 4 units, fp32 rows of 2; the payload ops use the bf16 layout
+    L = ep.Layout(cfg.T, cfg.K, cfg.E, cfg.A, cfg.H, cap)
+    Lp = ep.Layout(cfg.T, cfg.K, cfg.E, cfg.A, cfg.H, cap, dtype=prepare_dtype)
     handle = ep.new_handle(L)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    ep.prepare(L, torch.from_numpy(r.topk_idx).cuda(), counts, handle)
+    ep.prepare(Lp, torch.from_numpy(r.topk_idx).cuda(), counts, handle)
     return L, handle, counts
 
 
-@pytest.mark.parametrize("dense", [False, True])
-def test_large_dispatch_and_combine_bwd(case, dense):
+@pytest.mark.parametrize("prepare_dtype", ["bf16", "fp32"])
+def test_large_dispatch_and_combine_bwd(case, prepare_dtype):
     cfg, r, cap, p = case
-    L, handle, counts = _prepared(cfg, r, cap, dense)
+    L, handle, counts = _prepared(cfg, r, cap, prepare_dtype)
     m = ep.handle_maps(L, handle)
     assert np.array_equal(counts.cpu().numpy(), p.counts)
     assert np.array_equal(m["slot"].cpu().numpy(), p.slot)
@@ -80,7 +83,7 @@ def test_large_dispatch_and_combine_bwd(case, dense):
     live = p.live
     x = workloads.randn_bf16_torch((cfg.T, cfg.H), 31)
     w = torch.from_numpy(r.topk_weights).cuda()
-    log(f"large dense={dense}: dispatch")
+    log(f"large prepared for {prepare_dtype}: dispatch")
     recv = _canary_rows(cap, cfg.H)
     recv_w = torch.full((cap,), float(CANARY_F32), device="cuda")
     ep.dispatch(L, handle, x, w, recv, recv_w)
@@ -93,7 +96,7 @@ def test_large_dispatch_and_combine_bwd(case, dense):
     assert np.array_equal(got, want[:live]), "dispatch rows"
     assert np.array_equal(bits32(recv_w[:live].cpu().numpy()), bits32(want_w[:live]))
     del got, want
-    log(f"large dense={dense}: combine_bwd")
+    log(f"large prepared for {prepare_dtype}: combine_bwd")
     g = workloads.randn_bf16_torch((cfg.T, cfg.H), 32)
     gx = _canary_rows(cap, cfg.H)
     ep.combine_bwd(L, handle, g, gx)
@@ -108,7 +111,7 @@ def test_large_dispatch_and_combine_bwd(case, dense):
 
 def test_large_combine_and_dispatch_bwd(case):
     cfg, r, cap, p = case
-    L, handle, _ = _prepared(cfg, r, cap, False)
+    L, handle, _ = _prepared(cfg, r, cap, "bf16")
     live = p.live
     log("large: combine")
     Y = workloads.randn_bf16_torch((cap, cfg.H), 33)

@@ -1,12 +1,14 @@
 """Randomised GPU parity over shapes: top-k from 1 to 64 (every token-group
 size of the scatter), experts 1 to 400, alignments 1 to 128, ragged hidden
-sizes (short rows, long rows, and rows around the scatter's 8 KiB switch),
+sizes (short rows, long rows, and rows around the copies' 8 KiB prefetch
+rule),
 routings around the one-block prepare's cutover, masked, repeated and out-of-range ids, tight and overflowing
 capacities, every payload type and both pad policies. Each case runs every
 op through the C ABI against the oracle, bit for bit (the weighted backward's
 weight gradient within its summation bound), with canaries in every output.
 The cases are drawn from a fixed seed, so the set is the same on every run,
-and each runs twice: without and with the dense-routing hint.
+and each runs twice: without and with the tail policy (rows past the live
+total zeroed).
 """
 import zlib
 
@@ -46,7 +48,7 @@ def _cases(n=24):
 
 @pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _cases(),
                          ids=lambda v: str(v) if not isinstance(v, str) else v)
-def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, dense=False):
+def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, zero_tail=False):
     rng = np.random.default_rng(zlib.crc32(f"random-shape-{i}".encode()))
     if kind == "distinct":
         idx = np.argsort(rng.random((T, max(E, K))), axis=1)[:, :K] if T else \
@@ -61,11 +63,11 @@ def test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, dense=False):
     idx = np.asarray(idx, np.int64).reshape(T, K)
     worst = T * K + E * (A - 1)
     cap = {"worst": worst, "tight": worst // 2, "zero": 0}[cap_kind]
-    run_case(f"random{i}", idx, E, A, H, cap, dt, fill, rng, dense=dense)
+    run_case(f"random{i}", idx, E, A, H, cap, dt, fill, rng, zero_tail=zero_tail)
 
 
 def _long_row_cases(n=8):
-    # rows of 8 to 19 KiB: the scatter's plain unit order and 16-per-CU grid
+    # rows of 8 to 19 KiB: the copies stream the token rows ahead (K >= 4)
     rng = np.random.default_rng(20261203)
     out = []
     for i in range(n):
@@ -90,7 +92,7 @@ def test_random_long_rows(i, T, K, E, A, H, dt, fill, kind, cap_kind):
 
 def _boundary_cases(n=12):
     # routings around the one-block prepare's 4096-route cutover, and rows
-    # around the scatter's 8 KiB switch between its two unit orders
+    # around the copies' 8 KiB prefetch rule
     rng = np.random.default_rng(20261204)
     out = []
     for i in range(n):
@@ -120,7 +122,7 @@ def test_random_boundaries(i, T, K, E, A, H, dt, fill, kind, cap_kind):
 @pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind",
                          _cases() + _long_row_cases() + _boundary_cases(),
                          ids=lambda v: str(v) if not isinstance(v, str) else v)
-def test_random_dense_routing(i, T, K, E, A, H, dt, fill, kind, cap_kind):
-    """Every random case again with EP_LAYOUT_DENSE_ROUTING: the run-entry
-    copy, exact whether or not the routing masks routes."""
-    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, dense=True)
+def test_random_zero_tail(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+    """Every random case again under the tail policy: the rows past the live
+    total of every expert-major output are zeros, the rest unchanged."""
+    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, zero_tail=True)

@@ -3,14 +3,13 @@
 Forward and the row gradient are bit-exact against the oracle. The weight
 gradient is a dot product over H whose order the method does not fix; it is
 compared with the oracle's double-precision dot within the summation error
-bound of the kernel's fixed order: one wavefront takes the whole row, each
-lane chains 8 * ceil(V/64) fused multiply-adds over its 16-byte vectors
-(V = H/8 of them per row), then 6 butterfly adds combine the 64 lanes, so
-|got - exact| <= gamma_n * sum_h |g_h y_h| with n = 8 * ceil(V/64) + 6 and
-gamma_n = n u / (1 - n u), u = 2^-24. It must also be bit-identical from run
-to run.
+bound of the kernel's fixed order: each 64-lane piece of a row (P =
+ceil(V/64) of them, V = H/8 16-byte vectors) is a per-lane chain of 8 fused
+multiply-adds, then 6 butterfly adds over the lanes, and the P partials are
+summed in piece order, so |got - exact| <= gamma_n * sum_h |g_h y_h| with
+n = 8 + P + 5 and gamma_n = n u / (1 - n u), u = 2^-24. It must also be
+bit-identical from run to run.
 """
-import math
 import zlib
 
 import numpy as np
@@ -20,7 +19,7 @@ import torch
 import combine_ep_prepare_amd as ep
 import oracle
 import workloads
-from gpu_harness import (CANARY_BF16, CANARY_F32, GpuRun, _fill_bf16, _fill_f32, bits32,
+from gpu_harness import (CANARY_BF16, wbwd_gamma, CANARY_F32, GpuRun, _fill_bf16, _fill_f32, bits32,
                          dev_bf16, dev_f32, host_bf16, host_f32, log)
 
 pytestmark = pytest.mark.gpu
@@ -31,12 +30,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     oracle.build()
-
-
-def _gamma(H):
-    n = 8 * math.ceil(H / 8 / 64) + 6
-    u = 2.0 ** -24
-    return n * u / (1 - n * u)
 
 
 def _case(label, idx, E, A, H, cap, rng):
@@ -64,7 +57,7 @@ def _case(label, idx, E, A, H, cap, rng):
     got = host_f32(gw).astype(np.float64)
     assert (got[live:] == float(CANARY_F32)).all(), label          # untouched past live
     err = np.abs(got[:live] - o_gw[:live])
-    bound = _gamma(H) * o_abs[:live] + 1e-45
+    bound = wbwd_gamma(H) * o_abs[:live] + 1e-45
     assert (err <= bound).all(), (label, float((err / np.maximum(bound, 1e-300)).max()))
     pad = p.row_src[:live] < 0
     assert (bits32(host_f32(gw))[:live][pad] == 0).all()
@@ -92,7 +85,8 @@ def test_weighted_parity(name, T, H):
 @pytest.mark.parametrize("label,T,K,E,A,H", [("generic_k3", 300, 3, 16, 4, 64),
                                              ("generic_k12", 200, 12, 40, 8, 136),
                                              ("one_route", 333, 1, 8, 16, 520),
-                                             ("overflow", 500, 8, 32, 16, 64)])
+                                             ("overflow", 500, 8, 32, 16, 64),
+                                             ("wide_rows", 96, 4, 16, 4, 20488)])
 def test_weighted_edge_cases(label, T, K, E, A, H):
     rng = np.random.default_rng(zlib.crc32(label.encode()))
     keys = rng.random((T, max(E, K)))

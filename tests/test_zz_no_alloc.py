@@ -37,13 +37,14 @@ def _maps(L, handle, live):
     return out
 
 
-@pytest.mark.parametrize("dense", [False, True])
-def test_prepare_static_matches_prepare(dense):
+# the payload type sizes the run chunks (fp32 rows: half the routes a chunk)
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_prepare_static_matches_prepare(dt):
     for name, T, H in (("dsv3", 4096, 1024), ("masked_hot", 1500, 512), ("tiny", 256, 512)):
         cfg = workloads.scaled(workloads.CONFIGS[name], T=T, H=H)
         r = workloads.make_routing(cfg)
         cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
-        L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap, dense=dense)
+        L = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap, dtype=dt)
         regions = ep.handle_regions(L)
         log(f"prepare_static {name}: T={T} K={cfg.K} E={cfg.E} routes={T * cfg.K} "
             f"maps {regions.maps_bytes} of {regions.bytes} bytes")
@@ -68,7 +69,9 @@ def test_prepare_static_matches_prepare(dense):
         assert np.array_equal(b["slot"], p.slot)
         assert np.array_equal(b["row_src"], p.row_src[:p.live])
         assert ep.read_status(h_st) == p.status == ep.read_status(h_ref)
-        # every payload op run from either handle gives the same bits
+        # every payload op run from either handle gives the same bits (a
+        # handle serves every payload type: bf16 payloads here)
+        Lb = ep.Layout(T, cfg.K, cfg.E, cfg.A, H, cap)
         x = workloads.randn_bf16_torch((T, H), 40)
         w = torch.from_numpy(r.topk_weights).cuda()
         Y = workloads.randn_bf16_torch((cap, H), 41)
@@ -76,14 +79,14 @@ def test_prepare_static_matches_prepare(dense):
         for h in (h_ref, h_st):
             recv = torch.zeros(cap, H, dtype=torch.bfloat16, device="cuda")
             recv_w = torch.zeros(cap, device="cuda")
-            ep.dispatch(L, h, x, w, recv, recv_w)
+            ep.dispatch(Lb, h, x, w, recv, recv_w)
             res = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-            ep.combine(L, h, Y, res)
+            ep.combine(Lb, h, Y, res)
             gx = torch.zeros(cap, H, dtype=torch.bfloat16, device="cuda")
-            ep.combine_bwd(L, h, x, gx)
+            ep.combine_bwd(Lb, h, x, gx)
             gt = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
             gw = torch.empty(T, cfg.K, device="cuda")
-            ep.dispatch_bwd(L, h, Y, recv_w, gt, gw)
+            ep.dispatch_bwd(Lb, h, Y, recv_w, gt, gw)
             outs.append([recv, recv_w, res, gx, gt, gw])
         torch.cuda.synchronize()
         for u, v in zip(*outs):
