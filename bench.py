@@ -431,6 +431,57 @@ def measure_ceilings(T, K, H, launches, warmup):
     return out
 
 
+PREPARE_SWEEP_T = (4096, 16384, 65536, 131072, 262144, 524288)
+
+
+def prepare_sweep(workload: str, steps: int, warmup: int):
+    """prepare's time against the number of routes: the workload's routing
+    recipe at several token counts, prepare timed alone (back to back, HIP
+    events on its stream), one JSON line."""
+    import numpy as np
+    import torch
+
+    import combine_ep_prepare_amd as ep
+    import workloads
+
+    torch.cuda.set_device(0)
+    base = workloads.CONFIGS[workload]
+    stream = torch.cuda.current_stream()
+    points = []
+    for T in PREPARE_SWEEP_T:
+        cfg = workloads.scaled(base, T=T)
+        r = workloads.make_routing(cfg)
+        cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
+        L = ep.Layout(T, cfg.K, cfg.E, cfg.A, cfg.H, cap)
+        handle = ep.new_handle(L)
+        idx = torch.from_numpy(r.topk_idx).cuda()
+        counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+        for _ in range(warmup):
+            ep.prepare(L, idx, counts, handle, offsets)
+        evs = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ep.prepare(L, idx, counts, handle, offsets)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        assert ep.read_status(handle) & ~ep.STATUS_OVERFLOW == 0
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        routes = T * cfg.K
+        points.append({"T": T, "routes": routes, "units": -(-routes // 512),
+                       "avg_us": round(float(np.mean(us)), 2),
+                       "median_us": round(float(np.median(us)), 2),
+                       "ns_per_route": round(float(np.median(us)) * 1e3 / routes, 3)})
+        log(f"prepare T={T}: {points[-1]['median_us']} us")
+        del handle, idx
+    print(json.dumps({"metric": "prepare_us_vs_routes", "workload": workload, "K": base.K,
+                      "E": base.E, "A": base.A, "steps": steps, "warmup": warmup,
+                      "points": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +512,9 @@ def main():
                     help="write profiles/*_pmc.txt from two rocprofv3 counter runs")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run")
+    ap.add_argument("--prepare-sweep", action="store_true",
+                    help="time prepare alone on the workload's routing recipe at token "
+                         "counts from 4096 to 524288 and print one JSON line")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
@@ -475,6 +529,9 @@ def main():
         print("bench.py measures one GPU's share of the path; the library has no "
               "multi-GPU path, so only --gpus 1 runs.", file=sys.stderr)
         sys.exit(2)
+    if args.prepare_sweep:
+        prepare_sweep(args.workload, args.steps, args.warmup)
+        return
 
     import numpy as np
     import torch

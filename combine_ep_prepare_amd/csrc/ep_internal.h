@@ -97,9 +97,29 @@ inline int32_t prep_units(int64_t routes) {
   return (int32_t)((routes + kUnitRoutes - 1) / kUnitRoutes);
 }
 
-// Bytes of prepare's per-unit histograms (the first part of its scratch).
+// LDS one prepare block may take.
+constexpr size_t kPrepLdsBudget = 65536;
+
+// Units per block of the histogram kernel: eight wave-private E-entry
+// histograms, fewer when they do not fit the LDS budget.
+inline int32_t hist_block_units(int32_t E) {
+  int32_t nw = 8;
+  while (nw > 1 && sizeof(int32_t) * (size_t)nw * (size_t)E > kPrepLdsBudget) nw /= 2;
+  return nw;
+}
+
+// Block-sum rows of the histogram kernel: one per block, then one more for
+// the totals (written by the column scan when it runs).
+inline int32_t hist_block_rows(int32_t num_units, int32_t E) {
+  const int32_t nw = hist_block_units(E);
+  return (num_units + nw - 1) / nw + 1;
+}
+
+// Bytes of prepare's histograms (the first part of its scratch): the
+// per-unit rows [num_units][E], then the block-sum rows.
 inline size_t scratch_hist_bytes(int32_t num_units, int32_t E) {
-  return align256(sizeof(int32_t) * (size_t)num_units * (size_t)E);
+  return align256(sizeof(int32_t) * ((size_t)num_units + (size_t)hist_block_rows(num_units, E)) *
+                  (size_t)E);
 }
 
 // Bytes of prepare's whole scratch: the histograms, then the bad-id flags.

@@ -10,19 +10,24 @@
 //                shuffle exclusive scan of the aligned segment lengths, and a
 //                stable (route-ordered) slot map; prepare_fused_kernel does
 //                the same in one block and one launch for small routings.
-//   dispatch,    scatter_rows_kernel: the linear map D that copies token row
-//   combine_bwd  t into the received row of each of its valid routes and
-//                zero-fills pad rows. The routes of a group of tokens are
-//                dealt to the wavefronts of a block; a token slice is read
-//                from memory once and re-read from the caches.
+//                Both also write the run entries: each chunk of routes' rows
+//                in received-row order, chunk c on list c mod 8.
+//   dispatch,    run_rows_kernel: the linear map D that copies token row t
+//   combine_bwd  into the received row of each of its valid routes and
+//                zero-fills pad rows, walking the run entries so that the
+//                blocks of one XCD write dense bands of received rows and
+//                read each chunk's token rows from memory once, then from
+//                that XCD's L2. scatter_rows_kernel is the fallback for
+//                sizes past the run copy's 32-bit piece indices.
 //   combine,     reduce_rows_kernel: the transpose of D. Each token row is the
 //   dispatch_bwd fp32 sum, k ascending, of the received rows of its valid
 //                routes, rounded once to the payload type; the dispatch_bwd
 //                weight gradient is gathered in the same pass. With the
 //                received weights it is the fused weighted combine.
-//   weighted     weighted_bwd_kernel: the weighted combine's row gradient
-//   backward     (a scatter of w * g) and weight gradient (a dot product per
-//                route, in a fixed order).
+//   weighted     run_wbwd_kernel: the weighted combine's row gradient (w * g
+//   backward     copied along the run entries) and weight gradient (a dot
+//                product per route, summed in a fixed order);
+//                weighted_bwd_kernel is its token-group fallback.
 //
 // None of this is a dense contraction, so no MFMA: every kernel is bound by
 // HBM traffic (or, for prepare, by latency). Rows move as 16-byte vectors,
@@ -212,16 +217,76 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
     for (int e = lane; e < E; e += kWave) out[e] = hist[e];
     if (lane == 0) hv.unit_flags[u] = (nvalid << 1) | (bad_any ? 1 : 0);
   }
+  // the block's row of unit sums (rows of waves past the last unit are zero)
+  int32_t* brow = hv.unit_hist + ((int64_t)d.num_units + blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t sum = 0;
+    for (int q = 0; q < nw; ++q) sum += lds[q * E + e];
+    brow[e] = sum;
+  }
 }
 
-// Every block derives the same counts and aligned offsets from the unit
+// For routings of many units: an exclusive scan down each expert's column of
+// the block-sum rows (in place), and the column totals in the row after the
+// last block's. Block b takes 64 experts, one per lane; its eight wavefronts
+// split the rows into eight ranges, sum them, and rewrite them as running
+// sums from the ranges' starts. Linear in the rows; prepare_slots_kernel then
+// reads one row for its units' predecessors.
+__global__ void __launch_bounds__(512)
+prepare_scan_kernel(Dims d, HandleView hv, int32_t nb) {
+  __shared__ int32_t s_tot[8][kWave];
+  constexpr int kBatch = 16;
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int E = d.E;
+  const int e = blockIdx.x * kWave + lane;
+  const int ec = e < E ? e : E - 1;
+  int32_t* blk = hv.unit_hist + (int64_t)d.num_units * E;
+  const int32_t per = (nb + 7) / 8;
+  const int32_t r0 = w * per < nb ? w * per : nb;
+  const int32_t r1 = r0 + per < nb ? r0 + per : nb;
+  int32_t sum = 0;
+  for (int32_t rb = r0; rb < r1; rb += kBatch) {
+    int32_t v[kBatch];
+    static_for<kBatch>([&](auto j) {
+      const int32_t r = rb + j;
+      v[j] = blk[(int64_t)(r < r1 ? r : r1 - 1) * E + ec];
+    });
+    static_for<kBatch>([&](auto j) { sum += rb + j < r1 ? v[j] : 0; });
+  }
+  s_tot[w][lane] = sum;
+  __syncthreads();
+  int32_t run = 0, total = 0;
+  for (int q = 0; q < 8; ++q) {
+    run += q < w ? s_tot[q][lane] : 0;
+    total += s_tot[q][lane];
+  }
+  for (int32_t rb = r0; rb < r1; rb += kBatch) {
+    int32_t v[kBatch];
+    static_for<kBatch>([&](auto j) {
+      const int32_t r = rb + j;
+      v[j] = blk[(int64_t)(r < r1 ? r : r1 - 1) * E + ec];
+    });
+    static_for<kBatch>([&](auto j) {
+      const int32_t r = rb + j;
+      if (r < r1 && e < E) blk[(int64_t)r * E + e] = run;
+      run += r < r1 ? v[j] : 0;
+    });
+  }
+  if (w == 0 && e < E) blk[(int64_t)nb * E + e] = total;
+}
+
+// Every block derives the same counts and aligned offsets from the
 // histograms (block 0 publishes them), then its wavefronts hand out the rows
 // of their units: slot = segment start + routes of the same expert in earlier
 // units + the route's rank in its unit, which prepare_hist_kernel left in
-// slot[s].
+// slot[s]. The counts and the routes of earlier units come from the
+// histogram kernel's block-sum rows (nw1 units each): summed here when there
+// are few of them (scanned = 0), else read from the column scan's output.
 __global__ void __launch_bounds__(512)
 prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
-                     int32_t* __restrict__ user_offsets, int32_t ru, int32_t in_slot) {
+                     int32_t* __restrict__ user_offsets, int32_t ru, int32_t in_slot,
+                     int32_t nw1, int32_t scanned) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t s_wave_tot[2][16];
   __shared__ int32_t s_pads_live;
@@ -259,47 +324,66 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
       pk[i] = hv.slot[s < routes ? s : routes - 1];
     });
 
-  // 1. Column sums of the unit histograms over all units and over the units
-  //    before this block; this block's own unit rows are kept in LDS. Loads
-  //    are issued kBatch at a time per thread so that many are in flight.
-  constexpr int kBatch = 16;
-  const int ncols = E < nthr ? E : nthr;
-  const int nparts = nthr / ncols;
-  for (int e0 = 0; e0 < E; e0 += ncols) {
-    const int col = tid % ncols;
-    const int part = tid / ncols;
-    const int e = e0 + col;
-    int32_t all = 0, pre = 0;
-    if (part < nparts && e < E) {
-      for (int32_t ub = part; ub < U; ub += kBatch * nparts) {
-        int32_t v[kBatch];
-        static_for<kBatch>([&](auto j) {
-          const int32_t u = ub + j * nparts;
-          v[j] = hv.unit_hist[(int64_t)(u < U ? u : U - 1) * E + e];
-        });
-        static_for<kBatch>([&](auto j) {
-          const int32_t u = ub + j * nparts;
-          const int32_t c = u < U ? v[j] : 0;
-          all += c;
-          pre += u < u0 ? c : 0;
-          if (u >= u0 && u < u0 + nw) s_cursor[(u - u0) * E + e] = c;
-        });
-      }
+  // 1. Per expert: the routes of all units (counts) and of the units before
+  //    this block (s_pre), from the block-sum rows, then the rows of the
+  //    units between the start of unit u0's histogram block and u0; this
+  //    block's own unit rows are kept in LDS. Loads are issued kBatch at a
+  //    time per thread so that many are in flight.
+  const int32_t nb = (U + nw1 - 1) / nw1;
+  const int32_t hb0 = u0 / nw1 < nb ? u0 / nw1 : nb;
+  const int32_t* blk = hv.unit_hist + (int64_t)U * E;
+  if (scanned) {
+    for (int e = tid; e < E; e += nthr) {
+      s_counts[e] = blk[(int64_t)nb * E + e];
+      s_pre[e] = blk[(int64_t)hb0 * E + e];
     }
-    s_red[tid] = all;
-    s_red[nthr + tid] = pre;
-    __syncthreads();
-    if (tid < ncols && e < E) {
-      int32_t a = 0, p = 0;
-      for (int q = 0; q < nparts; ++q) {
-        a += s_red[q * ncols + tid];
-        p += s_red[nthr + q * ncols + tid];
+  } else {
+    constexpr int kBatch = 16;
+    const int ncols = E < nthr ? E : nthr;
+    const int nparts = nthr / ncols;
+    for (int e0 = 0; e0 < E; e0 += ncols) {
+      const int col = tid % ncols;
+      const int part = tid / ncols;
+      const int e = e0 + col;
+      int32_t all = 0, pre = 0;
+      if (part < nparts && e < E && nb > 0) {
+        for (int32_t rb = part; rb < nb; rb += kBatch * nparts) {
+          int32_t v[kBatch];
+          static_for<kBatch>([&](auto j) {
+            const int32_t r = rb + j * nparts;
+            v[j] = blk[(int64_t)(r < nb ? r : nb - 1) * E + e];
+          });
+          static_for<kBatch>([&](auto j) {
+            const int32_t r = rb + j * nparts;
+            const int32_t c = r < nb ? v[j] : 0;
+            all += c;
+            pre += r < hb0 ? c : 0;
+          });
+        }
       }
-      s_counts[e] = a;
-      s_pre[e] = p;
+      s_red[tid] = all;
+      s_red[nthr + tid] = pre;
+      __syncthreads();
+      if (tid < ncols && e < E) {
+        int32_t a = 0, p = 0;
+        for (int q = 0; q < nparts; ++q) {
+          a += s_red[q * ncols + tid];
+          p += s_red[nthr + q * ncols + tid];
+        }
+        s_counts[e] = a;
+        s_pre[e] = p;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
+  const int nq = U - u0 < nw ? (U - u0 > 0 ? U - u0 : 0) : nw;   // units of this block
+  for (int e = tid; e < E; e += nthr) {
+    int32_t p = 0;
+    for (int32_t u = hb0 * nw1; u < u0; ++u) p += hv.unit_hist[(int64_t)u * E + e];
+    s_pre[e] += p;
+    for (int q = 0; q < nq; ++q) s_cursor[q * E + e] = hv.unit_hist[(int64_t)(u0 + q) * E + e];
+  }
+  __syncthreads();
 
   // 2. Exclusive scans over experts of the aligned segment lengths and of the
   //    pad rows: a contiguous chunk per thread, a shuffle scan inside each
@@ -402,7 +486,6 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
 
   // 4. Per-wavefront cursors: segment start + routes of earlier units
   //    (turns the own-unit counts kept in LDS into running starts, in place).
-  const int nq = U - u0 < nw ? (U - u0 > 0 ? U - u0 : 0) : nw;   // units of this block
   for (int e = tid; e < E; e += nthr) {
     int32_t run = s_offs[e] + s_pre[e];
     for (int q = 0; q < nq; ++q) {
@@ -858,52 +941,31 @@ prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
 // instruction.
 typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
 
-// Work-item widths in 1 KiB column blocks, launch shapes and cache policy.
+// Launch shapes and cache policy, as measured on the MI355X.
+//
 // Output rows are written once, so every payload kernel stores them with the
 // streaming store below (non-temporal, written through the L2): it keeps one
-// op's dirty lines from being written back during the next op and measured
-// there. The reduce streams its input rows through once and loads them
-// non-temporally too; with plain loads its rows fill the caches that the next
-// run-entry copy needs for its token rows (measured: that copy 23% slower).
-#ifndef EP_SCATTER_CH
-#define EP_SCATTER_CH 2
-#endif
-// The scatter's grid in the plain order (rows over 8 KiB), in blocks per CU.
-// The scatter serves routings with masked routes (dense ones take the
-// run-entry copy), and those copy fastest on this grid: measured on the
-// MI355X against 16 per CU, masked routing 5% and a hot-expert routing 8%
-// faster (a dense routing without the hint 8% slower).
-#ifndef EP_SCATTER_BLOCKS_PER_CU
-#define EP_SCATTER_BLOCKS_PER_CU 64
-#endif
-// Rows of at most this many bytes take the interleaved unit order (token and
-// pad units spread evenly over the grid) and their own grid below.
-#ifndef EP_SCATTER_ILV_MAX_ROW
-#define EP_SCATTER_ILV_MAX_ROW 8192
-#endif
-#ifndef EP_SCATTER_ILV_BLOCKS_PER_CU
-#define EP_SCATTER_ILV_BLOCKS_PER_CU 32
-#endif
-#ifndef EP_BLOCKS_PER_CU
-#define EP_BLOCKS_PER_CU 128
-#endif
-#ifndef EP_SCATTER_NT_STORE
-#define EP_SCATTER_NT_STORE 1
-#endif
-// The scatter's token slices are loaded with the default (temporal) policy:
-// the wavefronts of a block that share a slice must find it in the caches.
-#ifndef EP_SCATTER_NT_LOAD
-#define EP_SCATTER_NT_LOAD 0
-#endif
-#ifndef EP_REDUCE_NT_STORE
-#define EP_REDUCE_NT_STORE 1
-#endif
-#ifndef EP_REDUCE_NT_LOAD
-#define EP_REDUCE_NT_LOAD 1
-#endif
-#ifndef EP_SCATTER_FENCE
-#define EP_SCATTER_FENCE 1
-#endif
+// op's dirty lines from being written back during the next op. The reduce
+// streams its input rows through once and loads them non-temporally too; with
+// plain loads its rows fill the caches that the next run-entry copy needs for
+// its token rows (that copy measured 23% slower). Token rows, which several
+// wavefronts or routes share, are loaded with the default (temporal) policy.
+constexpr bool kScatterNtStore = true;
+constexpr bool kScatterNtLoad = false;
+constexpr bool kReduceNtStore = true;
+constexpr bool kReduceNtLoad = true;
+// The scatter (the fallback copy for sizes past the run copy's 32-bit piece
+// indices): two 1 KiB column blocks per work item; rows over 8 KiB take the
+// plain unit order on 64 blocks per CU, shorter rows the interleaved order
+// (token and pad units spread evenly over the grid) on 32 blocks per CU.
+constexpr int kScatterCH = 2;
+constexpr int kScatterBlocksPerCU = 64;
+constexpr int64_t kScatterIlvMaxRow = 8192;
+constexpr int kScatterIlvBlocksPerCU = 32;
+// The reduce's grid cap, in blocks per CU.
+constexpr int kBlocksPerCU = 128;
+// The token-group weighted backward's grid, in blocks per CU.
+constexpr int kBwdBlocksPerCU = 16;
 
 namespace {
 
@@ -942,10 +1004,6 @@ __device__ __forceinline__ void store_row16(row16_t* p, row16_t v) {
   }
 }
 
-constexpr bool kScatterNtStore = EP_SCATTER_NT_STORE;
-constexpr bool kScatterNtLoad = EP_SCATTER_NT_LOAD;
-constexpr bool kReduceNtStore = EP_REDUCE_NT_STORE;
-constexpr bool kReduceNtLoad = EP_REDUCE_NT_LOAD;
 // The reduce's blocks: two wavefronts each. Its wavefronts mostly handle one
 // item and exit, and measured on the MI355X small blocks start faster than
 // blocks of 4 or more wavefronts at the same wavefronts per CU.
@@ -960,10 +1018,8 @@ constexpr int kBlock = 128;
 // once here instead of before every conditional store that follows.
 template <int N>
 __device__ __forceinline__ void consume(const row16_t (&buf)[N]) {
-#if EP_SCATTER_FENCE
 #pragma unroll
   for (int j = 0; j < N; ++j) asm volatile("" ::"v"(buf[j]));
-#endif
 }
 
 // Index of this wavefront among all wavefronts of the grid, as a scalar.
@@ -1400,6 +1456,8 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 // (pads, and the tail under the tail policy) are zeroed, with their weight
 // gradients, in each XCD's share as in the run copy.
 constexpr int kWbwdPieces = 4;                 // pieces per wavefront and round
+constexpr int kWbwdRounds = 2;                 // rounds per block step (weight gradient)
+constexpr int kWbwdBlocksPerCU = 32;           // grid cap (weight gradient)
 constexpr int kWbwdMaxPartials = 1024;         // LDS partials of one block step
 
 template <int DT, bool WANT_W>
@@ -1749,10 +1807,7 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // result is stored): the same bits on every run. Pad pieces (1 KiB of pad
 // rows, and their weight gradients) are zeroed when pads are filled.
 constexpr int kBwdWaves = 8;
-#ifndef EP_BWD_UNROLL
-#define EP_BWD_UNROLL 8
-#endif
-constexpr int kBwdUnroll = EP_BWD_UNROLL;
+constexpr int kBwdUnroll = 8;
 
 template <int DT, bool WANT_W>
 __global__ void __launch_bounds__(kBwdWaves * kWave)
@@ -1850,12 +1905,13 @@ int key_bits(int E) {
   return b;
 }
 
-constexpr size_t kLdsBudget = 65536;
+constexpr size_t kLdsBudget = kPrepLdsBudget;
+// Up to this many block-sum rows every slots block sums them itself (about
+// 64 * E loads each); past it the column scan takes its own launch, so that
+// prepare's work stays linear in the routes.
+constexpr int kPrepDirectBlockRows = 64;
 // Routings of at most this many routes take the single-block prepare.
-#ifndef EP_PREP_FUSED_MAX_ROUTES
-#define EP_PREP_FUSED_MAX_ROUTES 4096
-#endif
-constexpr int64_t kPrepFusedMaxRoutes = EP_PREP_FUSED_MAX_ROUTES;
+constexpr int64_t kPrepFusedMaxRoutes = 4096;
 static_assert(kPrepFusedMaxRoutes <= (int64_t)kFusedWaves * kPrepRounds * kWave,
               "the one-block prepare holds at most kPrepRounds rounds per wavefront");
 
@@ -1863,13 +1919,6 @@ size_t slots_lds_bytes(int E, int nw, int run_chunks) {
   return sizeof(int32_t) * (size_t)(4 * E + 2 + 2 * kWave * nw + (nw + 1) * E + run_chunks * E);
 }
 
-constexpr int kScatterCH = EP_SCATTER_CH;
-constexpr int kScatterBlocksPerCU = EP_SCATTER_BLOCKS_PER_CU;
-constexpr int kScatterIlvBlocksPerCU = EP_SCATTER_ILV_BLOCKS_PER_CU;
-constexpr int64_t kScatterIlvMaxRow = EP_SCATTER_ILV_MAX_ROW;
-constexpr int kBlocksPerCU = EP_BLOCKS_PER_CU;
-// The token-group weighted backward's grid, in blocks per CU.
-constexpr int kBwdBlocksPerCU = 16;
 
 
 int grid_for(int64_t items, int num_cus) {
@@ -1938,12 +1987,18 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
     if (err != hipSuccess) return err;
     return launch_prepare_runs(d, hv, topk_idx, ru, 1, stream);
   }
+  const int nw1 = hist_block_units(d.E);
+  const int nb = (U + nw1 - 1) / nw1;
+  const int scanned = nb > kPrepDirectBlockRows;
   if (U > 0) {
-    int nw1 = 8;
-    while (nw1 > 1 && sizeof(int32_t) * (size_t)nw1 * d.E > kLdsBudget) nw1 /= 2;
-    const int grid1 = (U + nw1 - 1) / nw1;
-    hipLaunchKernelGGL(prepare_hist_kernel, dim3(grid1), dim3(nw1 * kWave),
+    hipLaunchKernelGGL(prepare_hist_kernel, dim3(nb), dim3(nw1 * kWave),
                        sizeof(int32_t) * (size_t)nw1 * d.E, stream, d, hv, topk_idx, nbits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (scanned) {
+    hipLaunchKernelGGL(prepare_scan_kernel, dim3((d.E + kWave - 1) / kWave), dim3(8 * kWave), 0,
+                       stream, d, hv, (int32_t)nb);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1965,7 +2020,7 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   if (grid2 < 1) grid2 = 1;
   hipLaunchKernelGGL(prepare_slots_kernel, dim3(grid2), dim3(nw2 * kWave),
                      slots_lds_bytes(d.E, nw2, in_slots ? nw2 / ru : 0), stream, d, hv,
-                     user_counts, user_offsets, ru, in_slots);
+                     user_counts, user_offsets, ru, in_slots, (int32_t)nw1, (int32_t)scanned);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return in_slots ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 0, stream);
@@ -2137,14 +2192,21 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
   const int64_t lim = (int64_t)1 << 31;
   if (d.T == 0 || npc > kWbwdMaxPartials || scap * npc >= lim || zero_max * npc >= lim)
     return launch_weighted_bwd_groups(d, hv, g, y, rw, grad_rows, grad_w, num_cus, stream);
-  // rows per block step: as many whole rows as fill about 8 * kWbwdPieces
-  // pieces (one round), at least one
-  const int64_t round = (int64_t)kRunWaves * kWbwdPieces;
+  // rows per block step: as many whole rows as fill the step's rounds of
+  // 8 * kWbwdPieces pieces, at least one. With the weight gradient a step
+  // ends in two block barriers: two rounds a step and at most kWbwdBlocksPerCU
+  // blocks per CU (each taking more steps) measured best on the MI355X
+  // (dsv3 247 us against 257 us with one round and 96 blocks per CU, the
+  // masked share 209 against 231); the row gradient alone has no barrier and
+  // takes one round and the run copy's grid.
+  const bool want_w = grad_w != nullptr;
+  const int64_t round = (int64_t)kRunWaves * kWbwdPieces * (want_w ? kWbwdRounds : 1);
   int64_t R = round / npc;
   if (R < 1) R = 1;
   const int64_t dense = run_stream_dense(d.num_units, routes);
   int64_t bps = (dense + R - 1) / R;
-  const int64_t bps_cap = (int64_t)num_cus * kRunBlocksPerCU / kRunXcds;
+  const int64_t bps_cap =
+      (int64_t)num_cus * (want_w ? kWbwdBlocksPerCU : kRunBlocksPerCU) / kRunXcds;
   if (bps > bps_cap) bps = bps_cap;
   if (bps < 1) bps = 1;
   RunGeom geo;
