@@ -186,6 +186,16 @@ def _schedule(directory: str):
     return d["ops"]
 
 
+def _recorded_cmd(directory: str) -> str:
+    """The bench command line that wrote this profile directory's schedule,
+    with the directory written as <dir>."""
+    with open(os.path.join(directory, "schedule.json")) as f:
+        argv = json.load(f).get("argv", [])
+    # the path given to --schedule-out names the profile directory
+    return "python3 bench.py " + " ".join(
+        "<dir>/schedule.json" if a.endswith("schedule.json") else a for a in argv)
+
+
 def _is_payload(name: str) -> bool:
     return any(k in name for k in PAYLOAD_KERNELS)
 
@@ -245,12 +255,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
            "calibration": {"copy_mib": copy_mib,
                            "fetch_factor": res["FETCH_SIZE"]["factor"],
                            "write_factor": res["WRITE_SIZE"]["factor"]}}
-    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc <COUNTER> "
-           "-d <dir> -o <name> --output-format csv -- python3 bench.py --workload "
-           f"{workload} --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy-mib {copy_mib}"
-           " --schedule-out <dir>/schedule.json   (once with FETCH_SIZE, once with "
-           "WRITE_SIZE); then python bench.py --summarize-pmc <fetch dir> <write dir> "
-           f"--workload {workload} --calibration-copy-mib {copy_mib}")
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc <COUNTER> "
+           f"-d <dir> -o pmc --output-format csv -- {_recorded_cmd(fetch_dir)}   (once with "
+           "FETCH_SIZE, once with WRITE_SIZE); then python bench.py --summarize-pmc "
+           f"<fetch dir> <write dir> --workload {workload} --calibration-copy-mib {copy_mib}")
     for op in KERNEL_OF_OP:                    # warm launches only
         fb = res["FETCH_SIZE"]["per_op_bytes"].get(op)
         wb = res["WRITE_SIZE"]["per_op_bytes"].get(op)
@@ -261,6 +269,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
         summary.update({"op": op, "kernel": kern,
                         "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                         "hbm_bytes_per_launch": fb + wb})
+        fc = res["FETCH_SIZE"]["per_op_bytes"].get(op + COLD)
+        wc = res["WRITE_SIZE"]["per_op_bytes"].get(op + COLD)
+        if fc is not None and wc is not None:
+            # the same op launched right after the cache flush
+            summary.update({"cold_fetch_bytes_per_launch": fc, "cold_write_bytes_per_launch": wc})
         path = _pmc_path(op, workload)
         with open(path, "w") as f:
             f.write(f"# HBM traffic of {kern} ({op}), workload {workload}\n")
@@ -299,10 +312,8 @@ def summarize_trace(trace_dir: str, workload: str, steps: int, warmup: int,
                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     path = os.path.join(out_dir, f"ep_kernels_{workload}_kernel_stats.txt")
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <dir> -o "
-           f"trace --output-format csv -- python3 bench.py --workload {workload} --steps "
-           f"{steps} --warmup {warmup} --no-cpu-baseline --schedule-out <dir>/schedule.json; "
-           f"then python bench.py --summarize-trace <dir> --workload {workload} --steps "
-           f"{steps} --warmup {warmup}")
+           f"trace --output-format csv -- {_recorded_cmd(trace_dir)}; then python bench.py "
+           f"--summarize-trace <dir> --workload {workload} --steps {steps} --warmup {warmup}")
     with open(path, "w") as f:
         f.write(f"# rocprofv3 kernel statistics, workload {workload}\n")
         f.write(f"# command: {cmd}\n")
@@ -769,7 +780,7 @@ def main():
     if args.schedule_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.schedule_out)), exist_ok=True)
         with open(args.schedule_out, "w") as f:
-            json.dump({"ops": schedule}, f)
+            json.dump({"ops": schedule, "argv": sys.argv[1:]}, f)
 
     def gbs(op, nb):
         return nb / (avg[op] * 1e-3) / 1e9
