@@ -149,17 +149,25 @@ typedef struct ep_layout {
 /* Rows that can never overflow: every token sends min(K,E) distinct routes
  * and every expert adds at most A-1 pad rows: T*min(K,E) + E*(A-1). With
  * repeated ids in a token's top-k the bound is T*K + E*(A-1). Returns -1 for
- * out-of-range arguments. Host only. */
+ * out-of-range arguments. Host only. The library's own helper: the review of
+ * "[PyTorch] Expert Parallelism: PyTorch wrapper + autograd ops with symm-mem
+ * zero-copy" sizes the padded expert-major buffer for its worst case (the
+ * thread on buffer sizing and recv_capacity_per_rank); this is that bound for
+ * one GPU. */
 int64_t ep_recv_capacity_worst(int64_t num_tokens, int32_t topk, int32_t num_experts,
                                int32_t alignment);
 
 /* Bytes of device memory the caller must provide as `handle_mem` for this
- * layout (the handle-size query of the common C API). Returns 0 for an
- * invalid layout. Host only. */
+ * layout. Returns 0 for an invalid layout. Host only. The handle-size query
+ * of "Expert Parallelism: common C API + NCCL EP backend" (section "Public C
+ * API", its "Lifecycle" list: layer registration reports the handle_mem size
+ * the caller allocates); here it is a pure function of the layout, with no
+ * registration step. */
 size_t ep_handle_mem_size(const ep_layout_t* layout);
 
 /* Byte offsets, inside handle_mem, of the routing maps that prepare writes,
- * so that callers can read them (all int32 unless stated):
+ * so that callers can read them. The library's own addition: the handle of
+ * the common C API is opaque caller memory. All int32 unless stated:
  *   status   uint32 status word (EP_STATUS_* bits)
  *   counts   [E]     valid routes per expert
  *   offsets  [E+1]   segment starts, offsets[E] = total
@@ -202,7 +210,10 @@ ep_status_t ep_handle_regions(const ep_layout_t* layout, ep_handle_regions_t* ou
 
 /*
  * prepare: from the int64 routing table, write the per-expert token counts,
- * the aligned segment offsets and the slot map into the handle.
+ * the aligned segment offsets and the slot map into the handle. The
+ * per-step prepare of "Expert Parallelism: common C API + NCCL EP backend"
+ * (section "Per-step (allocation-free, CUDA-graph capturable)"), with the
+ * alignment taken from the layout.
  *   topk_idx        int64 [T,K]                  input
  *   token_counts    int32 [E]                    output: valid routes per expert
  *                                                (not padded)
@@ -223,7 +234,7 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
  * ep_prepare_static: ep_prepare for callers that cannot allocate (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation)
  * and so cannot give the handle room for prepare's scratch. The same work and
- * the same routing maps, bit for bit, but the scratch (the per-unit expert
+ * the same routing maps, bit for bit, but the scratch (the expert
  * histograms and bad-id flags of the prepare kernels) lives in a static
  * device array of the library, EP_PREPARE_STATIC_SCRATCH_BYTES per device,
  * held until the process ends; so handle_mem needs only the routing maps,
@@ -232,9 +243,12 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
  * call on each device. Every call on one device shares that device's array,
  * so calls of ep_prepare_static that overlap on one device (several streams,
  * no ordering between them) race and must not be made; ep_prepare and the
- * payload ops do not touch the array. A layout whose scratch, 4 bytes per
- * expert per 512 routes plus 4 per 512 routes (each part rounded up to
- * 256 bytes), exceeds the array returns EP_ERR_SCRATCH before any HIP call.
+ * payload ops do not touch the array. A layout whose scratch exceeds the
+ * array returns EP_ERR_SCRATCH before any HIP call. With U = ceil(T*K/512)
+ * units of routes the scratch is 4*E*(U + ceil(U/8) + 1) bytes of histograms
+ * (one row per unit, one per block of 8 units, one of totals) plus 4*U bytes
+ * of flags, each part rounded up to 256 bytes: at E = 256, 3626 units
+ * (about 1.86 M routes) fit.
  */
 #define EP_PREPARE_STATIC_SCRATCH_BYTES (4u << 20)
 
@@ -243,10 +257,12 @@ ep_status_t ep_prepare_static(const ep_layout_t* layout, const int64_t* topk_idx
                               size_t handle_bytes, hipStream_t stream);
 
 /*
- * dispatch: recv_tokens[r,:] = tokens[s/K,:] and recv_topk_weights[r] =
+ * dispatch (the per-step dispatch of the same section):
+ * recv_tokens[r,:] = tokens[s/K,:] and recv_topk_weights[r] =
  * topk_weights[s] for every live row r holding route s (bit copies); pad
  * rows get +0 in both (not written with EP_LAYOUT_NO_PAD_FILL). Rows at or
- * past min(total, recv_capacity) are not written.
+ * past min(total, recv_capacity) are not written (+0 with
+ * EP_LAYOUT_ZERO_TAIL).
  *   tokens             payload [T,H]
  *   topk_weights       fp32 [T,K] or NULL
  *   recv_tokens        payload [recv_capacity,H]
@@ -259,7 +275,8 @@ ep_status_t ep_dispatch(const ep_layout_t* layout, const void* handle_mem,
                         float* recv_topk_weights, hipStream_t stream);
 
 /*
- * combine: result[t,:] = the sum over the valid routes of t, k ascending, of
+ * combine (the per-step combine of the same section, unweighted there too):
+ * result[t,:] = the sum over the valid routes of t, k ascending, of
  * expert_out[slot(t,k),:], accumulated in fp32 starting from the first valid
  * row and rounded once to the payload type (see the rounding convention
  * above). A token with no valid route gets +0. Unweighted.
@@ -272,7 +289,8 @@ ep_status_t ep_combine(const ep_layout_t* layout, const void* handle_mem,
                        hipStream_t stream);
 
 /*
- * dispatch_bwd (adjoint of dispatch): grad_tokens = combine(grad) with the
+ * dispatch_bwd (the per-step dispatch backward of the same section; the
+ * adjoint of dispatch): grad_tokens = combine(grad) with the
  * same fp32 ascending-k rule; grad_topk_weights[s] = g_recv_topk_weights[r]
  * for the row r of a valid route s, else +0. A NULL g_recv_topk_weights
  * (no gradient flowed into the received weights) gives +0 everywhere; a NULL
@@ -288,10 +306,11 @@ ep_status_t ep_dispatch_bwd(const ep_layout_t* layout, const void* handle_mem,
                             float* grad_topk_weights, hipStream_t stream);
 
 /*
- * combine_bwd (adjoint of combine): grad_expert_out[r,:] = grad[s/K,:] for
+ * combine_bwd (the per-step combine backward of the same section; the
+ * adjoint of combine): grad_expert_out[r,:] = grad[s/K,:] for
  * every live row r holding route s; pad rows are zeroed (not written with
  * EP_LAYOUT_NO_PAD_FILL). Rows at or past min(total, recv_capacity) are not
- * written.
+ * written (+0 with EP_LAYOUT_ZERO_TAIL).
  *   grad             payload [T,H]
  *   grad_expert_out  payload [recv_capacity,H]
  */
@@ -338,7 +357,7 @@ ep_status_t ep_combine_weighted(const ep_layout_t* layout, const void* handle_me
  * chain N * P multiply-adds: n = N * P + 6 there.) With
  * grad_recv_topk_weights NULL only the row gradient is computed and
  * expert_out may be NULL. Rows at or past min(total, recv_capacity) are not
- * written.
+ * written (+0, and +0 weight gradients, with EP_LAYOUT_ZERO_TAIL).
  *   grad                    payload [T,H]
  *   expert_out              payload [recv_capacity,H] or NULL
  *   recv_topk_weights       fp32 [recv_capacity]
@@ -352,10 +371,15 @@ ep_status_t ep_combine_weighted_bwd(const ep_layout_t* layout, const void* handl
                                     hipStream_t stream);
 
 /* Copy the handle's status word (EP_STATUS_* bits) to *host_out. Waits for
- * `stream`; not for the hot path. host_out is a host pointer. */
+ * `stream`; not for the hot path. host_out is a host pointer. The library's
+ * own addition: the review of "[PyTorch] Expert Parallelism: PyTorch wrapper
+ * + autograd ops with symm-mem zero-copy" (thread on recv_capacity_per_rank)
+ * has a sync-free mode drop what exceeds the static capacity and raise a
+ * flag; this call reads that flag, and the bad-id and layout flags, back. */
 ep_status_t ep_read_status(const void* handle_mem, uint32_t* host_out, hipStream_t stream);
 
-/* Static description of an ep_status_t. Never NULL. Host only. */
+/* Static description of an ep_status_t. Never NULL. Host only. The
+ * library's own addition. */
 const char* ep_status_str(ep_status_t status);
 
 #ifdef __cplusplus
