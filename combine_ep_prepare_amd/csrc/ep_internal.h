@@ -127,9 +127,16 @@ inline size_t scratch_hist_bytes(int32_t num_units, int32_t E) {
                   (size_t)E);
 }
 
-// Bytes of prepare's whole scratch: the histograms, then the bad-id flags.
+// Bytes of prepare's per-unit words: each unit's flag word, then (for as
+// many chunks as there can be, one per unit) each chunk's start in its
+// stream's run list, which the column scan writes for large routings.
+inline size_t scratch_unit_bytes(int32_t num_units) {
+  return align256(2 * sizeof(int32_t) * (size_t)num_units);
+}
+
+// Bytes of prepare's whole scratch: the histograms, then the per-unit words.
 inline size_t scratch_bytes(int32_t num_units, int32_t E) {
-  return scratch_hist_bytes(num_units, E) + align256(sizeof(int32_t) * (size_t)num_units);
+  return scratch_hist_bytes(num_units, E) + scratch_unit_bytes(num_units);
 }
 
 inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) {
@@ -148,7 +155,7 @@ inline HandleLayout handle_layout(int64_t T, int32_t K, int32_t E, int64_t cap) 
   at += align256(sizeof(RunEntry) * (size_t)kRunXcds * (size_t)run_stream_cap(h.num_units));
   h.maps_bytes = at;
   h.unit_hist = at;    at += scratch_hist_bytes(h.num_units, E);
-  h.unit_flags = at;   at += align256(sizeof(int32_t) * (size_t)h.num_units);
+  h.unit_flags = at;   at += scratch_unit_bytes(h.num_units);
   h.bytes = at;
   return h;
 }
@@ -163,7 +170,8 @@ struct HandleView {
   int32_t* row_src;
   int32_t* pad_rows;
   int32_t* unit_hist;
-  int32_t* unit_flags;   // per unit: (valid routes << 1) | bad-id flag
+  int32_t* unit_flags;   // per unit: (valid routes << 1) | bad-id flag; then
+                         // per chunk: its start in its stream's list
   RunEntry* runs;
 };
 

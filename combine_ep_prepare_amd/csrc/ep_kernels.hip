@@ -233,7 +233,7 @@ prepare_hist_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
 // sums from the ranges' starts. Linear in the rows; prepare_slots_kernel then
 // reads one row for its units' predecessors.
 __global__ void __launch_bounds__(512)
-prepare_scan_kernel(Dims d, HandleView hv, int32_t nb) {
+prepare_scan_kernel(Dims d, HandleView hv, int32_t nb, int32_t ru) {
   __shared__ int32_t s_tot[8][kWave];
   constexpr int kBatch = 16;
   const int lane = lane_id();
@@ -274,6 +274,30 @@ prepare_scan_kernel(Dims d, HandleView hv, int32_t nb) {
     });
   }
   if (w == 0 && e < E) blk[(int64_t)nb * E + e] = total;
+  if (blockIdx.x != 0) return;
+  // Block 0 also gives every chunk of ru units its start in its stream's run
+  // list: wavefront x walks stream x's chunks c = x + 8 j in order, 64 at a
+  // time, and scans their valid routes (from the unit flags).
+  const int32_t U = d.num_units;
+  const int32_t nch = (U + ru - 1) / ru;
+  int32_t* cbase = hv.unit_flags + U;
+  int32_t base = 0;
+  for (int32_t j0 = 0; w + kRunXcds * j0 < nch; j0 += kWave) {
+    const int32_t c = w + kRunXcds * (j0 + lane);
+    int32_t v = 0;
+    if (c < nch)
+      for (int32_t i = 0; i < ru; ++i) {
+        const int32_t u = c * ru + i;
+        if (u < U) v += hv.unit_flags[u] >> 1;
+      }
+    int32_t inc = v;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (c < nch) cbase[c] = base + inc - v;
+    base += __shfl(inc, kWave - 1);
+  }
 }
 
 // Every block derives the same counts and aligned offsets from the
@@ -543,11 +567,15 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
     // stream's earlier chunks (whole chunks of ru units each), and the
     // chunk's own valid routes
     const int32_t c = (u0 + qa) / ru;
-    const int32_t nprev = c / kRunXcds * ru;
     int32_t vb = 0, vo = 0;
-    for (int32_t i = tid; i < nprev; i += nthr) {
-      const int32_t cp = c % kRunXcds + kRunXcds * (i / ru);
-      vb += hv.unit_flags[cp * ru + i % ru] >> 1;
+    if (scanned) {
+      if (tid == 0) vb = hv.unit_flags[U + c];     // from the column scan
+    } else {
+      const int32_t nprev = c / kRunXcds * ru;
+      for (int32_t i = tid; i < nprev; i += nthr) {
+        const int32_t cp = c % kRunXcds + kRunXcds * (i / ru);
+        vb += hv.unit_flags[cp * ru + i % ru] >> 1;
+      }
     }
     for (int32_t i = tid; i < qb - qa; i += nthr) vo += hv.unit_flags[u0 + qa + i] >> 1;
     for (int off = kWave / 2; off > 0; off >>= 1) {
@@ -843,7 +871,7 @@ constexpr int kRunThreads = 1024;
 
 __global__ void __launch_bounds__(kRunThreads)
 prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx, int32_t ru,
-                    int32_t write_live) {
+                    int32_t write_live, int32_t scanned) {
   extern __shared__ int32_t s_run[];                // base[E] (counts first), first[E]
   __shared__ int32_t s_wave_tot[kRunThreads / kWave];
   __shared__ int32_t s_total;
@@ -870,7 +898,9 @@ prepare_runs_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
   }
   __syncthreads();
   // the chunk's start in its stream's list
-  if (!write_live) {
+  if (!write_live && scanned) {
+    if (tid == 0) atomicAdd(&s_sbase, hv.unit_flags[d.num_units + c]);   // from the column scan
+  } else if (!write_live) {
     const int32_t nprev = c / kRunXcds * ru;
     int32_t vb = 0;
     for (int32_t i = tid; i < nprev; i += nthr)
@@ -1910,6 +1940,9 @@ constexpr size_t kLdsBudget = kPrepLdsBudget;
 // 64 * E loads each); past it the column scan takes its own launch, so that
 // prepare's work stays linear in the routes.
 constexpr int kPrepDirectBlockRows = 64;
+// Routings of two-unit chunks build their run entries in the slot kernel
+// from this many units on.
+constexpr int32_t kSlotRunsMinUnits = 1536;
 // Routings of at most this many routes take the single-block prepare.
 constexpr int64_t kPrepFusedMaxRoutes = 4096;
 static_assert(kPrepFusedMaxRoutes <= (int64_t)kFusedWaves * kPrepRounds * kWave,
@@ -1961,11 +1994,12 @@ row16_t* rows_out(void* p) { return static_cast<row16_t*>(p); }
 namespace {
 
 hipError_t launch_prepare_runs(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
-                               int32_t ru, int write_live, hipStream_t stream) {
+                               int32_t ru, int write_live, int scanned, hipStream_t stream) {
   if (d.T == 0) return hipSuccess;
   const int64_t chunks = ((int64_t)d.num_units + ru - 1) / ru;
   hipLaunchKernelGGL(prepare_runs_kernel, dim3((unsigned)chunks), dim3(kRunThreads),
-                     2 * sizeof(int32_t) * (size_t)d.E, stream, d, hv, topk_idx, ru, write_live);
+                     2 * sizeof(int32_t) * (size_t)d.E, stream, d, hv, topk_idx, ru, write_live,
+                     scanned);
   return hipGetLastError();
 }
 
@@ -1985,7 +2019,7 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
                        stream, d, hv, topk_idx, user_counts, user_offsets, nbits, ru);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_prepare_runs(d, hv, topk_idx, ru, 1, stream);
+    return launch_prepare_runs(d, hv, topk_idx, ru, 1, 0, stream);
   }
   const int nw1 = hist_block_units(d.E);
   const int nb = (U + nw1 - 1) / nw1;
@@ -1998,17 +2032,21 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   }
   if (scanned) {
     hipLaunchKernelGGL(prepare_scan_kernel, dim3((d.E + kWave - 1) / kWave), dim3(8 * kWave), 0,
-                       stream, d, hv, (int32_t)nb);
+                       stream, d, hv, (int32_t)nb, ru);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // The slot kernel also builds the run entries when a chunk is two or more
-  // units and its blocks hold whole chunks; otherwise they take their own
-  // launch. Measured on the MI355X: this saves 1.3-2.2 us of prepare at 4
-  // units per chunk and costs 6 us at 1 (eight chunk scans per block).
+  // The slot kernel also builds the run entries when its blocks hold whole
+  // chunks and a chunk is four units, or two units on a routing of at least
+  // kSlotRunsMinUnits units; otherwise they take their own launch. Measured
+  // on the MI355X (prepare us, top-8 over 256 experts; 4 units a chunk
+  // saves 1.3-2.2 us and 1 unit costs 6 us): at 2 units a chunk, 27.0 in
+  // the slot kernel against 23.6 separately at 4096 tokens, 33.0 against
+  // 30.6 at 65536, but 39.7 against 42.0 at 131072 and 66.3 against 67.1
+  // at 262144 (32 experts: 42.7 against 54.2).
   int nw2 = 8;
   int in_slots = 0;
-  if (ru >= 2) {
+  if (ru >= 4 || (ru == 2 && U >= kSlotRunsMinUnits)) {
     while (nw2 >= ru && slots_lds_bytes(d.E, nw2, nw2 / ru) > kLdsBudget) nw2 /= 2;
     in_slots = nw2 >= ru && nw2 % ru == 0 && slots_lds_bytes(d.E, nw2, nw2 / ru) <= kLdsBudget;
   }
@@ -2023,7 +2061,7 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
                      user_counts, user_offsets, ru, in_slots, (int32_t)nw1, (int32_t)scanned);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return in_slots ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 0, stream);
+  return in_slots ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 0, scanned, stream);
 }
 
 hipError_t launch_scatter_rows(const Dims& d, const HandleView& hv, const void* src,

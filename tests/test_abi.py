@@ -68,8 +68,9 @@ def test_handle_size_and_regions():
     assert r.runs + 8 * (64 * 64 + 2048) * 8 == r.maps_bytes
     # prepare's scratch closes the handle: 256-expert histograms of the 64
     # units of 512 routes, of their 8 blocks of 8 units and one totals row,
-    # then one flag per unit, each part 256-byte aligned
-    assert n - r.maps_bytes == (64 + 8 + 1) * 256 * 4 + 256
+    # then two words per unit (its flags, a chunk start), each part
+    # 256-byte aligned
+    assert n - r.maps_bytes == (64 + 8 + 1) * 256 * 4 + 512
     # the handle grows with the capacity and does not depend on H
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=512)) == n
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=7168, cap=L.cap * 2)) > n
@@ -295,10 +296,10 @@ def test_prepare_static_host_checks():
     assert fn(C.byref(big), P, P, None, P, 1 << 40, None) == ep.EP_ERR_SCRATCH
     assert "static" in ep.status_str(ep.EP_ERR_SCRATCH)
     # the largest layout it takes at E = 256: 4 MiB holds the 256-entry
-    # histograms of 3626 units, of their 454 blocks of 8 and one totals row
-    # (4081 KiB), plus the units' flags (14.25 KiB); at 3627 units the rows
-    # alone take 4082 KiB, and with the flags that is past 4 MiB
-    for units, want_ok in ((3626, True), (3627, False)):
+    # histograms of 3614 units, of their 452 blocks of 8 and one totals row
+    # (4067 KiB), plus two words per unit (28.25 KiB); 3615 units need 1 KiB
+    # more rows, and with their words that is past 4 MiB
+    for units, want_ok in ((3614, True), (3615, False)):
         Lu = lay(T=units * 64, K=8, E=256, A=1, H=64, cap=64)
         code = fn(C.byref(Lu), P, P, None, MIS, 1 << 40, None)
         assert code == (ep.EP_ERR_ALIGN if want_ok else ep.EP_ERR_SCRATCH)

@@ -8,9 +8,11 @@ the routes. With many experts the slot kernel's blocks hold fewer units than
 the histogram kernel's, and a block then also adds the unit rows between the
 start of its histogram block and its first unit. These cases sit on both
 sides of the 64-row switch, with 100, 256 and 2048 experts, masked routes
-and ragged tails, and compare counts, offsets, slot map, row map, run
-entries and status with the oracle bit for bit; two also run dispatch and
-combine on the prepared handle.
+and ragged tails, for chunks of 4, 2 and 1 units (whose run entries are
+built in the slot kernel or in a launch of their own, their list starts
+summed there or taken from the column scan), and compare counts, offsets,
+slot map, row map, run entries and status with the oracle bit for bit; two
+also run dispatch and combine on the prepared handle.
 """
 import zlib
 
@@ -51,12 +53,21 @@ CASES = [
 ]
 
 
+# the layout's row sets the chunk size (token rows of a chunk at most
+# 2.5 MiB): 128-byte rows take 4 units a chunk (run entries built in the
+# slot kernel), 14 KiB rows 2 (in the slot kernel from 1536 units, else in
+# their own launch), 28 KiB rows 1 (their own launch)
+ROWS = [(64, "bf16"), (7168, "bf16"), (7168, "fp32")]
+
+
+@pytest.mark.parametrize("H,dt", ROWS, ids=["row128B", "row14KiB", "row28KiB"])
 @pytest.mark.parametrize("label,T,K,E,A,masked", CASES, ids=[c[0] for c in CASES])
-def test_prepare_both_scan_forms(label, T, K, E, A, masked):
+def test_prepare_both_scan_forms(label, T, K, E, A, masked, H, dt):
     idx = _routing(label, T, K, E, masked)
     cap = oracle.recv_capacity_worst(T, K, E, A)
-    log(f"prepare {label}: T={T} K={K} E={E} A={A} cap={cap} units={-(-T * K // 512)}")
-    run = GpuRun(idx, E, A, 64, cap)
+    log(f"prepare {label}: T={T} K={K} E={E} A={A} cap={cap} units={-(-T * K // 512)} "
+        f"row {H} {dt}")
+    run = GpuRun(idx, E, A, H, cap, prepare_dtype=dt)
     run.prepare()
     p = oracle.prepare(idx, E, A, cap)
     check_prepare(run, p)
