@@ -126,3 +126,30 @@ def test_random_zero_tail(i, T, K, E, A, H, dt, fill, kind, cap_kind):
     """Every random case again under the tail policy: the rows past the live
     total of every expert-major output are zeros, the rest unchanged."""
     test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, zero_tail=True)
+
+
+def _medium_cases(n=10):
+    # thousands of tokens and rows of 1-16 KiB: several chunks per run list,
+    # chunks of 1, 2 and 4 units, the token-row streaming blocks on (K >= 4,
+    # rows of 8 KiB or more) and off, and the reduce's token groups at every
+    # density
+    rng = np.random.default_rng(20261205)
+    out = []
+    for i in range(n):
+        K = int(rng.choice([2, 4, 6, 8]))
+        E = int(rng.choice([8, 32, 64, 128, 256]))
+        A = int(rng.choice([1, 16, 128]))
+        H = int(rng.choice([512, 2048, 4096, 5120, 7168, 8192]))
+        T = int(rng.integers(1000, 6001))
+        dt = str(rng.choice(["bf16", "fp16", "fp32"]))
+        fill = bool(rng.random() < 0.7)
+        kind = str(rng.choice(["distinct", "distinct", "masked", "repeats"]))
+        cap_kind = str(rng.choice(["worst", "worst", "tight"]))
+        out.append((300 + i, T, K, E, A, H, dt, fill, kind, cap_kind))
+    return out
+
+
+@pytest.mark.parametrize("i,T,K,E,A,H,dt,fill,kind,cap_kind", _medium_cases(),
+                         ids=lambda v: str(v) if not isinstance(v, str) else v)
+def test_random_medium_shapes(i, T, K, E, A, H, dt, fill, kind, cap_kind):
+    test_random_shape(i, T, K, E, A, H, dt, fill, kind, cap_kind, zero_tail=bool(i % 2))
