@@ -1,9 +1,10 @@
 """ep_prepare_static against ep_prepare, through the C ABI.
 
 The variant keeps prepare's scratch in the library's static device array, so
-its handle holds the routing maps alone. Two calls in a row, the second with
-a smaller routing (both large enough for the two-kernel prepare, which uses
-the scratch), then a small one that takes the one-block prepare: every
+its handle holds the routing maps alone. Calls in a row, each with a smaller
+routing than the last: one large enough for the column-scan prepare, two
+for the two-kernel prepare (all three use the scratch), then a small one
+that takes the one-block prepare: every
 routing map and every payload op run from the variant's handle must equal,
 bit for bit, what the same calls give from ep_prepare's handle, and the
 oracle's maps.
@@ -40,7 +41,10 @@ def _maps(L, handle, live):
 # the payload type sizes the run chunks (fp32 rows: half the routes a chunk)
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_prepare_static_matches_prepare(dt):
-    for name, T, H in (("dsv3", 4096, 1024), ("masked_hot", 1500, 512), ("tiny", 256, 512)):
+    # 40000 tokens of top-8: 625 units, past the 64 histogram-block rows, so
+    # the column scan (and its chunk starts) runs in the static array too
+    for name, T, H in (("dsv3", 40000, 256), ("dsv3", 4096, 1024), ("masked_hot", 1500, 512),
+                       ("tiny", 256, 512)):
         cfg = workloads.scaled(workloads.CONFIGS[name], T=T, H=H)
         r = workloads.make_routing(cfg)
         cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
