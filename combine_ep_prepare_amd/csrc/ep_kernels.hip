@@ -1481,8 +1481,9 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 // a per-lane chain of fused multiply-adds over the piece's elements, then a
 // fixed xor butterfly over the 64 lanes; the partials go to LDS, and one
 // thread per row sums its npc partials in column order. So the weight
-// gradient has the same bits on every run, and it sums each product through
-// at most N + 6 + npc roundings (N elements per 16-byte vector). Zero rows
+// gradient has the same bits on every run, and each product passes through
+// at most N + npc + 5 roundings (N elements per 16-byte vector: N in the
+// lane's chain, six in the butterfly, npc - 1 over the pieces). Zero rows
 // (pads, and the tail under the tail policy) are zeroed, with their weight
 // gradients, in each XCD's share as in the run copy.
 constexpr int kWbwdPieces = 4;                 // pieces per wavefront and round
