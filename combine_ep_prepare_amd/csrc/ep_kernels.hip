@@ -317,6 +317,8 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
   __shared__ int32_t s_run_tot[16];     // kept entries of each of this block's chunks
   __shared__ int32_t s_run_valid[16];   // valid routes of each of this block's chunks
   __shared__ int32_t s_run_base[16];    // each chunk's start in its stream's list
+  __shared__ int32_t s_wave_vb[16];     // per wavefront: its share of a chunk's start
+  __shared__ int32_t s_wave_vo[16];     // per wavefront: its share of a chunk's valid routes
   __shared__ int32_t s_live[kRunXcds];
   const int32_t run_units = in_slot ? ru : 0;
   const int nthr = blockDim.x;
@@ -525,76 +527,83 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
   //     block's units: chunk q's routes to expert e hold rows
   //     [cursor(first unit of q), cursor(first unit of q + 1)), of which those
   //     below the capacity are kept; an exclusive scan of the kept counts over
-  //     experts gives each run's start among the chunk's entries.
+  //     experts gives each run's start among the chunk's entries. The block's
+  //     chunks are handled side by side: chunk q by the run_units wavefronts
+  //     that own its units (thread group q), with two block barriers in all.
   const int nchb = run_units > 0 ? (nq + run_units - 1) / run_units : 0;
-  for (int q = 0; q < nchb; ++q) {
+  if (run_units > 0) {
+    const int q = w / run_units;                 // this thread's chunk
+    const int gsz = run_units * kWave;           // threads of a group
+    const int gt = tid - q * gsz;
+    const bool active = q < nchb;
     const int qa = q * run_units;
     const int qb = qa + run_units < nq ? qa + run_units : nq;
-    int32_t loc = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = b0 + i;
-      if (e < E) {
-        const int32_t first = s_cursor[qa * E + e];
-        const int32_t cnt = s_cursor[qb * E + e] - first;
-        const int64_t room = d.cap - (int64_t)first;
-        const int32_t kept = room <= 0 ? 0 : (room < cnt ? (int32_t)room : cnt);
-        loc += kept;
+    const int per_g = (E + gsz - 1) / gsz;
+    const int b0g = gt * per_g;
+    int32_t loc = 0, vb = 0, vo = 0;
+    if (active) {
+      for (int i = 0; i < per_g; ++i) {
+        const int e = b0g + i;
+        if (e < E) {
+          const int32_t first = s_cursor[qa * E + e];
+          const int32_t cnt = s_cursor[qb * E + e] - first;
+          const int64_t room = d.cap - (int64_t)first;
+          loc += room <= 0 ? 0 : (room < cnt ? (int32_t)room : cnt);
+        }
       }
+      // the chunk's start in its stream's list: the valid routes of the
+      // stream's earlier chunks (whole chunks of ru units each), and the
+      // chunk's own valid routes
+      const int32_t c = (u0 + qa) / ru;
+      if (scanned) {
+        if (gt == 0) vb = hv.unit_flags[U + c];    // from the column scan
+      } else {
+        const int32_t nprev = c / kRunXcds * ru;
+        for (int32_t i = gt; i < nprev; i += gsz) {
+          const int32_t cp = c % kRunXcds + kRunXcds * (i / ru);
+          vb += hv.unit_flags[cp * ru + i % ru] >> 1;
+        }
+      }
+      for (int32_t i = gt; i < qb - qa; i += gsz) vo += hv.unit_flags[u0 + qa + i] >> 1;
     }
     int32_t inc = loc;
     for (int off = 1; off < kWave; off <<= 1) {
       const int32_t t = __shfl_up(inc, off);
       if (lane >= off) inc += t;
     }
-    if (lane == kWave - 1) s_wave_tot[0][w] = inc;
-    __syncthreads();
-    int32_t ex = inc - loc;
-    for (int qq = 0; qq < w; ++qq) ex += s_wave_tot[0][qq];
-    for (int i = 0; i < per; ++i) {
-      const int e = b0 + i;
-      if (e < E) {
-        const int32_t first = s_cursor[qa * E + e];
-        const int32_t cnt = s_cursor[qb * E + e] - first;
-        const int64_t room = d.cap - (int64_t)first;
-        const int32_t kept = room <= 0 ? 0 : (room < cnt ? (int32_t)room : cnt);
-        s_rbase[q * E + e] = ex;
-        ex += kept;
-      }
-    }
-    if (tid == nthr - 1) s_run_tot[q] = ex;
-    __syncthreads();          // every wave has read s_wave_tot for its scan
-    // the chunk's start in its stream's list: the valid routes of the
-    // stream's earlier chunks (whole chunks of ru units each), and the
-    // chunk's own valid routes
-    const int32_t c = (u0 + qa) / ru;
-    int32_t vb = 0, vo = 0;
-    if (scanned) {
-      if (tid == 0) vb = hv.unit_flags[U + c];     // from the column scan
-    } else {
-      const int32_t nprev = c / kRunXcds * ru;
-      for (int32_t i = tid; i < nprev; i += nthr) {
-        const int32_t cp = c % kRunXcds + kRunXcds * (i / ru);
-        vb += hv.unit_flags[cp * ru + i % ru] >> 1;
-      }
-    }
-    for (int32_t i = tid; i < qb - qa; i += nthr) vo += hv.unit_flags[u0 + qa + i] >> 1;
     for (int off = kWave / 2; off > 0; off >>= 1) {
       vb += __shfl_xor(vb, off);
       vo += __shfl_xor(vo, off);
     }
+    if (lane == kWave - 1) s_wave_tot[0][w] = inc;
     if (lane == 0) {
-      s_wave_tot[0][w] = vb;
-      s_wave_tot[1][w] = vo;
+      s_wave_vb[w] = vb;
+      s_wave_vo[w] = vo;
     }
     __syncthreads();
-    if (tid == 0) {
-      int32_t b = 0, o = 0;
-      for (int qq = 0; qq < nw; ++qq) {
-        b += s_wave_tot[0][qq];
-        o += s_wave_tot[1][qq];
+    if (active) {
+      int32_t ex = inc - loc;
+      for (int qq = q * run_units; qq < w; ++qq) ex += s_wave_tot[0][qq];
+      for (int i = 0; i < per_g; ++i) {
+        const int e = b0g + i;
+        if (e < E) {
+          const int32_t first = s_cursor[qa * E + e];
+          const int32_t cnt = s_cursor[qb * E + e] - first;
+          const int64_t room = d.cap - (int64_t)first;
+          s_rbase[q * E + e] = ex;
+          ex += room <= 0 ? 0 : (room < cnt ? (int32_t)room : cnt);
+        }
       }
-      s_run_base[q] = b;
-      s_run_valid[q] = o;
+      if (gt == gsz - 1) s_run_tot[q] = ex;
+      if (gt == 0) {
+        int32_t sb = 0, so = 0;
+        for (int qq = q * run_units; qq < (q + 1) * run_units; ++qq) {
+          sb += s_wave_vb[qq];
+          so += s_wave_vo[qq];
+        }
+        s_run_base[q] = sb;
+        s_run_valid[q] = so;
+      }
     }
     __syncthreads();
   }
@@ -1941,9 +1950,6 @@ constexpr size_t kLdsBudget = kPrepLdsBudget;
 // 64 * E loads each); past it the column scan takes its own launch, so that
 // prepare's work stays linear in the routes.
 constexpr int kPrepDirectBlockRows = 64;
-// Routings of two-unit chunks build their run entries in the slot kernel
-// from this many units on.
-constexpr int32_t kSlotRunsMinUnits = 1536;
 // Routings of at most this many routes take the single-block prepare.
 constexpr int64_t kPrepFusedMaxRoutes = 4096;
 static_assert(kPrepFusedMaxRoutes <= (int64_t)kFusedWaves * kPrepRounds * kWave,
@@ -2038,16 +2044,15 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
     if (err != hipSuccess) return err;
   }
   // The slot kernel also builds the run entries when its blocks hold whole
-  // chunks and a chunk is four units, or two units on a routing of at least
-  // kSlotRunsMinUnits units; otherwise they take their own launch. Measured
-  // on the MI355X (prepare us, top-8 over 256 experts; 4 units a chunk
-  // saves 1.3-2.2 us and 1 unit costs 6 us): at 2 units a chunk, 27.0 in
-  // the slot kernel against 23.6 separately at 4096 tokens, 33.0 against
-  // 30.6 at 65536, but 39.7 against 42.0 at 131072 and 66.3 against 67.1
-  // at 262144 (32 experts: 42.7 against 54.2).
+  // chunks (its LDS allowing); otherwise they take their own launch.
+  // Measured on the MI355X with the block's chunks scanned side by side
+  // (prepare us, in the slot kernel against a launch of their own): top-8 of
+  // 256 experts with 2-unit chunks 22.3 against 23.4 at 4096 tokens and 28.5
+  // against 30.8 at 65536; top-2 of 8 with 1-unit chunks 20.7 against 21.3
+  // at 16384 tokens and 28.6 against 43.0 at 524288.
   int nw2 = 8;
   int in_slots = 0;
-  if (ru >= 4 || (ru == 2 && U >= kSlotRunsMinUnits)) {
+  {
     while (nw2 >= ru && slots_lds_bytes(d.E, nw2, nw2 / ru) > kLdsBudget) nw2 /= 2;
     in_slots = nw2 >= ru && nw2 % ru == 0 && slots_lds_bytes(d.E, nw2, nw2 / ru) <= kLdsBudget;
   }
