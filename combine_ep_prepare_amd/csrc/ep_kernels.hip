@@ -661,15 +661,17 @@ prepare_slots_kernel(Dims d, HandleView hv, int32_t* __restrict__ user_counts,
 // route order), load their ids once and count them into a wavefront-private
 // LDS row; the block turns the rows into counts, aligned offsets and
 // per-wavefront cursors; each wavefront then hands out rows from its ids
-// exactly as the two-kernel form does. One launch, and the histograms stay in
-// LDS. Measured on the MI355X it beats the two launches up to a few thousand
-// routes; one CU is too slow beyond.
+// exactly as the two-kernel form does. With runs_here it also writes the run
+// entries (each one-unit chunk alone in its stream's list), so that the whole
+// prepare is one launch; the histograms stay in LDS. Measured on the MI355X it
+// beats the two launches up to a few thousand routes; one CU is too slow
+// beyond.
 constexpr int kFusedWaves = 16;
 
 __global__ void __launch_bounds__(kFusedWaves * kWave)
 prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx,
                      int32_t* __restrict__ user_counts, int32_t* __restrict__ user_offsets,
-                     int nbits, int32_t ru) {
+                     int nbits, int32_t ru, int32_t runs_here) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t s_wave_tot[2][kFusedWaves];
   __shared__ int32_t s_pads_live;
@@ -684,6 +686,12 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   int32_t* s_counts = s_cur + kFusedWaves * E;   // [E]
   int32_t* s_offs = s_counts + E;                // [E+1]
   int32_t* s_padoff = s_offs + E + 1;            // [E+1]
+  // with runs_here: per chunk (one unit each, at most kRunXcds of them), each
+  // expert's first row and its run's start among the chunk's entries
+  int32_t* s_cfirst = s_padoff + E + 1;          // [kRunXcds][E]
+  int32_t* s_crb = s_cfirst + kRunXcds * E;      // [kRunXcds][E]
+  __shared__ int32_t s_ckept[kRunXcds];
+  __shared__ int32_t s_cvalid[kRunXcds];
 
   for (int i = tid; i < kFusedWaves * E; i += nthr) s_cur[i] = 0;
   if (tid == 0) {
@@ -696,7 +704,10 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
   //    registers for step 5.
   const int64_t routes = d.T * d.K;
   const int32_t n_rounds = (int32_t)((routes + kWave - 1) / kWave);
-  const int32_t per_wave = (n_rounds + kFusedWaves - 1) / kFusedWaves;   // <= kPrepRounds
+  // a power of two (<= kPrepRounds), so that each 8-round unit is the rounds
+  // of whole wavefronts
+  int32_t per_wave = 1;
+  while (per_wave * kFusedWaves < n_rounds) per_wave *= 2;
   const int32_t ra = min(n_rounds, w * per_wave);
   const int32_t nr = min(n_rounds, ra + per_wave) - ra;
   const int64_t base = (int64_t)ra * kWave;
@@ -817,11 +828,55 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
     h->run_units = ru;
     h->magic = kHandleMagic;
   }
-  // the run lists' lengths: set by the run-entry kernel that follows (no
-  // route: every list stays empty)
-  if (tid < kRunXcds) hv.header->stream_live[tid] = 0;
+  // the run lists' lengths: set below with runs_here, else by the run-entry
+  // kernel that follows (no route: every list stays empty)
+  if (tid < kRunXcds && !runs_here) hv.header->stream_live[tid] = 0;
   for (int i = tid; i < kFusedWaves * E; i += nthr) s_cur[i] += s_offs[i % E];
   __syncthreads();
+
+  // 4b. Run entries (runs_here): the routing has at most 8 units and prepare
+  //     cuts it into one-unit chunks, so chunk q is the rounds of wavefronts
+  //     [q wpc, (q + 1) wpc) and stream q's whole list. Its routes to expert
+  //     e hold rows [cursor of its first wavefront, cursor of the next
+  //     chunk's), of which those below the capacity are kept; wavefront q
+  //     scans the kept counts over experts.
+  const int32_t nch = (int32_t)((routes + kUnitRoutes - 1) / kUnitRoutes);
+  const int wpc = kPrepRounds / per_wave;
+  if (runs_here) {
+    if (w < nch) {
+      const int q = w;
+      int32_t run = 0, valid = 0;
+      for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        int32_t kept = 0;
+        if (e < E) {
+          const int32_t first = s_cur[q * wpc * E + e];
+          const int32_t next = (q + 1) * wpc < kFusedWaves ? s_cur[(q + 1) * wpc * E + e]
+                                                         : s_offs[e] + s_counts[e];
+          const int64_t room = d.cap - (int64_t)first;
+          const int32_t cnt = next - first;
+          kept = room <= 0 ? 0 : (room < cnt ? (int32_t)room : cnt);
+          valid += cnt;
+          s_cfirst[q * E + e] = first;
+        }
+        int32_t inc = kept;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int32_t t = __shfl_up(inc, off);
+          if (lane >= off) inc += t;
+        }
+        if (e < E) s_crb[q * E + e] = run + inc - kept;
+        run += __shfl(inc, kWave - 1);
+      }
+      for (int off = kWave / 2; off > 0; off >>= 1) valid += __shfl_xor(valid, off);
+      if (lane == 0) {
+        s_ckept[q] = run;
+        s_cvalid[q] = valid;
+      }
+    }
+    __syncthreads();
+    if (tid < kRunXcds) hv.header->stream_live[tid] = tid < nch ? s_cvalid[tid] : 0;
+  }
+  const int64_t scap = run_stream_cap(d.num_units);
 
   // 5. Stable slots, round by round in route order: the lowest lane of each
   //    distinct id claims popc(peers) rows from the wavefront's cursor; every
@@ -843,9 +898,20 @@ prepare_fused_kernel(Dims d, HandleView hv, const int64_t* __restrict__ topk_idx
         const bool keep = valid && row < d.cap;
         hv.slot[s] = keep ? (int32_t)row : -1;
         if (keep) hv.row_src[row] = (int32_t)s;
+        if (keep && runs_here) {
+          const int q = (int)(s / kUnitRoutes);
+          hv.runs[(int64_t)q * scap + s_crb[q * E + key] +
+                  ((int32_t)row - s_cfirst[q * E + key])] = RunEntry{(int32_t)row, (int32_t)s};
+        }
       }
     }
   });
+
+  // a chunk's valid routes dropped past the capacity leave empty entries
+  if (runs_here)
+    for (int q = 0; q < nch; ++q)
+      for (int32_t i = s_ckept[q] + tid; i < s_cvalid[q]; i += nthr)
+        hv.runs[(int64_t)q * scap + i] = RunEntry{-1, -1};
 
   // 6. Pad rows: row_src = -1 and the ascending list of live pad rows.
   for (int e = w; e < E; e += kFusedWaves) {
@@ -2022,11 +2088,16 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   const int32_t ru = run_chunk_units(U, d.K, d.V * (int64_t)sizeof(row16_t));
   const size_t fused_lds = sizeof(int32_t) * ((size_t)(kFusedWaves + 3) * d.E + 2);
   if (d.T * (int64_t)d.K <= (int64_t)kPrepFusedMaxRoutes && fused_lds <= kLdsBudget) {
-    hipLaunchKernelGGL(prepare_fused_kernel, dim3(1), dim3(kFusedWaves * kWave), fused_lds,
-                       stream, d, hv, topk_idx, user_counts, user_offsets, nbits, ru);
+    // the run entries in the same block when their rows fit its LDS (and
+    // the chunks are one unit each, which at most 8 units always are)
+    const size_t runs_lds = fused_lds + sizeof(int32_t) * 2 * kRunXcds * (size_t)d.E;
+    const int runs_here = ru == 1 && runs_lds <= kLdsBudget;
+    hipLaunchKernelGGL(prepare_fused_kernel, dim3(1), dim3(kFusedWaves * kWave),
+                       runs_here ? runs_lds : fused_lds, stream, d, hv, topk_idx, user_counts,
+                       user_offsets, nbits, ru, runs_here);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_prepare_runs(d, hv, topk_idx, ru, 1, 0, stream);
+    return runs_here ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 1, 0, stream);
   }
   const int nw1 = hist_block_units(d.E);
   const int nb = (U + nw1 - 1) / nw1;
