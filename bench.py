@@ -442,7 +442,7 @@ def measure_ceilings(T, K, H, launches, warmup):
     return out
 
 
-PREPARE_SWEEP_T = (4096, 16384, 65536, 131072, 262144, 524288)
+PREPARE_SWEEP_T = (256, 512, 1024, 2048, 4096, 16384, 65536, 131072, 262144, 524288)
 
 
 def prepare_sweep(workload: str, steps: int, warmup: int):
@@ -525,7 +525,7 @@ def main():
                     help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run")
     ap.add_argument("--prepare-sweep", action="store_true",
                     help="time prepare alone on the workload's routing recipe at token "
-                         "counts from 4096 to 524288 and print one JSON line")
+                         "counts from 256 to 524288 and print one JSON line")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
