@@ -1351,26 +1351,46 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // two routes per token (mixtral) it costs 7 us instead, so it is not used
 // there.
 //
-// P, the pieces per wavefront, depends on the row length and on the pad
-// fill. Measured on the MI355X with A/B runs on one device (dispatch /
-// combine_bwd µs), on two devices: rows of 14 KiB (dsv3) with the pad fill take
-// 119.6-124 / 124-129 at P = 4 and 118.5-119 / 114-115.6 at P = 3 (P = 2 and 5
-// are slower than both), 28 KiB rows (dsv3 in fp32) 231.5 against 226;
-// without the pad fill the same rows are 4 µs faster at P = 4; rows of 8 KiB
-// (mixtral) are fastest at P = 4 and lose 3-7% at P = 3 or 6; rows of 4 KiB
-// (qwen3) take 58.4 / 54.7 at P = 6 against 60.1 / 56.3 at P = 4, while a
+// P, the pieces per wavefront, is 4, or 6 for narrow rows with the pad fill.
+// Measured on the MI355X with A/B runs on one device (dispatch µs): rows of
+// 14 KiB (dsv3) take 121-125 at P = 4 against 131-132 at P = 3 and 135 at
+// P = 5, fp32 rows of 28 KiB 252 against 256 at P = 3; rows of 8 KiB
+// (mixtral) lose 3-7% at P = 3 or 6; rows of 4 KiB (qwen3) take 58.4 / 54.7
+// (dispatch / combine_bwd) at P = 6 against 60.1 / 56.3 at P = 4, while a
 // launch-bound routing of 1 KiB rows in 16 blocks (T = 256) loses 0.8 µs at
 // P = 6, so six pieces need a grid that fills the device.
 constexpr int kRunWaves = 8;
-constexpr int kRunPiecesLong = 3;     // rows of kRunLongRow pieces or more, pads filled
-constexpr int kRunPiecesShort = 4;    // the rest
+constexpr int kRunPieces = 4;
 constexpr int kRunPiecesNarrow = 6;   // rows of kRunNarrowRow pieces or fewer, pads filled
-constexpr int64_t kRunLongRow = 12;   // 1 KiB pieces
-constexpr int64_t kRunNarrowRow = 4;
+constexpr int64_t kRunNarrowRow = 4;  // 1 KiB pieces
 constexpr int64_t kRunNarrowMinBlocks = 2048;
-// Copy blocks per CU at most (the grid of a routing with masked routes is
-// sized for the dense case and capped here).
-constexpr int64_t kRunBlocksPerCU = 96;
+// The copy grid is sized for a dense routing, one step of kRunWaves * P
+// pieces per block, and launched whole while that is at most kRunBlocksPerCU
+// blocks per CU. A larger grid is capped at kRunCapBlocksPerCU per CU, its
+// blocks then taking steps bps apart. Large routings are mostly one GPU's
+// share of an expert-parallel layer, where most routes are masked and the
+// blocks past a stream's live pieces have no work: they exit at once, but
+// they are still dispatched after all the working ones. Measured on the
+// MI355X (dispatch µs): the masked share (about one route in eight local,
+// 14 KiB rows) takes 140 at 64 blocks per CU, 154 at 96 and 167.5 at 128;
+// the hot-expert share, whose live pieces need 1.6 steps a block at 64,
+// takes 235 against 225 at 96; dsv3 in fp32 (28 KiB rows, 112 blocks per CU
+// when dense) takes 222 whole against 251 at 96 and 265 at 64, where blocks
+// of two steps kept two regions of the lists in flight. On the masked share,
+// sizing each block's share from the live count on the device, taking the
+// next step's entries early, or dispatching the empty blocks among the
+// working ones (front and back halves in turn, or each block's steps from
+// the live step count) took 141, 142.5, 150 and 140 µs at 64 blocks per CU
+// and 178, 167, 189 and 162 at 96 or 128.
+constexpr int64_t kRunBlocksPerCU = 128;
+constexpr int64_t kRunCapBlocksPerCU = 64;
+
+// Copy blocks per stream for bps_dense one-step blocks.
+inline int64_t run_copy_blocks(int64_t bps_dense, int num_cus) {
+  if (bps_dense > (int64_t)num_cus * kRunBlocksPerCU / kRunXcds)
+    bps_dense = (int64_t)num_cus * kRunCapBlocksPerCU / kRunXcds;
+  return bps_dense < 1 ? 1 : bps_dense;
+}
 // Token rows streamed by leading blocks when they are at most this many bytes
 // in all, each row is at least kRunPrefetchMinRow bytes and each token has at
 // least kRunPrefetchMinK routes.
@@ -2177,18 +2197,13 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   const int64_t routes = d.T * (int64_t)d.K;
   const int64_t scap = run_stream_cap(d.num_units);
   const int64_t dense = run_stream_dense(d.num_units, routes);
-  int P = !d.fill_pads ? kRunPiecesShort
-          : npc >= kRunLongRow ? kRunPiecesLong
-          : npc <= kRunNarrowRow ? kRunPiecesNarrow : kRunPiecesShort;
+  int P = d.fill_pads && npc <= kRunNarrowRow ? kRunPiecesNarrow : kRunPieces;
   // narrow rows take six pieces only while the grid still fills the device
   if (P == kRunPiecesNarrow &&
       (dense * npc + kRunWaves * P - 1) / (kRunWaves * P) * kRunXcds < kRunNarrowMinBlocks)
-    P = kRunPiecesShort;
+    P = kRunPieces;
   const int64_t per_block = (int64_t)kRunWaves * P;
-  int64_t bps = (dense * npc + per_block - 1) / per_block;
-  const int64_t bps_cap = (int64_t)num_cus * kRunBlocksPerCU / kRunXcds;
-  if (bps > bps_cap) bps = bps_cap;
-  if (bps < 1) bps = 1;
+  const int64_t bps = run_copy_blocks((dense * npc + per_block - 1) / per_block, num_cus);
   const int64_t zero_max = d.zero_tail ? d.cap : ((int64_t)d.E * (d.A - 1) < d.cap
                                                       ? (int64_t)d.E * (d.A - 1) : d.cap);
   // 32-bit piece indices: a stream's list, the steps past it, the zero rows
@@ -2214,16 +2229,12 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
     g.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
   }
   const int64_t grid = (int64_t)g.npf + kRunXcds * bps;
-  if (P == kRunPiecesLong)
-    hipLaunchKernelGGL(run_rows_kernel<kRunPiecesLong>, dim3((unsigned)grid),
-                       dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
-                       &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
-  else if (P == kRunPiecesNarrow)
+  if (P == kRunPiecesNarrow)
     hipLaunchKernelGGL(run_rows_kernel<kRunPiecesNarrow>, dim3((unsigned)grid),
                        dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                        &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
   else
-    hipLaunchKernelGGL(run_rows_kernel<kRunPiecesShort>, dim3((unsigned)grid),
+    hipLaunchKernelGGL(run_rows_kernel<kRunPieces>, dim3((unsigned)grid),
                        dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                        &hv.header->status, rows_in(src), w, rows_out(dst), dst_w, g);
   return hipGetLastError();
@@ -2320,10 +2331,13 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
   if (R < 1) R = 1;
   const int64_t dense = run_stream_dense(d.num_units, routes);
   int64_t bps = (dense + R - 1) / R;
-  const int64_t bps_cap =
-      (int64_t)num_cus * (want_w ? kWbwdBlocksPerCU : kRunBlocksPerCU) / kRunXcds;
-  if (bps > bps_cap) bps = bps_cap;
-  if (bps < 1) bps = 1;
+  if (want_w) {
+    const int64_t bps_cap = (int64_t)num_cus * kWbwdBlocksPerCU / kRunXcds;
+    if (bps > bps_cap) bps = bps_cap;
+    if (bps < 1) bps = 1;
+  } else {
+    bps = run_copy_blocks(bps, num_cus);
+  }
   RunGeom geo;
   geo.npc = (uint32_t)npc;
   geo.bps = (uint32_t)bps;

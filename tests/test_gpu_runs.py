@@ -113,9 +113,9 @@ def test_runs_payload_types_and_pad_policy(dt, fill_pads, name, T, H):
 @pytest.mark.parametrize("fill_pads", [True, False])
 @pytest.mark.parametrize("T,H", [(1, 6144), (9, 6152), (300, 6144), (2049, 6152)])
 def test_runs_long_rows(T, H, fill_pads):
-    """Rows of 12 KiB and more, where the copy takes three pieces per wavefront
-    when it also fills the pads (four otherwise): 6144 is exactly 12 pieces,
-    6152 has a ragged 13th; token counts around the unit boundaries."""
+    """Rows of 12 KiB and more, with and without the pad fill: 6144 is exactly
+    12 pieces of 1 KiB, 6152 has a ragged 13th; token counts around the unit
+    boundaries."""
     rng = np.random.default_rng(zlib.crc32(f"long{T}-{H}-{fill_pads}".encode()))
     K, E, A = 8, 64, 16
     idx = _edge_ids(rng, T, K, E, "uniform")
