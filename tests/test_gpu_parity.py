@@ -66,7 +66,18 @@ def test_parity_reduced(name, T, H):
 def test_parity_full_size(name):
     """Full workload sizes, every element compared. Large payloads are drawn on
     the GPU with a seeded generator and copied to the host for the oracle."""
-    cfg = workloads.CONFIGS[name]
+    _full_size(workloads.CONFIGS[name], name)
+
+
+def test_parity_dense_routing_past_the_whole_copy_grid():
+    """The dsv3 recipe at 12288 tokens: a dense routing whose run copy, sized
+    for one step a block, would take more than 128 blocks per CU (5376 a
+    stream on 256 CUs), so its grid is capped and every block takes two or
+    three steps; every element compared."""
+    _full_size(workloads.scaled(workloads.CONFIGS["dsv3"], T=12288), "dsv3-T12288")
+
+
+def _full_size(cfg, name):
     r = workloads.make_routing(cfg)
     p = oracle.prepare(r.topk_idx, cfg.E, cfg.A,
                        oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A))
