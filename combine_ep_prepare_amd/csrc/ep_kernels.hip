@@ -1351,6 +1351,14 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // two routes per token (mixtral) it costs 7 us instead, so it is not used
 // there.
 //
+// Where the token rows are not streamed, kRunXcds leading blocks instead
+// read the run lists, block x the list its XCD copies, so that the copy
+// blocks find their entries in their XCD's L2 rather than in HBM after the
+// caches were flushed. Measured on the MI355X with the caches flushed before
+// the op: qwen3 dispatch 70.7 -> 66.4-67.2 us, combine_bwd 67.5 -> 65.3-66.2;
+// mixtral and the masked share level, warm runs level; beside the token-row
+// streaming (dsv3) it made the cold combine_bwd 6 us slower.
+//
 // P, the pieces per wavefront, is 4, or 6 for narrow rows with the pad fill.
 // Measured on the MI355X with A/B runs on one device (dispatch µs): rows of
 // 14 KiB (dsv3) take 121-125 at P = 4 against 131-132 at P = 3 and 135 at
@@ -1406,6 +1414,9 @@ struct RunGeom {
   uint32_t bps;       // copy blocks per stream
   uint32_t npf;       // leading blocks that stream the token rows
   uint32_t pf_per;    // 16-byte vectors each lane of a streaming block loads
+  uint32_t nlp;       // leading blocks that read the run lists: 0, or kRunXcds
+                      // when npf is 0
+  uint32_t lp_ent;    // entries of each list they read (even, at most scap)
   uint32_t cap_pieces;  // pieces a stream's list can hold: scap * npc
   int64_t scap;       // entries a stream's list can hold
 };
@@ -1424,6 +1435,17 @@ __device__ __forceinline__ void stream_token_rows(const Dims& d, const RunGeom& 
     const int64_t vv = base + (int64_t)i * kWave;
     if (vv < nvec) acc ^= src4[vv];
   }
+  asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
+}
+
+// A leading block's work when the token rows are not streamed: read the
+// first lp_ent entries of run list x (16 bytes, two entries, a lane) into
+// the caches with plain loads.
+__device__ __forceinline__ void read_run_list(const RunEntry* __restrict__ runs,
+                                              const RunGeom& g, uint32_t x) {
+  const row16_t* __restrict__ l4 = reinterpret_cast<const row16_t*>(runs + (int64_t)x * g.scap);
+  row16_t acc = row16_t{0u, 0u, 0u, 0u};
+  for (uint32_t i = threadIdx.x; i < g.lp_ent / 2; i += blockDim.x) acc ^= l4[i];
   asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
 }
 
@@ -1504,7 +1526,12 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
     stream_token_rows(d, g, src4, wv, lane);
     return;
   }
-  const uint32_t tb = blockIdx.x - g.npf;
+  if (blockIdx.x < g.nlp) {
+    // npf is 0 here, so block x runs on the XCD that copies list x
+    read_run_list(runs, g, blockIdx.x);
+    return;
+  }
+  const uint32_t tb = blockIdx.x - g.npf - g.nlp;
   const uint32_t x = tb % kRunXcds;
   const uint32_t k = tb / kRunXcds;
   const RunEntry* __restrict__ list = runs + (int64_t)x * g.scap;
@@ -2228,7 +2255,9 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
     g.npf = (uint32_t)npf;
     g.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
   }
-  const int64_t grid = (int64_t)g.npf + kRunXcds * bps;
+  g.nlp = g.npf == 0 ? (uint32_t)kRunXcds : 0u;
+  g.lp_ent = (uint32_t)(dense < scap ? dense : scap) & ~1u;
+  const int64_t grid = (int64_t)g.npf + g.nlp + kRunXcds * bps;
   if (P == kRunPiecesNarrow)
     hipLaunchKernelGGL(run_rows_kernel<kRunPiecesNarrow>, dim3((unsigned)grid),
                        dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
@@ -2345,6 +2374,8 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
   geo.scap = scap;
   geo.npf = 0;
   geo.pf_per = 0;
+  geo.nlp = 0;
+  geo.lp_ent = 0;
   const int64_t row_bytes = d.V * (int64_t)sizeof(row16_t);
   if (d.K >= kRunPrefetchMinK && row_bytes >= kRunPrefetchMinRow &&
       d.T * row_bytes <= kRunPrefetchMaxBytes) {
