@@ -1351,10 +1351,10 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // two routes per token (mixtral) it costs 7 us instead, so it is not used
 // there.
 //
-// Where the token rows are not streamed, kRunXcds leading blocks instead
-// read the run lists, block x the list its XCD copies, so that the copy
-// blocks find their entries in their XCD's L2 rather than in HBM after the
-// caches were flushed. Measured on the MI355X with the caches flushed before
+// Where the token rows are not streamed, leading blocks instead read the
+// run lists, each on the XCD that copies its list and at most
+// kRunListBlockBytes of it, so that the copy blocks find their entries in
+// their XCD's L2 rather than in HBM after the caches were flushed. Measured on the MI355X with the caches flushed before
 // the op: qwen3 dispatch 70.7 -> 66.4-67.2 us, combine_bwd 67.5 -> 65.3-66.2;
 // mixtral and the masked share level, warm runs level; beside the token-row
 // streaming (dsv3) it made the cold combine_bwd 6 us slower.
@@ -1406,6 +1406,9 @@ constexpr int64_t kRunPrefetchMaxBytes = (int64_t)96 << 20;
 constexpr int kRunPrefetchMinK = 4;
 constexpr int64_t kRunPrefetchMinRow = 8192;
 constexpr int64_t kRunPrefetchBlocks = 2048;
+// Run-list bytes one leading block reads, and such blocks per XCD at most.
+constexpr int64_t kRunListBlockBytes = (int64_t)64 << 10;
+constexpr int64_t kRunListBlocks = 64;
 
 // Sizes of a run-entry copy, computed on the host; every piece index of the
 // launch is below 2^32 (the launcher checks), so index arithmetic is 32-bit.
@@ -1414,8 +1417,8 @@ struct RunGeom {
   uint32_t bps;       // copy blocks per stream
   uint32_t npf;       // leading blocks that stream the token rows
   uint32_t pf_per;    // 16-byte vectors each lane of a streaming block loads
-  uint32_t nlp;       // leading blocks that read the run lists: 0, or kRunXcds
-                      // when npf is 0
+  uint32_t nlp;       // leading blocks that read the run lists: 0, or a
+                      // multiple of kRunXcds when npf is 0
   uint32_t lp_ent;    // entries of each list they read (even, at most scap)
   uint32_t cap_pieces;  // pieces a stream's list can hold: scap * npc
   int64_t scap;       // entries a stream's list can hold
@@ -1438,14 +1441,16 @@ __device__ __forceinline__ void stream_token_rows(const Dims& d, const RunGeom& 
   asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
 }
 
-// A leading block's work when the token rows are not streamed: read the
-// first lp_ent entries of run list x (16 bytes, two entries, a lane) into
-// the caches with plain loads.
+// A leading block's work when the token rows are not streamed: its share
+// (part of per) of the first lp_ent entries of run list x, 16 bytes (two
+// entries) a lane, read into the caches with plain loads.
 __device__ __forceinline__ void read_run_list(const RunEntry* __restrict__ runs,
-                                              const RunGeom& g, uint32_t x) {
+                                              const RunGeom& g, uint32_t x, uint32_t part,
+                                              uint32_t per) {
   const row16_t* __restrict__ l4 = reinterpret_cast<const row16_t*>(runs + (int64_t)x * g.scap);
   row16_t acc = row16_t{0u, 0u, 0u, 0u};
-  for (uint32_t i = threadIdx.x; i < g.lp_ent / 2; i += blockDim.x) acc ^= l4[i];
+  for (uint32_t i = part * blockDim.x + threadIdx.x; i < g.lp_ent / 2; i += per * blockDim.x)
+    acc ^= l4[i];
   asm volatile("" ::"v"(acc));      // the loads are kept (and waited for)
 }
 
@@ -1527,8 +1532,9 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
     return;
   }
   if (blockIdx.x < g.nlp) {
-    // npf is 0 here, so block x runs on the XCD that copies list x
-    read_run_list(runs, g, blockIdx.x);
+    // npf is 0 here and nlp a multiple of kRunXcds, so block i runs on the
+    // XCD that copies list i mod kRunXcds
+    read_run_list(runs, g, blockIdx.x % kRunXcds, blockIdx.x / kRunXcds, g.nlp / kRunXcds);
     return;
   }
   const uint32_t tb = blockIdx.x - g.npf - g.nlp;
@@ -2255,8 +2261,18 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
     g.npf = (uint32_t)npf;
     g.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
   }
-  g.nlp = g.npf == 0 ? (uint32_t)kRunXcds : 0u;
-  g.lp_ent = (uint32_t)(dense < scap ? dense : scap) & ~1u;
+  g.nlp = 0;
+  g.lp_ent = 0;
+  if (g.npf == 0) {
+    int64_t ent = dense < scap ? dense : scap;
+    int64_t per = (ent * (int64_t)sizeof(RunEntry) + kRunListBlockBytes - 1) / kRunListBlockBytes;
+    if (per < 1) per = 1;
+    if (per > kRunListBlocks) per = kRunListBlocks;
+    if (ent > per * kRunListBlockBytes / (int64_t)sizeof(RunEntry))
+      ent = per * kRunListBlockBytes / (int64_t)sizeof(RunEntry);
+    g.nlp = (uint32_t)(kRunXcds * per);
+    g.lp_ent = (uint32_t)ent & ~1u;
+  }
   const int64_t grid = (int64_t)g.npf + g.nlp + kRunXcds * bps;
   if (P == kRunPiecesNarrow)
     hipLaunchKernelGGL(run_rows_kernel<kRunPiecesNarrow>, dim3((unsigned)grid),
