@@ -1354,10 +1354,11 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // Where the token rows are not streamed, leading blocks instead read the
 // run lists, each on the XCD that copies its list and at most
 // kRunListBlockBytes of it, so that the copy blocks find their entries in
-// their XCD's L2 rather than in HBM after the caches were flushed. Measured on the MI355X with the caches flushed before
-// the op: qwen3 dispatch 70.7 -> 66.4-67.2 us, combine_bwd 67.5 -> 65.3-66.2;
-// mixtral and the masked share level, warm runs level; beside the token-row
-// streaming (dsv3) it made the cold combine_bwd 6 us slower.
+// their XCD's L2 rather than in HBM after the caches were flushed. Measured
+// on the MI355X with the caches flushed before the op: qwen3 dispatch 70.7
+// -> 66.4-67.2 us, combine_bwd 67.5 -> 65.3-66.2; mixtral and the masked
+// share level, warm runs level; beside the token-row streaming (dsv3) it made
+// the cold combine_bwd 6 us slower.
 //
 // P, the pieces per wavefront, is 4, or 6 for narrow rows with the pad fill.
 // Measured on the MI355X with A/B runs on one device (dispatch µs): rows of
@@ -1614,6 +1615,18 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 // lane's chain, six in the butterfly, npc - 1 over the pieces). Zero rows
 // (pads, and the tail under the tail policy) are zeroed, with their weight
 // gradients, in each XCD's share as in the run copy.
+//
+// With the weight gradient, when fewer than half of the routes hold a row
+// (one GPU's share of an expert-parallel layer), the blocks walk the
+// received rows in order instead, block b taking rows bR, (b + nb)R, ... and
+// skipping the pads: each token row is then read about once either way, and
+// the rows of y and of the gradient stream in address order. Same pieces,
+// same partial sums, same bits. Measured on the MI355X (µs, warm / cold):
+// the masked share 209-212 / 220-222 against 211-212 / 235-236 along the
+// run lists, the hot-expert share 377-379 / 386-388 against 394-395 /
+// 392-393; dsv3 takes 289 in received order against 248, qwen3 and mixtral
+// 5-10% more. The row gradient alone keeps the run lists: with both walks
+// in one kernel it ran 4-6 us slower on qwen3 and mixtral.
 constexpr int kWbwdPieces = 4;                 // pieces per wavefront and round
 constexpr int kWbwdRounds = 2;                 // rounds per block step (weight gradient)
 constexpr int kWbwdBlocksPerCU = 32;           // grid cap (weight gradient)
@@ -1625,7 +1638,8 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
                 const int32_t* __restrict__ pad_rows, uint32_t* status,
                 const row16_t* __restrict__ g4, const row16_t* __restrict__ y4,
                 const float* __restrict__ rw, row16_t* __restrict__ o4,
-                float* __restrict__ grad_w, RunGeom g, uint32_t rows_per_step) {
+                float* __restrict__ grad_w, RunGeom g, uint32_t rows_per_step,
+                const int32_t* __restrict__ row_src) {
   using Pl = Payload<DT>;
   __shared__ float s_part[kWbwdMaxPartials];
   const uint32_t lane = threadIdx.x & (kWave - 1);
@@ -1644,71 +1658,92 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
     if (tb == 0 && threadIdx.x == 0) atomicOr(status, EP_STATUS_LAYOUT);
     return;
   }
-  const uint32_t live0 = (uint32_t)h->stream_live[x];
-  const uint32_t live = live0 < (uint32_t)g.scap ? live0 : (uint32_t)g.scap;
   const uint32_t routes = (uint32_t)(d.T * d.K);
   const uint32_t R = rows_per_step;
   constexpr uint32_t kRound = kRunWaves * kWbwdPieces;
-  for (uint32_t e0 = k * R; e0 < live; e0 += g.bps * R) {
-    const uint32_t nrows = live - e0 < R ? live - e0 : R;
-    const uint32_t npieces = nrows * g.npc;
-    for (uint32_t r0 = 0; r0 < npieces; r0 += kRound) {
-      RunEntry ent[kWbwdPieces];
-      uint32_t col[kWbwdPieces];
-      bool use[kWbwdPieces];
-      static_for<kWbwdPieces>([&](auto j) {
-        const uint32_t pp = r0 + j * kRunWaves + wv;
-        const bool in = pp < npieces;
-        const uint32_t pq = in ? pp : 0u;
-        const uint32_t ei = pq / g.npc;
-        col[j] = pq - ei * g.npc;
-        ent[j] = list[e0 + ei];
-        use[j] = in && ent[j].row >= 0 && (int64_t)ent[j].row < d.cap &&
-                 (uint32_t)ent[j].route < routes;
-      });
-      row16_t gv[kWbwdPieces], yv[kWbwdPieces];
-      float wk[kWbwdPieces];
-      static_for<kWbwdPieces>([&](auto j) {
-        const uint32_t t = use[j] ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
-        const int64_t r = use[j] ? (int64_t)ent[j].row : 0;
-        const int64_t v = (int64_t)(col[j] * kWave + lane);
-        const int64_t vc = v < V ? v : V - 1;
-        gv[j] = load_row16<kScatterNtLoad>(g4 + (int64_t)t * V + vc);
-        if constexpr (WANT_W) yv[j] = load_row16<kReduceNtLoad>(y4 + r * V + vc);
-        wk[j] = rw[r];
-      });
-      static_for<kWbwdPieces>([&](auto j) {
-        const int64_t v = (int64_t)(col[j] * kWave + lane);
-        float prod[Pl::N];
-        float pd = 0.0f;
-        static_for<Pl::N>([&](auto q) {
-          constexpr int i = q;
-          const float gi = Pl::template get<i>(gv[j]);
-          prod[i] = wk[j] * gi;
-          if constexpr (WANT_W) pd = __builtin_fmaf(gi, Pl::template get<i>(yv[j]), pd);
-        });
-        if (use[j] && v < V)
-          store_row16<kScatterNtStore>(o4 + (int64_t)ent[j].row * V + v, Pl::pack(prod));
-        if constexpr (WANT_W) {
-          pd = v < V ? pd : 0.0f;
-          for (int off = kWave / 2; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
+  // The walk over `live` entries, this block taking entries kb R, (kb +
+  // kstride) R, ...; entry(e) gives entry e. Instantiated once per walk, so
+  // that neither tests the walk per piece.
+  auto walk = [&](auto entry, uint32_t live, uint32_t kb, uint32_t kstride) {
+    for (uint32_t e0 = kb * R; e0 < live; e0 += kstride * R) {
+      const uint32_t nrows = live - e0 < R ? live - e0 : R;
+      const uint32_t npieces = nrows * g.npc;
+      for (uint32_t r0 = 0; r0 < npieces; r0 += kRound) {
+        RunEntry ent[kWbwdPieces];
+        uint32_t col[kWbwdPieces];
+        bool use[kWbwdPieces];
+        static_for<kWbwdPieces>([&](auto j) {
           const uint32_t pp = r0 + j * kRunWaves + wv;
-          if (lane == 0 && pp < npieces) s_part[pp] = pd;
-        }
-      });
-    }
-    if constexpr (WANT_W) {
-      __syncthreads();
-      if (threadIdx.x < nrows) {
-        const RunEntry e = list[e0 + threadIdx.x];
-        if (e.row >= 0 && (int64_t)e.row < d.cap && (uint32_t)e.route < routes) {
-          float sum = 0.0f;
-          for (uint32_t c = 0; c < g.npc; ++c) sum += s_part[threadIdx.x * g.npc + c];
-          grad_w[e.row] = sum;
-        }
+          const bool in = pp < npieces;
+          const uint32_t pq = in ? pp : 0u;
+          const uint32_t ei = pq / g.npc;
+          col[j] = pq - ei * g.npc;
+          ent[j] = entry(e0 + ei);
+          use[j] = in && ent[j].row >= 0 && (int64_t)ent[j].row < d.cap &&
+                   (uint32_t)ent[j].route < routes;
+        });
+        row16_t gv[kWbwdPieces], yv[kWbwdPieces];
+        float wk[kWbwdPieces];
+        static_for<kWbwdPieces>([&](auto j) {
+          const uint32_t t = use[j] ? (uint32_t)ent[j].route / (uint32_t)d.K : 0u;
+          const int64_t r = use[j] ? (int64_t)ent[j].row : 0;
+          const int64_t v = (int64_t)(col[j] * kWave + lane);
+          const int64_t vc = v < V ? v : V - 1;
+          gv[j] = load_row16<kScatterNtLoad>(g4 + (int64_t)t * V + vc);
+          if constexpr (WANT_W) yv[j] = load_row16<kReduceNtLoad>(y4 + r * V + vc);
+          wk[j] = rw[r];
+        });
+        static_for<kWbwdPieces>([&](auto j) {
+          const int64_t v = (int64_t)(col[j] * kWave + lane);
+          float prod[Pl::N];
+          float pd = 0.0f;
+          static_for<Pl::N>([&](auto q) {
+            constexpr int i = q;
+            const float gi = Pl::template get<i>(gv[j]);
+            prod[i] = wk[j] * gi;
+            if constexpr (WANT_W) pd = __builtin_fmaf(gi, Pl::template get<i>(yv[j]), pd);
+          });
+          if (use[j] && v < V)
+            store_row16<kScatterNtStore>(o4 + (int64_t)ent[j].row * V + v, Pl::pack(prod));
+          if constexpr (WANT_W) {
+            pd = v < V ? pd : 0.0f;
+            for (int off = kWave / 2; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
+            const uint32_t pp = r0 + j * kRunWaves + wv;
+            if (lane == 0 && pp < npieces) s_part[pp] = pd;
+          }
+        });
       }
-      __syncthreads();
+      if constexpr (WANT_W) {
+        __syncthreads();
+        if (threadIdx.x < nrows) {
+          const RunEntry e = entry(e0 + threadIdx.x);
+          if (e.row >= 0 && (int64_t)e.row < d.cap && (uint32_t)e.route < routes) {
+            float sum = 0.0f;
+            for (uint32_t c = 0; c < g.npc; ++c) sum += s_part[threadIdx.x * g.npc + c];
+            grad_w[e.row] = sum;
+          }
+        }
+        __syncthreads();
+      }
     }
+  };
+  // with the weight gradient, the received rows in order on sparse routings
+  // (a pad giving row -1); else the run list
+  bool by_rows = false;
+  if constexpr (WANT_W) {
+    const int64_t rows_total = (int64_t)hh.total < d.cap ? (int64_t)hh.total : d.cap;
+    if (2 * (rows_total - (int64_t)hh.pads_live) < (int64_t)routes) {
+      by_rows = true;
+      walk([&](uint32_t e) -> RunEntry {
+        const int32_t s = row_src[e];
+        return RunEntry{s >= 0 ? (int32_t)e : -1, s};
+      }, (uint32_t)rows_total, tb, g.bps * kRunXcds);
+    }
+  }
+  if (!by_rows) {
+    const uint32_t live0 = (uint32_t)h->stream_live[x];
+    walk([&](uint32_t e) -> RunEntry { return list[e]; },
+         live0 < (uint32_t)g.scap ? live0 : (uint32_t)g.scap, k, g.bps);
   }
   if (d.fill_pads || d.zero_tail) {
     const ZeroRows zr = zero_rows_of(hh, d);
@@ -2408,12 +2443,12 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
       hipLaunchKernelGGL((run_wbwd_kernel<DT, true>), dim3((unsigned)grid),
                          dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                          &hv.header->status, rows_in(g), rows_in(y), rw, rows_out(grad_rows),
-                         grad_w, geo, (uint32_t)R);
+                         grad_w, geo, (uint32_t)R, hv.row_src);
     } else {
       hipLaunchKernelGGL((run_wbwd_kernel<DT, false>), dim3((unsigned)grid),
                          dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                          &hv.header->status, rows_in(g), nullptr, rw, rows_out(grad_rows),
-                         nullptr, geo, (uint32_t)R);
+                         nullptr, geo, (uint32_t)R, hv.row_src);
     }
     return hipGetLastError();
   });

@@ -99,6 +99,31 @@ def test_weighted_edge_cases(label, T, K, E, A, H):
     _case(label, idx, E, A, H, cap, rng)
 
 
+@pytest.mark.parametrize("label,masked", [("sparse_rows", 0.85), ("dense_lists", 0.0)])
+def test_weighted_both_walks(label, masked):
+    """The backward walks the received rows in order when fewer than half of
+    the routes hold a row, else the run lists: the same routing shape on
+    either side, every output checked."""
+    T, K, E, A, H = 1500, 8, 48, 8, 1032
+    rng = np.random.default_rng(zlib.crc32(label.encode()))
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int64)
+    idx[rng.random((T, K)) < masked] = -1
+    _case(label, idx, E, A, H, T * K + E * (A - 1), rng)
+
+
+def test_weighted_sparse_rows_in_several_rounds():
+    """The hot-expert recipe at 20000 tokens and H = 7168: the received rows
+    (about 37000 of them) outnumber what one round of the capped grid takes
+    (32768 on 256 CUs), so blocks walk rows in two rounds."""
+    cfg = workloads.scaled(workloads.CONFIGS["masked_hot"], T=20000)
+    r = workloads.make_routing(cfg)
+    p = oracle.prepare(r.topk_idx, cfg.E, cfg.A,
+                       oracle.recv_capacity_worst(cfg.T, cfg.K, cfg.E, cfg.A))
+    cap = (p.total + 4095) // 4096 * 4096
+    _case("masked_hot-T20000", r.topk_idx, cfg.E, cfg.A, cfg.H, cap,
+          np.random.default_rng(34))
+
+
 def test_weighted_full_size_dsv3():
     cfg = workloads.CONFIGS["dsv3"]
     r = workloads.make_routing(cfg)
