@@ -32,18 +32,21 @@ struct RunEntry {
 };
 constexpr int kRunXcds = 8;             // chunks are dealt round-robin to 8 streams
 constexpr int kRunMaxUnits = 4;         // at most 4 units (2048 routes) per chunk
-constexpr int64_t kRunChunkBytes = 2560 * 1024;   // token rows of one chunk, at most
+constexpr int64_t kRunChunkBytes = 3584 * 1024;   // token rows of one chunk, at most
 
 // Units per chunk: the most (up to 4) whose tokens' rows (RU * 512 / K of
 // them) fit in kRunChunkBytes, so that a chunk's token rows stay in one XCD's
 // 4 MB L2 while its runs are written; fewer if that leaves some stream with
 // no chunk. Chosen by prepare from its layout's row size and kept in the
 // header, so payload ops of another payload type read the same entries.
-// Measured on the MI355X (dsv3 routing, fp32 rows of 28 KiB): with 3.5 MiB
-// of token rows a chunk, every row was fetched 2.6 times from beyond the L2
-// (307 MB for 117 MB of rows); with 2.5 MiB (one unit a chunk) 1.08 times,
-// for 2% more time (the re-reads had been Infinity Cache hits). bf16 rows of
-// every workload keep their chunk sizes or take the same time.
+// Measured on the MI355X (dsv3 routing, the copy launched one step a block):
+// 3.5 MiB (four units a chunk for 14 KiB rows, two for fp32 rows of 28 KiB)
+// against 2.5 MiB takes combine_bwd from 127 to 120 us warm and 128 to 125
+// cold, dispatch and the masked shares level, with the same bytes fetched
+// (fp32 dispatch 1506 MB for 1505 algorithmic); the weighted backward on
+// dsv3 fetches 707 MB for 625 (its y rows push token rows out of the L2) in
+// the same time, and its row gradient alone is 8 us faster on dsv3 and 8 us
+// slower on the hot-expert share.
 inline int32_t run_chunk_units(int32_t units, int32_t K, int64_t row_bytes) {
   int32_t ru = kRunMaxUnits;
   while (ru > 1 && (int64_t)ru * kUnitRoutes / K * row_bytes > kRunChunkBytes) ru /= 2;

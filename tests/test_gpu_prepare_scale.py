@@ -54,13 +54,13 @@ CASES = [
 
 
 # the layout's row sets the chunk size (token rows of a chunk at most
-# 2.5 MiB): 128-byte rows take 4 units a chunk (run entries built in the
-# slot kernel), 14 KiB rows 2 (in the slot kernel from 1536 units, else in
-# their own launch), 28 KiB rows 1 (their own launch)
-ROWS = [(64, "bf16"), (7168, "bf16"), (7168, "fp32")]
+# 3.5 MiB): 128-byte rows take 4 units a chunk, fp32 rows of 28 KiB 2 and
+# fp32 rows of 56 KiB 1; the run entries are built in the slot kernel where
+# its LDS holds a block's chunks, else in a launch of their own
+ROWS = [(64, "bf16"), (7168, "fp32"), (14336, "fp32")]
 
 
-@pytest.mark.parametrize("H,dt", ROWS, ids=["row128B", "row14KiB", "row28KiB"])
+@pytest.mark.parametrize("H,dt", ROWS, ids=["row128B", "row28KiB", "row56KiB"])
 @pytest.mark.parametrize("label,T,K,E,A,masked", CASES, ids=[c[0] for c in CASES])
 def test_prepare_both_scan_forms(label, T, K, E, A, masked, H, dt):
     idx = _routing(label, T, K, E, masked)
