@@ -140,11 +140,15 @@ def test_graph_replays_match_eager_and_oracle(name, T, H, zero_tail):
                                   oracle.combine(p, host_bf16(g_step.expert_out)))
 
 
-@pytest.mark.parametrize("dt,fill", [("fp32", False), ("fp16", True)])
-def test_graph_weighted_ops_other_payload_types(dt, fill):
+@pytest.mark.parametrize("dt,fill,alternate", [("fp32", False, False), ("fp16", True, False),
+                                              ("bf16", True, True)])
+def test_graph_weighted_ops_other_payload_types(dt, fill, alternate):
     # prepare, dispatch, weighted combine and its backward captured on an
     # fp32 layout without the pad fill (and fp16 with it); every replay on new
-    # routing equals an eager run bit for bit, the weight gradient included
+    # routing equals an eager run bit for bit, the weight gradient included.
+    # With `alternate`, odd replays mask 85% of the routes, so the backward's
+    # walk (received rows on sparse routings, run lists on dense ones),
+    # chosen on the device, changes from replay to replay of one graph.
     cfg = workloads.CONFIGS["qwen3"]
     T, H = 600, 512
     cap = ep.recv_capacity_worst(T, cfg.K, cfg.E, cfg.A)
@@ -168,7 +172,10 @@ def test_graph_weighted_ops_other_payload_types(dt, fill):
     def fill_inputs(b, seed):
         c = workloads.scaled(cfg, T=T, H=H)
         r = workloads.make_routing(c, seed)
-        b["idx"].copy_(torch.from_numpy(r.topk_idx))
+        idx = r.topk_idx.copy()
+        if alternate and seed % 2:
+            idx[np.random.default_rng(seed).random(idx.shape) < 0.85] = -1
+        b["idx"].copy_(torch.from_numpy(idx))
         b["w"].copy_(torch.from_numpy(r.topk_weights))
         b["x"].copy_(workloads.randn_bf16_torch((T, H), 600 + seed).to(tdt))
         b["g"].copy_(workloads.randn_bf16_torch((T, H), 700 + seed).to(tdt))
