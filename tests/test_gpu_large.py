@@ -4,7 +4,7 @@ Every route local: T = 40960 tokens, each with 8 distinct experts of 32
 drawn uniformly, H = 7168 bf16 (14 KiB rows), alignment 128. That gives
 327 680 routes and about 331 000 live received rows, 4.7 GB: rows past
 149 796 start beyond 2^31 bytes and rows past 299 593 beyond 2^32, so every
-64-bit row offset in the copy, the scatter and the reduce is exercised. The
+64-bit row offset in the run copy and the reduce is exercised. The
 shape is the masked workload's (DeepSeek-V3 rows, a local slice of 32
 experts) with no route masked, the largest receive buffer that slice can
 need.
