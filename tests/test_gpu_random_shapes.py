@@ -1,5 +1,5 @@
 """Randomised GPU parity over shapes: top-k from 1 to 64 (every token-group
-size of the scatter), experts 1 to 400, alignments 1 to 128, ragged hidden
+size of the reduce), experts 1 to 400, alignments 1 to 128, ragged hidden
 sizes (short rows, long rows, and rows around the copies' 8 KiB prefetch
 rule),
 routings around the one-block prepare's cutover, masked, repeated and out-of-range ids, tight and overflowing
