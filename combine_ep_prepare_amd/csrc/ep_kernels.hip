@@ -1851,8 +1851,11 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
         static_for<KT>([&](auto k) {
           if (lane == k) mine = sl[k];
         });
-        if (cb == 0 && dst_w != nullptr && lane < KT)
-          dst_w[t * KT + lane] = (mine >= 0 && g_w != nullptr) ? g_w[mine] : 0.0f;
+        // the gathered weight gradient is loaded here and stored after the
+        // row loads, so that the row loads do not wait for it
+        const bool wgrad = cb == 0 && dst_w != nullptr;
+        float gwv = 0.0f;
+        if (wgrad && g_w != nullptr && lane < KT && mine >= 0) gwv = g_w[mine];
         float wl = 0.0f;
         if constexpr (WEIGHTED) {
           if (lane < KT && mine >= 0) wl = rw[mine];
@@ -1887,6 +1890,7 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
         if (v < V)
           store_row16<kReduceNtStore>(dst4 + t * V + v,
                                       have ? P::pack(acc) : row16_t{0u, 0u, 0u, 0u});
+        if (wgrad && lane < KT) dst_w[t * KT + lane] = gwv;
       }
       return;
     }
@@ -1911,8 +1915,10 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
     const int64_t t0 = g * G;
     const int ntok = (int)((int64_t)G < d.T - t0 ? (int64_t)G : d.T - t0);
     const int64_t s = g * GK + lane;
-    if (cb == 0 && dst_w != nullptr && lane < GK && s < routes)
-      dst_w[s] = (sl >= 0 && g_w != nullptr) ? g_w[sl] : 0.0f;
+    // the gathered weight gradient: loaded here, stored after the rows
+    const bool wgrad = cb == 0 && dst_w != nullptr;
+    float gwv = 0.0f;
+    if (wgrad && g_w != nullptr && lane < GK && s < routes && sl >= 0) gwv = g_w[sl];
     float wl = 0.0f;
     if constexpr (WEIGHTED) {
       if (sl >= 0) wl = rw[sl];
@@ -1981,6 +1987,7 @@ reduce_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
       done = cur + 1;
     }
     for (; done < ntok; ++done) store_tok(done, false);
+    if (wgrad && lane < GK && s < routes) dst_w[s] = gwv;
   }
 }
 
