@@ -2176,7 +2176,6 @@ hipError_t launch_prepare_runs(const Dims& d, const HandleView& hv, const int64_
 hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* topk_idx,
                           int32_t* user_counts, int32_t* user_offsets, int num_cus,
                           hipStream_t stream) {
-  (void)num_cus;
   const int nbits = key_bits(d.E);
   const int U = d.num_units;
   // run chunks sized from this layout's payload row
@@ -2216,12 +2215,22 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
   // 256 experts with 2-unit chunks 22.3 against 23.4 at 4096 tokens and 28.5
   // against 30.8 at 65536; top-2 of 8 with 1-unit chunks 20.7 against 21.3
   // at 16384 tokens and 28.6 against 43.0 at 524288.
-  int nw2 = 8;
-  int in_slots = 0;
-  {
-    while (nw2 >= ru && slots_lds_bytes(d.E, nw2, nw2 / ru) > kLdsBudget) nw2 /= 2;
-    in_slots = nw2 >= ru && nw2 % ru == 0 && slots_lds_bytes(d.E, nw2, nw2 / ru) <= kLdsBudget;
-  }
+  // A block holds one chunk (ru wavefronts), or whole chunks up to 8 units
+  // while it has fewer threads than experts (its per-expert steps then take
+  // one pass) or one chunk a block would give more blocks than CUs: a
+  // wavefront hands out its unit's rows one round after another, so while
+  // the grid fits the CUs, smaller blocks spread the work over more of them,
+  // and past that they queue and repeat each block's setup. Measured
+  // (prepare us, one chunk a block against eight units): top-8 of 256 at
+  // 4096 tokens 20.3 against 22.1, top-8 of 128 at 8192 19.0 against 20.5,
+  // the 32-expert masked share at 32768 19.3 against 20.7, top-2 of 8 at
+  // 16384 16.8 against 20.6 and at 131072 18.7 against 22.0; level at 256
+  // blocks; top-8 of 256 at 524288 tokens (2048 blocks) 104 against 95, and
+  // at 1024 tokens (2-unit chunks, 128 threads) 26.0 against 24.5.
+  int nw2 = ru;
+  while (nw2 < 8 && (nw2 * kWave < d.E || (U + nw2 - 1) / nw2 > num_cus)) nw2 *= 2;
+  while (nw2 > ru && slots_lds_bytes(d.E, nw2, nw2 / ru) > kLdsBudget) nw2 /= 2;
+  const int in_slots = slots_lds_bytes(d.E, nw2, nw2 / ru) <= kLdsBudget;
   if (!in_slots) {
     nw2 = 8;
     while (nw2 > 1 && slots_lds_bytes(d.E, nw2, 0) > kLdsBudget) nw2 /= 2;
