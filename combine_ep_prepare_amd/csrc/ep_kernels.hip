@@ -1360,17 +1360,20 @@ scatter_rows_kernel(Dims d, const HandleHeader* __restrict__ h,
 // share level, warm runs level; beside the token-row streaming (dsv3) it made
 // the cold combine_bwd 6 us slower.
 //
-// P, the pieces per wavefront, is 4, or 6 for narrow rows with the pad fill.
+// P, the pieces per wavefront, is 4, or 8 for narrow rows with the pad fill.
 // Measured on the MI355X with A/B runs on one device (dispatch µs): rows of
 // 14 KiB (dsv3) take 121-125 at P = 4 against 131-132 at P = 3 and 135 at
 // P = 5, fp32 rows of 28 KiB 252 against 256 at P = 3; rows of 8 KiB
 // (mixtral) lose 3-7% at P = 3 or 6; rows of 4 KiB (qwen3) take 58.4 / 54.7
-// (dispatch / combine_bwd) at P = 6 against 60.1 / 56.3 at P = 4, while a
-// launch-bound routing of 1 KiB rows in 16 blocks (T = 256) loses 0.8 µs at
-// P = 6, so six pieces need a grid that fills the device.
+// (dispatch / combine_bwd) at P = 6 against 60.1 / 56.3 at P = 4, and
+// 57.4-58.0 / 53.5-53.8 at P = 8 against 59.9-60.6 / 54.3-55.1 at P = 6 on
+// warm steps, 68.0-68.3 / 68.2-68.3 against 66.3-66.8 / 64.9-65.5 after a
+// cache flush (P = 5 level with 6). A launch-bound routing of 1 KiB rows in
+// 16 blocks (T = 256) loses 0.8 µs at P = 6, so the wide steps need a grid
+// that fills the device.
 constexpr int kRunWaves = 8;
 constexpr int kRunPieces = 4;
-constexpr int kRunPiecesNarrow = 6;   // rows of kRunNarrowRow pieces or fewer, pads filled
+constexpr int kRunPiecesNarrow = 8;   // rows of kRunNarrowRow pieces or fewer, pads filled
 constexpr int64_t kRunNarrowRow = 4;  // 1 KiB pieces
 constexpr int64_t kRunNarrowMinBlocks = 2048;
 // The copy grid is sized for a dense routing, one step of kRunWaves * P
@@ -2282,7 +2285,7 @@ hipError_t launch_run_rows(const Dims& d, const HandleView& hv, const void* src,
   const int64_t scap = run_stream_cap(d.num_units);
   const int64_t dense = run_stream_dense(d.num_units, routes);
   int P = d.fill_pads && npc <= kRunNarrowRow ? kRunPiecesNarrow : kRunPieces;
-  // narrow rows take six pieces only while the grid still fills the device
+  // narrow rows take eight pieces only while the grid still fills the device
   if (P == kRunPiecesNarrow &&
       (dense * npc + kRunWaves * P - 1) / (kRunWaves * P) * kRunXcds < kRunNarrowMinBlocks)
     P = kRunPieces;
