@@ -10,9 +10,11 @@ start of its histogram block and its first unit. These cases sit on both
 sides of the 64-row switch, with 100, 256 and 2048 experts, masked routes
 and ragged tails, for chunks of 4, 2 and 1 units (whose run entries are
 built in the slot kernel or in a launch of their own, their list starts
-summed there or taken from the column scan), and compare counts, offsets,
-slot map, row map, run entries and status with the oracle bit for bit; two
-also run dispatch and combine on the prepared handle.
+summed there or taken from the column scan), and on both sides of the
+slot kernel's block sizing (one chunk a block, or more while the grid would
+outnumber the CUs or a block has fewer threads than experts), and compare
+counts, offsets, slot map, row map, run entries and status with the oracle
+bit for bit; two also run dispatch and combine on the prepared handle.
 """
 import zlib
 
@@ -50,6 +52,11 @@ CASES = [
     ("direct_wide_experts", 20000, 8, 2048, 1, 0.0),  # 313 units, 40 rows
     ("scan_wide_experts", 66000, 8, 2048, 16, 0.2),  # 1032 units, 129 rows
     ("scan_masked_1m", 131072, 8, 256, 128, 0.875),  # 2048 units, 256 rows
+    # the slot kernel's blocks: one chunk each while that gives no more
+    # blocks than the 256 CUs and a thread per expert, else larger
+    ("slot_blocks_at_cus", 65536, 8, 128, 16, 0.0),    # 1024 units, 256 blocks of 4
+    ("slot_blocks_past_cus", 65600, 8, 128, 16, 0.0),  # 1025 units, blocks of 8
+    ("slot_blocks_per_expert", 4096, 8, 300, 2, 0.3),  # 64 units, 300 experts
 ]
 
 
