@@ -1430,13 +1430,14 @@ struct RunGeom {
 
 namespace {
 
-// A leading block's work: stream its slice of the token rows [T, H] through
-// the caches with plain loads.
+// A leading block's work (W wavefronts): stream its slice of the token rows
+// [T, H] through the caches with plain loads.
+template <int W>
 __device__ __forceinline__ void stream_token_rows(const Dims& d, const RunGeom& g,
                                                   const row16_t* __restrict__ src4,
                                                   uint32_t wv, uint32_t lane) {
   const int64_t nvec = d.T * d.V;
-  const int64_t base = ((int64_t)blockIdx.x * kRunWaves + wv) * g.pf_per * kWave + lane;
+  const int64_t base = ((int64_t)blockIdx.x * W + wv) * g.pf_per * kWave + lane;
   row16_t acc = row16_t{0u, 0u, 0u, 0u};
   for (uint32_t i = 0; i < g.pf_per; ++i) {
     const int64_t vv = base + (int64_t)i * kWave;
@@ -1532,7 +1533,7 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t V = d.V;
   if (blockIdx.x < g.npf) {
-    stream_token_rows(d, g, src4, wv, lane);
+    stream_token_rows<kRunWaves>(d, g, src4, wv, lane);
     return;
   }
   if (blockIdx.x < g.nlp) {
@@ -1607,7 +1608,7 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 //   grad_rows[r] = payload(fp32(w_r * g_t))    grad_w[r] = sum_h g_t[h] * y_r[h]
 // Block (x, k) of stream x takes the rows of R consecutive entries of x's
 // list per step (entries kR, (k + bps)R, ...), their R * npc pieces dealt to
-// the eight wavefronts as in the run copy (so the block writes each row's
+// the block's wavefronts as in the run copy (so the block writes each row's
 // pieces as one dense band, and a chunk's token rows are read from memory
 // once and then from its XCD's L2). Each piece's share of the dot product is
 // a per-lane chain of fused multiply-adds over the piece's elements, then a
@@ -1630,13 +1631,27 @@ run_rows_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
 // 392-393; dsv3 takes 289 in received order against 248, qwen3 and mixtral
 // 5-10% more. The row gradient alone keeps the run lists: with both walks
 // in one kernel it ran 4-6 us slower on qwen3 and mixtral.
+//
+// With the weight gradient a block has four wavefronts, and the grid cap
+// doubles, so the waves per CU stay the same: each block step's two barriers
+// then hold fewer wavefronts. Measured on the MI355X (µs, warm / cold,
+// against eight wavefronts): dsv3 245.4 / 245.0 against 247.3 / 246.5, the
+// masked share 206.9 / 219.4 against 210.3 / 221.0, the hot-expert share
+// 367.8 / 388.3 against 377.2 / 386.9, qwen3 117.0 / 121.2 against 119.2 /
+// 122.6, mixtral 112.9 / 131.3 against 112.2 / 128.5. The row gradient
+// alone keeps eight (four made dsv3's 3-8 us slower).
 constexpr int kWbwdPieces = 4;                 // pieces per wavefront and round
 constexpr int kWbwdRounds = 2;                 // rounds per block step (weight gradient)
-constexpr int kWbwdBlocksPerCU = 32;           // grid cap (weight gradient)
+constexpr int kWbwdWaves = 4;                  // wavefronts per block (weight gradient)
+constexpr int kWbwdBlocksPerCU = 64;           // grid cap (weight gradient)
 constexpr int kWbwdMaxPartials = 1024;         // LDS partials of one block step
 
+__host__ __device__ constexpr int wbwd_waves(bool want_w) {
+  return want_w ? kWbwdWaves : kRunWaves;
+}
+
 template <int DT, bool WANT_W>
-__global__ void __launch_bounds__(kRunWaves * kWave)
+__global__ void __launch_bounds__(wbwd_waves(WANT_W) * kWave)
 run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __restrict__ runs,
                 const int32_t* __restrict__ pad_rows, uint32_t* status,
                 const row16_t* __restrict__ g4, const row16_t* __restrict__ y4,
@@ -1644,12 +1659,13 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
                 float* __restrict__ grad_w, RunGeom g, uint32_t rows_per_step,
                 const int32_t* __restrict__ row_src) {
   using Pl = Payload<DT>;
+  constexpr int kW = wbwd_waves(WANT_W);
   __shared__ float s_part[kWbwdMaxPartials];
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t V = d.V;
   if (blockIdx.x < g.npf) {
-    stream_token_rows(d, g, g4, wv, lane);
+    stream_token_rows<kW>(d, g, g4, wv, lane);
     return;
   }
   const uint32_t tb = blockIdx.x - g.npf;
@@ -1663,7 +1679,7 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
   }
   const uint32_t routes = (uint32_t)(d.T * d.K);
   const uint32_t R = rows_per_step;
-  constexpr uint32_t kRound = kRunWaves * kWbwdPieces;
+  constexpr uint32_t kRound = kW * kWbwdPieces;
   // The walk over `live` entries, this block taking entries kb R, (kb +
   // kstride) R, ...; entry(e) gives entry e. Instantiated once per walk, so
   // that neither tests the walk per piece.
@@ -1676,7 +1692,7 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
         uint32_t col[kWbwdPieces];
         bool use[kWbwdPieces];
         static_for<kWbwdPieces>([&](auto j) {
-          const uint32_t pp = r0 + j * kRunWaves + wv;
+          const uint32_t pp = r0 + j * kW + wv;
           const bool in = pp < npieces;
           const uint32_t pq = in ? pp : 0u;
           const uint32_t ei = pq / g.npc;
@@ -1711,7 +1727,7 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
           if constexpr (WANT_W) {
             pd = v < V ? pd : 0.0f;
             for (int off = kWave / 2; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
-            const uint32_t pp = r0 + j * kRunWaves + wv;
+            const uint32_t pp = r0 + j * kW + wv;
             if (lane == 0 && pp < npieces) s_part[pp] = pd;
           }
         });
@@ -1756,7 +1772,7 @@ run_wbwd_kernel(Dims d, const HandleHeader* __restrict__ h, const RunEntry* __re
     const uint32_t send = (x + 1) * share < all ? (x + 1) * share : all;
     const uint32_t lo = x * share + k * qn;
     const uint32_t hi = lo + qn < send ? lo + qn : send;
-    for (uint32_t p0 = lo + wv; p0 < hi; p0 += kRunWaves) {
+    for (uint32_t p0 = lo + wv; p0 < hi; p0 += kW) {
       const int64_t r0 = zero_row(zr, pad_rows, p0 / g.npc);
       const uint32_t c0 = p0 - (p0 / g.npc) * g.npc;
       const int64_t v0 = (int64_t)(c0 * kWave + lane);
@@ -2418,14 +2434,15 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
   if (d.T == 0 || npc > kWbwdMaxPartials || scap * npc >= lim || zero_max * npc >= lim)
     return launch_weighted_bwd_groups(d, hv, g, y, rw, grad_rows, grad_w, num_cus, stream);
   // rows per block step: as many whole rows as fill the step's rounds of
-  // 8 * kWbwdPieces pieces, at least one. With the weight gradient a step
-  // ends in two block barriers: two rounds a step and at most kWbwdBlocksPerCU
-  // blocks per CU (each taking more steps) measured best on the MI355X
-  // (dsv3 247 us against 257 us with one round and 96 blocks per CU, the
-  // masked share 209 against 231); the row gradient alone has no barrier and
-  // takes one round and the run copy's grid.
+  // waves * kWbwdPieces pieces, at least one. With the weight gradient a step
+  // ends in two block barriers: two rounds a step and at most 256 wavefronts
+  // per CU (each block taking more steps) measured best on the MI355X, with
+  // eight-wavefront blocks (dsv3 247 us against 257 us with one round and 96
+  // blocks per CU, the masked share 209 against 231); the row gradient alone
+  // has no barrier and takes one round and the run copy's grid.
   const bool want_w = grad_w != nullptr;
-  const int64_t round = (int64_t)kRunWaves * kWbwdPieces * (want_w ? kWbwdRounds : 1);
+  const int waves = wbwd_waves(want_w);
+  const int64_t round = (int64_t)waves * kWbwdPieces * (want_w ? kWbwdRounds : 1);
   int64_t R = round / npc;
   if (R < 1) R = 1;
   const int64_t dense = run_stream_dense(d.num_units, routes);
@@ -2450,22 +2467,22 @@ hipError_t launch_weighted_bwd(const Dims& d, const HandleView& hv, const void* 
   if (d.K >= kRunPrefetchMinK && row_bytes >= kRunPrefetchMinRow &&
       d.T * row_bytes <= kRunPrefetchMaxBytes) {
     const int64_t nvec = d.T * d.V;
-    int64_t npf = (nvec + (int64_t)kRunWaves * kWave * 4 - 1) / ((int64_t)kRunWaves * kWave * 4);
+    int64_t npf = (nvec + (int64_t)waves * kWave * 4 - 1) / ((int64_t)waves * kWave * 4);
     if (npf > kRunPrefetchBlocks) npf = kRunPrefetchBlocks;
     geo.npf = (uint32_t)npf;
-    geo.pf_per = (uint32_t)((nvec + npf * kRunWaves * kWave - 1) / (npf * kRunWaves * kWave));
+    geo.pf_per = (uint32_t)((nvec + npf * waves * kWave - 1) / (npf * waves * kWave));
   }
   const int64_t grid = (int64_t)geo.npf + kRunXcds * bps;
   return with_dtype(d.dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
     if (grad_w != nullptr) {
       hipLaunchKernelGGL((run_wbwd_kernel<DT, true>), dim3((unsigned)grid),
-                         dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                         dim3(waves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                          &hv.header->status, rows_in(g), rows_in(y), rw, rows_out(grad_rows),
                          grad_w, geo, (uint32_t)R, hv.row_src);
     } else {
       hipLaunchKernelGGL((run_wbwd_kernel<DT, false>), dim3((unsigned)grid),
-                         dim3(kRunWaves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
+                         dim3(waves * kWave), 0, stream, d, hv.header, hv.runs, hv.pad_rows,
                          &hv.header->status, rows_in(g), nullptr, rw, rows_out(grad_rows),
                          nullptr, geo, (uint32_t)R, hv.row_src);
     }
