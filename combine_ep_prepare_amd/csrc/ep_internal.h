@@ -108,10 +108,23 @@ inline int32_t prep_units(int64_t routes) {
 // LDS one prepare block may take.
 constexpr size_t kPrepLdsBudget = 65536;
 
-// Units per block of the histogram kernel: eight wave-private E-entry
-// histograms, fewer when they do not fit the LDS budget.
-inline int32_t hist_block_units(int32_t E) {
-  int32_t nw = 8;
+// Up to this many block-sum rows every block of the slot kernel sums them
+// itself (about 64 * E loads each); past it the column scan takes its own
+// launch, so that prepare's work stays linear in the routes.
+constexpr int kPrepDirectBlockRows = 64;
+
+// Units per block of the histogram kernel (one wave-private E-entry
+// histogram each): four while the block rows stay within
+// kPrepDirectBlockRows, else eight; fewer when they do not fit the LDS
+// budget. Its wavefronts spend most of their time matching peers one round
+// after another, so while the direct sums allow, smaller blocks spread them
+// over more CUs. Measured on the MI355X (prepare us, four units a block
+// against eight): top-8 of 256 at 4096 tokens 19.3 against 20.3, top-8 of
+// 128 at 8192 18.1 against 19.0, top-2 of 8 at 16384 16.5 against 16.7; the
+// 32-expert masked share at 32768 (512 units) 21.6 against 19.3, where four
+// would take the column scan; two units a block were slower.
+inline int32_t hist_block_units(int32_t num_units, int32_t E) {
+  int32_t nw = num_units <= 4 * kPrepDirectBlockRows ? 4 : 8;
   while (nw > 1 && sizeof(int32_t) * (size_t)nw * (size_t)E > kPrepLdsBudget) nw /= 2;
   return nw;
 }
@@ -119,7 +132,7 @@ inline int32_t hist_block_units(int32_t E) {
 // Block-sum rows of the histogram kernel: one per block, then one more for
 // the totals (written by the column scan when it runs).
 inline int32_t hist_block_rows(int32_t num_units, int32_t E) {
-  const int32_t nw = hist_block_units(E);
+  const int32_t nw = hist_block_units(num_units, E);
   return (num_units + nw - 1) / nw + 1;
 }
 

@@ -2126,10 +2126,6 @@ int key_bits(int E) {
 }
 
 constexpr size_t kLdsBudget = kPrepLdsBudget;
-// Up to this many block-sum rows every slots block sums them itself (about
-// 64 * E loads each); past it the column scan takes its own launch, so that
-// prepare's work stays linear in the routes.
-constexpr int kPrepDirectBlockRows = 64;
 // Routings of at most this many routes take the single-block prepare.
 constexpr int64_t kPrepFusedMaxRoutes = 4096;
 static_assert(kPrepFusedMaxRoutes <= (int64_t)kFusedWaves * kPrepRounds * kWave,
@@ -2212,7 +2208,7 @@ hipError_t launch_prepare(const Dims& d, const HandleView& hv, const int64_t* to
     if (err != hipSuccess) return err;
     return runs_here ? hipSuccess : launch_prepare_runs(d, hv, topk_idx, ru, 1, 0, stream);
   }
-  const int nw1 = hist_block_units(d.E);
+  const int nw1 = hist_block_units(U, d.E);
   const int nb = (U + nw1 - 1) / nw1;
   const int scanned = nb > kPrepDirectBlockRows;
   if (U > 0) {

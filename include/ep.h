@@ -245,10 +245,11 @@ ep_status_t ep_prepare(const ep_layout_t* layout, const int64_t* topk_idx,
  * no ordering between them) race and must not be made; ep_prepare and the
  * payload ops do not touch the array. A layout whose scratch exceeds the
  * array returns EP_ERR_SCRATCH before any HIP call. With U = ceil(T*K/512)
- * units of routes the scratch is 4*E*(U + ceil(U/8) + 1) bytes of histograms
- * (one row per unit, one per block of 8 units, one of totals) plus 8*U bytes
- * of per-unit words, each part rounded up to 256 bytes: at E = 256, 3614
- * units (about 1.85 M routes) fit.
+ * units of routes the scratch is 4*E*(U + B + 1) bytes of histograms (one
+ * row per unit, one per block of units, B = ceil(U/4) blocks of 4 units up
+ * to 256 units and ceil(U/8) blocks of 8 past that, one row of totals) plus
+ * 8*U bytes of per-unit words, each part rounded up to 256 bytes: at
+ * E = 256, 3614 units (about 1.85 M routes) fit.
  */
 #define EP_PREPARE_STATIC_SCRATCH_BYTES (4u << 20)
 

@@ -67,10 +67,10 @@ def test_handle_size_and_regions():
     # entries each (U = 64 units of 512 routes), 8 bytes an entry
     assert r.runs + 8 * (64 * 64 + 2048) * 8 == r.maps_bytes
     # prepare's scratch closes the handle: 256-expert histograms of the 64
-    # units of 512 routes, of their 8 blocks of 8 units and one totals row,
+    # units of 512 routes, of their 16 blocks of 4 units and one totals row,
     # then two words per unit (its flags, a chunk start), each part
     # 256-byte aligned
-    assert n - r.maps_bytes == (64 + 8 + 1) * 256 * 4 + 512
+    assert n - r.maps_bytes == (64 + 16 + 1) * 256 * 4 + 512
     # the handle grows with the capacity and does not depend on H
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=512)) == n
     assert ep.handle_mem_size(lay(T=4096, K=8, E=256, A=128, H=7168, cap=L.cap * 2)) > n

@@ -61,8 +61,10 @@ def test_regions_of_any_valid_layout(L):
     assert r.run_list_entries == 64 * U + 2048
     assert r.maps_bytes - r.runs == a256(8 * 8 * r.run_list_entries)
     # prepare's scratch closes the handle: histogram rows (units, blocks of
-    # 8 units, a totals row) and two words per unit
-    assert n - r.maps_bytes == a256(4 * E * (U + -(-U // 8) + 1)) + a256(8 * U)
+    # 4 units up to 256 units and of 8 past that, a totals row) and two
+    # words per unit
+    blocks = -(-U // 4) if U <= 256 else -(-U // 8)
+    assert n - r.maps_bytes == a256(4 * E * (U + blocks + 1)) + a256(8 * U)
     # nothing but T, K, E, A and the capacity sizes the handle
     for dt in ("bf16", "fp16", "fp32"):
         other = ep.Layout(T, K, E, L.A, 8, cap, dtype=dt)

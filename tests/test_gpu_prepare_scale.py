@@ -1,12 +1,12 @@
 """GPU parity of prepare across its two ways of finding each unit's start.
 
 prepare's histogram kernel writes one row of per-expert counts per unit of
-512 routes and one row of sums per block of 8 units. Up to 64 block rows,
-every block of the slot kernel sums them itself; past that, a column scan
-over the block rows takes its own launch, so that the work stays linear in
-the routes. With many experts the slot kernel's blocks hold fewer units than
-the histogram kernel's, and a block then also adds the unit rows between the
-start of its histogram block and its first unit. These cases sit on both
+512 routes and one row of sums per block of units (4, or 8 past 256 units).
+Up to 64 block rows, every block of the slot kernel sums them itself; past
+that, a column scan over the block rows takes its own launch, so that the
+work stays linear in the routes. Where the slot kernel's blocks hold fewer
+units than the histogram kernel's, a block also adds the unit rows between
+the start of its histogram block and its first unit. These cases sit on both
 sides of the 64-row switch, with 100, 256 and 2048 experts, masked routes
 and ragged tails, for chunks of 4, 2 and 1 units (whose run entries are
 built in the slot kernel or in a launch of their own, their list starts
@@ -45,6 +45,7 @@ def _routing(label, T, K, E, masked):
 
 
 # label, T, K, E, A, masked fraction; block rows = ceil(ceil(T K / 512) / 8)
+# past 256 units
 CASES = [
     ("direct_64_rows", 32768, 8, 256, 128, 0.0),     # 512 units, 64 block rows
     ("scan_65_rows", 32769, 8, 256, 128, 0.0),       # 513 units, 65 rows
